@@ -1,0 +1,191 @@
+"""The five MoE-layer workloads, as data.
+
+Each workload stands in for one MoE layer of a model the pages discuss:
+
+* ``c1`` tiny fp32 layer, sigmoid + bias top-4 (the smallest parity case);
+* ``c2`` DeepSeek-Flash-style decode: 256 experts, sqrt(softplus) top-6 x1.5,
+  int8 blocks of 32 with an fp16 scale (the pages keep "decision" tensors at
+  Q8_0/F32: NeutronStar README, "The model");
+* ``c3`` Hy3-style decode/verify: 192 experts, sigmoid + per-expert bias top-8
+  (NeutronStar README, main branch, Hy3 paragraph), T in {1, 2};
+* ``c4`` prefill chunk, 512 tokens, near-uniform routing;
+* ``c5`` long prefill, 4096 tokens, expert bias skewed so that the hottest ~4%
+  of experts receive ~30% of the selections (the popularity skew the pages
+  report for the host expert cache: NeutronStar README, "SSD streaming
+  optimizations").
+
+Stream ids under the master seed: x 1, router weights 2, bias 3, gate 4, up 5,
+down 6, shared gate/up/down 7/8/9, distinct decode tokens 10, skew
+calibration batch 11.  Row t of x is elements [t*d, (t+1)*d) of its stream,
+so a smaller T is a prefix of a larger one.
+"""
+from __future__ import annotations
+
+import copy
+import math
+
+import numpy as np
+
+from . import normal_bf16, normal_f32, q8b32, uniform_f32, zipf_bias
+
+S_X, S_WR, S_BIAS, S_GATE, S_UP, S_DOWN, S_SGATE, S_SUP, S_SDOWN, S_DECODE, S_CALIB = range(1, 12)
+
+# Skew strength of the c5 bias, b_e = -beta * ln(rank_e).  Found by bisection
+# with the oracle router on the 4096-token calibration batch (stream 11) so that
+# the 10 hottest experts (3.9%) receive 30% of the top-8 selections; the script
+# that finds it is tests/golden/calibrate_skew.py and its output is
+# tests/golden/skew_beta.json.
+C5_BETA = 0.07193540781736374
+
+CONFIGS = {
+    "c1": dict(T=4, d=512, E=32, k=4, F=256, Fs=256, n_shared=1, score="sigmoid", scale=1.0,
+               act="f32", w="f32", x_sigma=0.02, wr_sigma=0.02, w_sigma=0.02,
+               bias="uniform", bias_lo=-0.1, bias_hi=0.1, path="decode"),
+    "c2": dict(T=1, d=4096, E=256, k=6, F=2048, Fs=2048, n_shared=1, score="sqrt_softplus",
+               scale=1.5, act="bf16", w="q8b32", x_sigma=0.02, wr_sigma=0.02, w_sigma=0.02,
+               bias="none", path="decode"),
+    "c3": dict(T=1, d=4096, E=192, k=8, F=1536, Fs=1536, n_shared=1, score="sigmoid", scale=1.0,
+               act="bf16", w="bf16", x_sigma=1.0, wr_sigma=1.0 / 64.0, w_sigma=0.02,
+               bias="uniform", bias_lo=-0.01, bias_hi=0.01, path="decode"),
+    "c4": dict(T=512, d=6144, E=256, k=8, F=2048, Fs=2048, n_shared=1, score="sigmoid",
+               scale=1.0, act="bf16", w="bf16", x_sigma=1.0, wr_sigma=1.0 / math.sqrt(6144.0),
+               w_sigma=0.02, bias="uniform", bias_lo=-0.01, bias_hi=0.01, path="prefill"),
+    "c5": dict(T=4096, d=6144, E=256, k=8, F=2048, Fs=2048, n_shared=1, score="sigmoid",
+               scale=1.0, act="bf16", w="bf16", x_sigma=1.0, wr_sigma=1.0 / math.sqrt(6144.0),
+               w_sigma=0.02, bias="zipf", beta=C5_BETA, path="prefill"),
+}
+
+
+def get(name: str, **over) -> dict:
+    """A copy of workload ``name`` with fields overridden (e.g. ``T=2``)."""
+    cfg = copy.deepcopy(CONFIGS[name])
+    cfg.update(over)
+    cfg["name"] = name
+    cfg.setdefault("seed", 0)
+    return cfg
+
+
+def custom(**fields) -> dict:
+    """A workload from explicit fields (defaults: c1's distributions)."""
+    cfg = copy.deepcopy(CONFIGS["c1"])
+    cfg.update(fields)
+    cfg.setdefault("name", "custom")
+    cfg.setdefault("seed", 0)
+    return cfg
+
+
+def _normal(cfg, stream, n, sigma, start=0, dtype=None):
+    dtype = dtype or cfg["act"]
+    if dtype == "f32":
+        return normal_f32(cfg["seed"], stream, n, sigma, start=start)
+    return normal_bf16(cfg["seed"], stream, n, sigma, start=start)
+
+
+def gen_x(cfg, T=None, stream=S_X, token0=0):
+    """Activations [T, d] (fp32, or bf16 bits as uint16)."""
+    T = cfg["T"] if T is None else T
+    d = cfg["d"]
+    return _normal(cfg, stream, T * d, cfg["x_sigma"], start=token0 * d).reshape(T, d)
+
+
+def gen_router(cfg):
+    E, d = cfg["E"], cfg["d"]
+    return normal_f32(cfg["seed"], S_WR, E * d, cfg["wr_sigma"]).reshape(E, d)
+
+
+def gen_bias(cfg):
+    kind = cfg.get("bias", "none")
+    if kind == "none":
+        return None
+    if kind == "uniform":
+        return uniform_f32(cfg["seed"], S_BIAS, cfg["E"], cfg["bias_lo"], cfg["bias_hi"])
+    if kind == "zipf":
+        return zipf_bias(cfg["seed"], S_BIAS, cfg["E"], cfg["beta"])[0]
+    raise ValueError(kind)
+
+
+def skew_ranks(cfg):
+    """1-based popularity ranks behind a ``zipf`` bias (rank 1 = hottest)."""
+    return zipf_bias(cfg["seed"], S_BIAS, cfg["E"], cfg.get("beta", 0.0))[1]
+
+
+_MAT_STREAM = {"gate": S_GATE, "up": S_UP, "down": S_DOWN,
+               "s_gate": S_SGATE, "s_up": S_SUP, "s_down": S_SDOWN}
+
+
+def mat_shape(cfg, which):
+    """(n_experts, rows, cols) of an expert weight tensor; cols is the reduction dim."""
+    d = cfg["d"]
+    if which in ("gate", "up"):
+        return cfg["E"], cfg["F"], d
+    if which == "down":
+        return cfg["E"], d, cfg["F"]
+    if which in ("s_gate", "s_up"):
+        return cfg["n_shared"], cfg["Fs"], d
+    if which == "s_down":
+        return cfg["n_shared"], d, cfg["Fs"]
+    raise ValueError(which)
+
+
+def gen_mat(cfg, which, e0=0, e1=None):
+    """Experts [e0, e1) of one expert weight tensor.
+
+    fp32 -> float32 [n, rows, cols]; bf16 -> uint16 bits; q8b32 ->
+    (int8 [n, rows, cols], uint16 fp16-bits [n, rows, cols/32]).
+    """
+    n_e, rows, cols = mat_shape(cfg, which)
+    e1 = n_e if e1 is None else e1
+    n = e1 - e0
+    st, sig = _MAT_STREAM[which], cfg["w_sigma"]
+    if cfg["w"] == "q8b32":
+        q, s = q8b32(cfg["seed"], st, n * rows, cols, sig, row0=e0 * rows)
+        return q.reshape(n, rows, cols), s.reshape(n, rows, cols // 32)
+    start = e0 * rows * cols
+    if cfg["w"] == "f32":
+        a = normal_f32(cfg["seed"], st, n * rows * cols, sig, start=start)
+    else:
+        a = normal_bf16(cfg["seed"], st, n * rows * cols, sig, start=start)
+    return a.reshape(n, rows, cols)
+
+
+def empty_mat(cfg, which):
+    """Zero-filled host tensor of the full shape (pages are only touched when written)."""
+    n_e, rows, cols = mat_shape(cfg, which)
+    if cfg["w"] == "q8b32":
+        return (np.zeros((n_e, rows, cols), np.int8), np.zeros((n_e, rows, cols // 32), np.uint16))
+    return np.zeros((n_e, rows, cols), np.float32 if cfg["w"] == "f32" else np.uint16)
+
+
+def fill_experts(cfg, which, mat, experts):
+    """Write the listed experts' weights into a tensor from :func:`empty_mat`."""
+    for e in sorted(set(int(e) for e in experts)):
+        part = gen_mat(cfg, which, e, e + 1)
+        if isinstance(mat, tuple):
+            mat[0][e] = part[0][0]
+            mat[1][e] = part[1][0]
+        else:
+            mat[e] = part[0]
+    return mat
+
+
+def make_layer(cfg, T=None, experts=None):
+    """All inputs of one layer call as numpy arrays.
+
+    ``experts`` (optional) restricts the routed expert weights that are filled;
+    the others stay zero.  Used where only a sample of tokens is evaluated.
+    """
+    L = dict(cfg=cfg, x=gen_x(cfg, T), w_router=gen_router(cfg), bias=gen_bias(cfg))
+    for which in ("gate", "up", "down"):
+        if experts is None:
+            L[which] = gen_mat(cfg, which)
+        else:
+            L[which] = fill_experts(cfg, which, empty_mat(cfg, which), experts)
+    for which in ("s_gate", "s_up", "s_down"):
+        L[which] = gen_mat(cfg, which) if cfg["n_shared"] else None
+    return L
+
+
+def algorithmic_bytes_per_expert(cfg) -> int:
+    """HBM bytes of one routed expert's three matrices in the stored format."""
+    n = 3 * cfg["F"] * cfg["d"]
+    return {"f32": 4 * n, "bf16": 2 * n, "q8b32": n + n // 16}[cfg["w"]]
