@@ -1,0 +1,168 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * One MoE layer: a router scores every token against n_expert experts, keeps
+ * the top-k, renormalises their weights; the token rows are grouped by expert;
+ * each selected expert applies a SwiGLU FFN; an always-on shared expert is
+ * added; the weighted results return to token order.
+ *
+ *   logits  l[t,e] = sum_i x[t,i] * Wr[e,i]            (row stride n_expert)
+ *   score   s = sigmoid(l)  or  s = sqrt(softplus(l))
+ *   key     s + bias[e]  (bias optional; it selects, it never weights)
+ *   select  top-k keys; equal keys -> lower expert index first; NaN last
+ *   weight  w_j = route_scale * s_j / sum over the selected s
+ *   FFN_e   Wd[e] . (silu(Wg[e] x) * (Wu[e] x)),  silu(g) = g / (1 + e^-g)
+ *   y[t]    FFN_shared(x_t) + sum_j w_j FFN_{e_j}(x_t)
+ *
+ * Sources: "256 experts, 512 lines" blog post - section "Why GLM-5.2 in an
+ * engine built for DeepSeek" (sigmoid routing, top-8, MoE with a shared
+ * expert) and section "The constant that always said 256" (sqrt(softplus)
+ * scores, top-6, the 1.5 scale, logits addressed with stride n_expert and
+ * n_expert a runtime value, a parallel top-k rather than a serial one);
+ * NeutronStar README, main branch - Hy3 paragraph (192-expert top-8 sigmoid
+ * router with expert bias, shared expert); NeutronStar README - "The model"
+ * (decision tensors kept at Q8_0/F32), "GLM-5.2 CUDA port" (gate/up and down
+ * projection kernels) and the MTP paragraph (only the selected experts' weights
+ * are read for small batches; batch kernels address whole [E, rows, cols]
+ * expert tensors).
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or synchronises.  `stream` is a hipStream_t (NULL = the
+ *    null stream); all work is enqueued on it and the call returns at once.
+ *  - Every call validates its arguments first.  On failure it returns a
+ *    nonzero moe_status and enqueues nothing.  MOE_ERR_DEVICE reports a launch
+ *    error seen right after enqueueing; faults inside kernels surface at the
+ *    caller's next synchronisation.
+ *  - Device pointers must be 16-byte aligned; sizes are element counts.
+ *  - Layouts are row-major.  Weight tensors are [n, rows, cols] with cols the
+ *    reduction dimension.  bf16 and fp16 values are passed as their bit
+ *    patterns (uint16).  Q8B32 = int8 quants [n, rows, cols] plus one fp16
+ *    scale per 32 consecutive columns [n, rows, cols/32]; weight = scale * q.
+ *  - Results: expert indices and the permutation are exact and do not depend
+ *    on the path taken; logits and scores are accumulated in fp64 and rounded
+ *    once to fp32; the SwiGLU intermediate is rounded to the activation format
+ *    (bf16, or fp32 for fp32 layers); y is fp32.
+ *  - The workspace (`ws`, `ws_bytes`) is caller-owned scratch of at least
+ *    moe_workspace_bytes(cfg) bytes.  It must be zero-filled before its first
+ *    use; every call leaves its synchronisation counters zero again.  Calls
+ *    that share a workspace must not overlap.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,     /* NULL/misaligned pointer, value out of range, bad enum */
+    MOE_ERR_UNSUPPORTED = 2, /* valid but not provided: dtype pair, d/F not multiples of 64, path */
+    MOE_ERR_WORKSPACE = 3,   /* ws_bytes < moe_workspace_bytes(cfg) */
+    MOE_ERR_DEVICE = 4       /* the HIP runtime refused a launch */
+} moe_status;
+
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SQRT_SOFTPLUS = 1 } moe_score;
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_Q8B32 = 2 } moe_dtype;
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 } moe_path;
+
+/* Largest token count the decode path accepts (MOE_PATH_AUTO takes it for
+ * n_tokens <= MOE_DECODE_MAX_TOKENS). */
+#define MOE_DECODE_MAX_TOKENS 8
+
+typedef struct {
+    int32_t n_tokens;    /* T >= 1 */
+    int32_t d_model;     /* d: multiple of 64 */
+    int32_t n_expert;    /* E in [1, 1024], a runtime value */
+    int32_t top_k;       /* k in [1, min(E, 32)] */
+    int32_t d_ff;        /* F: routed expert hidden size, multiple of 64 */
+    int32_t n_shared;    /* 0 or 1 shared expert */
+    int32_t d_ff_shared; /* Fs: shared expert hidden size, multiple of 64 (if n_shared) */
+    int32_t score;       /* moe_score */
+    float route_scale;   /* finite, > 0: 1.5 for the sqrt(softplus) router, 1.0 for sigmoid */
+    int32_t act_dtype;   /* moe_dtype of x and of the SwiGLU intermediate: F32 or BF16 */
+    int32_t w_dtype;     /* moe_dtype of the expert weights: (F32,F32) (BF16,BF16) (BF16,Q8B32) */
+    int32_t path;        /* moe_path, used by moe_layer_forward */
+} moe_config;
+
+typedef struct {
+    const void *q;          /* [n, rows, cols] elements of w_dtype (int8 for Q8B32) */
+    const uint16_t *scale;  /* Q8B32 only: fp16 bits [n, rows, cols/32]; else ignored */
+} moe_mat;
+
+typedef struct {
+    const float *w_router;  /* [E, d] fp32 */
+    const float *bias;      /* [E] fp32 or NULL */
+    moe_mat gate, up;       /* [E, F, d] */
+    moe_mat down;           /* [E, d, F] */
+    moe_mat s_gate, s_up;   /* [1, Fs, d]   (ignored when n_shared == 0) */
+    moe_mat s_down;         /* [1, d, Fs] */
+} moe_weights;
+
+/* Optional outputs of moe_layer_forward; any field may be NULL. */
+typedef struct {
+    float *logits;      /* [T, E] */
+    int32_t *topk_idx;  /* [T, k] */
+    float *topk_w;      /* [T, k] */
+    int32_t *offsets;   /* [E+1] */
+    int32_t *perm_rows; /* [T*k] */
+    int32_t *inv_perm;  /* [T*k] */
+} moe_debug;
+
+/* Bytes of workspace every entry point below may use for this config
+ * (0 if the config is invalid).  Monotone in every size field. */
+size_t moe_workspace_bytes(const moe_config *cfg);
+
+/* Router: logits (optional, [T,E]) and the top-k selection.
+ * x [T, d] act_dtype; w_router [E, d] fp32; bias [E] or NULL;
+ * topk_idx [T, k] int32 in rank order; topk_w [T, k] fp32. */
+int moe_route(const moe_config *cfg, const void *x, const float *w_router, const float *bias,
+              float *logits, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              void *stream);
+
+/* Selection alone, from given fp32 logits [T, E] (row stride n_expert).
+ * n_expert == 256 runs a compile-time 256-expert instantiation of the top-k;
+ * cfg->path == MOE_PATH_PREFILL forces the runtime-n_expert kernel instead
+ * (both give identical results; the switch exists so that can be checked). */
+int moe_select(const moe_config *cfg, const float *logits, const float *bias, int32_t *topk_idx,
+               float *topk_w, void *stream);
+
+/* Token->expert grouping: a stable counting sort of the flat assignments
+ * f = t*k + j by expert.  offsets [E+1] (exclusive prefix sum of the expert
+ * counts); perm_rows [T*k]: the f of every assignment, ordered by (expert, f);
+ * inv_perm [T*k]: position of f in perm_rows.  Indices outside [0, E) are left
+ * out: inv_perm = -1, and the unused tail of perm_rows is -1. */
+int moe_permute(const moe_config *cfg, const int32_t *topk_idx, int32_t *offsets,
+                int32_t *perm_rows, int32_t *inv_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Routed and shared experts.  slot_out [T*k, d] fp32: row f = w_f *
+ * FFN_{expert of f}(x_t); shared_out [T, d] fp32 = FFN_shared(x_t), or NULL
+ * when n_shared == 0.  offsets / perm_rows as produced by moe_permute; topk_w
+ * [T, k].  Rows of assignments that perm_rows does not list are not written.
+ * Offsets that are not a monotone split of [0, T*k] (checked on the device)
+ * leave every slot row unwritten; the shared expert is still computed. */
+int moe_expert_ffn(const moe_config *cfg, const void *x, const moe_weights *w,
+                   const int32_t *offsets, const int32_t *perm_rows, const float *topk_w,
+                   float *slot_out, float *shared_out, void *ws, size_t ws_bytes, void *stream);
+
+/* y [T, d] fp32 = shared_out[t] (if not NULL) + sum_j slot_out[t*k + j]. */
+int moe_combine(const moe_config *cfg, const float *slot_out, const float *shared_out, float *y,
+                void *stream);
+
+/* The whole layer: route, group, experts, combine.  y [T, d] fp32.
+ * cfg->path picks the decode path (GEMV over the selected experts' weights,
+ * combine fused; n_tokens <= MOE_DECODE_MAX_TOKENS) or the prefill path
+ * (grouped GEMMs, bf16 on MFMA); MOE_PATH_AUTO chooses by n_tokens. */
+int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w, float *y,
+                      moe_debug *dbg, void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

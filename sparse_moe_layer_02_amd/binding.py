@@ -1,0 +1,206 @@
+"""ctypes binding of the C ABI in include/moe.h (libmoe_mi355x.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Functions take torch tensors on the GPU (PyTorch supplies device
+memory and streams) and return the library status, raising ``MoeError`` on
+anything but MOE_OK.  The library is loaded from this package's directory;
+there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+SCORE = {"sigmoid": 0, "sqrt_softplus": 1}
+DTYPE = {"f32": 0, "bf16": 1, "q8b32": 2}
+PATH = {"auto": 0, "decode": 1, "prefill": 2}
+DECODE_MAX_TOKENS = 8
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s (status %d)" % (msg, status))
+        self.status = status
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_expert", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("d_ff_shared", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("route_scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("path", ctypes.c_int32)]
+
+
+class moe_mat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("gate", moe_mat), ("up", moe_mat), ("down", moe_mat),
+                ("s_gate", moe_mat), ("s_up", moe_mat), ("s_down", moe_mat)]
+
+
+class moe_debug(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
+                ("topk_w", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("perm_rows", ctypes.c_void_p), ("inv_perm", ctypes.c_void_p)]
+
+
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_permute", "moe_expert_ffn",
+           "moe_combine", "moe_layer_forward", "moe_status_str")
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libmoe_mi355x.so is not built (run __graft_entry__.build() or "
+                          "python sparse_moe_layer_02_amd/build.py); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P, C = ctypes.c_void_p, ctypes.POINTER(moe_config)
+    W = ctypes.POINTER(moe_weights)
+    lib.moe_workspace_bytes.argtypes = [C]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_route.argtypes = [C, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_select.argtypes = [C, P, P, P, P, P]
+    lib.moe_permute.argtypes = [C, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_expert_ffn.argtypes = [C, P, W, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_combine.argtypes = [C, P, P, P, P]
+    lib.moe_layer_forward.argtypes = [C, P, W, P, ctypes.POINTER(moe_debug), P, ctypes.c_size_t, P]
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    for name in EXPORTS[1:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def make_config(T, d, E, k, F, n_shared=1, Fs=None, score="sigmoid", route_scale=1.0, act="bf16",
+                w="bf16", path="auto") -> moe_config:
+    return moe_config(n_tokens=T, d_model=d, n_expert=E, top_k=k, d_ff=F, n_shared=n_shared,
+                      d_ff_shared=F if Fs is None else Fs, score=SCORE.get(score, score),
+                      route_scale=route_scale, act_dtype=DTYPE.get(act, act),
+                      w_dtype=DTYPE.get(w, w), path=PATH.get(path, path))
+
+
+def config_from(cfg: dict, T=None, path="auto") -> moe_config:
+    """A moe_config from a workload dict (keys T, d, E, k, F, Fs, n_shared, score, scale, act, w)."""
+    return make_config(cfg["T"] if T is None else T, cfg["d"], cfg["E"], cfg["k"], cfg["F"],
+                       cfg["n_shared"], cfg["Fs"], cfg["score"], cfg["scale"], cfg["act"], cfg["w"], path)
+
+
+def ptr(t) -> int | None:
+    """Device address of a tensor (None passes through as NULL)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def mat(m) -> moe_mat:
+    """moe_mat from a tensor or a (quants, scales) pair of tensors."""
+    if m is None:
+        return moe_mat(None, None)
+    if isinstance(m, (tuple, list)):
+        return moe_mat(ptr(m[0]), ptr(m[1]))
+    return moe_mat(ptr(m), None)
+
+
+def make_weights(W: dict) -> moe_weights:
+    """moe_weights from a dict of device tensors (keys as in the header)."""
+    return moe_weights(ptr(W["w_router"]), ptr(W.get("bias")), mat(W["gate"]), mat(W["up"]),
+                       mat(W["down"]), mat(W.get("s_gate")), mat(W.get("s_up")), mat(W.get("s_down")))
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(st, lib=None):
+    if st != MOE_OK:
+        lib = lib or load()
+        raise MoeError(st, lib.moe_status_str(st).decode())
+    return st
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def moe_workspace_bytes(cfg: moe_config) -> int:
+    return load().moe_workspace_bytes(ctypes.byref(cfg))
+
+
+def moe_status_str(status: int) -> str:
+    return load().moe_status_str(status).decode()
+
+
+def moe_route(cfg, x, w_router, bias, logits, topk_idx, topk_w, ws, stream=None):
+    lib = load()
+    return _check(lib.moe_route(ctypes.byref(cfg), ptr(x), ptr(w_router), ptr(bias), ptr(logits),
+                                ptr(topk_idx), ptr(topk_w), ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream)), lib)
+
+
+def moe_select(cfg, logits, bias, topk_idx, topk_w, stream=None):
+    lib = load()
+    return _check(lib.moe_select(ctypes.byref(cfg), ptr(logits), ptr(bias), ptr(topk_idx), ptr(topk_w),
+                                 _stream(stream)), lib)
+
+
+def moe_permute(cfg, topk_idx, offsets, perm_rows, inv_perm, ws, stream=None):
+    lib = load()
+    return _check(lib.moe_permute(ctypes.byref(cfg), ptr(topk_idx), ptr(offsets), ptr(perm_rows),
+                                  ptr(inv_perm), ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), lib)
+
+
+def moe_expert_ffn(cfg, x, weights: moe_weights, offsets, perm_rows, topk_w, slot_out, shared_out, ws,
+                   stream=None):
+    lib = load()
+    return _check(lib.moe_expert_ffn(ctypes.byref(cfg), ptr(x), ctypes.byref(weights), ptr(offsets),
+                                     ptr(perm_rows), ptr(topk_w), ptr(slot_out), ptr(shared_out), ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), lib)
+
+
+def moe_combine(cfg, slot_out, shared_out, y, stream=None):
+    lib = load()
+    return _check(lib.moe_combine(ctypes.byref(cfg), ptr(slot_out), ptr(shared_out), ptr(y),
+                                  _stream(stream)), lib)
+
+
+def moe_layer_forward(cfg, x, weights: moe_weights, y, ws, debug: dict | None = None, stream=None):
+    lib = load()
+    dbg = None
+    if debug:
+        dbg = moe_debug(*(ptr(debug.get(k)) for k in
+                          ("logits", "topk_idx", "topk_w", "offsets", "perm_rows", "inv_perm")))
+    return _check(lib.moe_layer_forward(ctypes.byref(cfg), ptr(x), ctypes.byref(weights), ptr(y),
+                                        ctypes.byref(dbg) if dbg else None, ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)), lib)
+
+
+def workspace(cfg: moe_config, device="cuda"):
+    """A zero-filled workspace tensor of moe_workspace_bytes(cfg) bytes (the library
+    requires zero-filled memory before first use)."""
+    import torch
+    n = moe_workspace_bytes(cfg)
+    if n == 0:
+        raise MoeError(MOE_ERR_INVALID, "invalid config")
+    return torch.zeros(n, dtype=torch.uint8, device=device)

@@ -1,0 +1,333 @@
+// api.hip - the C ABI of include/moe.h: argument validation (nothing is
+// enqueued on failure), the workspace layout, and the choice between the
+// decode path (GEMVs over the selected experts) and the prefill path (grouped
+// MFMA GEMMs).  All device work is enqueued on the caller's stream; nothing
+// here allocates, frees or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int MAX_TOKENS = 1 << 20;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+bool opt_ptr_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+int validate_config(const moe_config* c) {
+    if (!c) return MOE_ERR_INVALID;
+    if (c->n_tokens < 1 || c->n_tokens > MAX_TOKENS) return MOE_ERR_INVALID;
+    if (c->d_model < 1 || c->d_ff < 1) return MOE_ERR_INVALID;
+    if (c->n_expert < 1 || c->n_expert > 1024) return MOE_ERR_INVALID;
+    if (c->top_k < 1 || c->top_k > c->n_expert || c->top_k > 32) return MOE_ERR_INVALID;
+    if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_INVALID;
+    if (c->n_shared == 1 && c->d_ff_shared < 1) return MOE_ERR_INVALID;
+    if (c->score != MOE_SCORE_SIGMOID && c->score != MOE_SCORE_SQRT_SOFTPLUS) return MOE_ERR_INVALID;
+    if (!(c->route_scale > 0.0f) || isinf(c->route_scale)) return MOE_ERR_INVALID;
+    if (c->act_dtype < 0 || c->act_dtype > 1 || c->w_dtype < 0 || c->w_dtype > 2) return MOE_ERR_INVALID;
+    if (c->path < MOE_PATH_AUTO || c->path > MOE_PATH_PREFILL) return MOE_ERR_INVALID;
+    const bool pair_ok = (c->act_dtype == MOE_DT_F32 && c->w_dtype == MOE_DT_F32) ||
+                         (c->act_dtype == MOE_DT_BF16 && c->w_dtype == MOE_DT_BF16) ||
+                         (c->act_dtype == MOE_DT_BF16 && c->w_dtype == MOE_DT_Q8B32);
+    if (!pair_ok) return MOE_ERR_UNSUPPORTED;
+    if (c->d_model % 64 || c->d_ff % 64 || (c->n_shared && c->d_ff_shared % 64)) return MOE_ERR_UNSUPPORTED;
+    if ((size_t)c->d_model > (1u << 20) || (size_t)c->d_ff > (1u << 20) ||
+        (c->n_shared && (size_t)c->d_ff_shared > (1u << 20)))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int ldh_of(const moe_config* c) {
+    return c->n_shared ? (c->d_ff > c->d_ff_shared ? c->d_ff : c->d_ff_shared) : c->d_ff;
+}
+
+int max_tiles_of(const moe_config* c) {
+    const long n = (long)c->n_tokens * c->top_k;
+    long t = (n + GEMM_BM - 1) / GEMM_BM + (n < c->n_expert ? n : c->n_expert);
+    if (c->n_shared) t += (c->n_tokens + GEMM_BM - 1) / GEMM_BM;
+    return (int)t;
+}
+
+Layout make_layout(const moe_config* c) {
+    Layout L;
+    const size_t T = (size_t)c->n_tokens, E = (size_t)c->n_expert, k = (size_t)c->top_k;
+    const size_t d = (size_t)c->d_model, n = T * k;
+    const size_t hsz = c->act_dtype == MOE_DT_BF16 ? 2 : 4;
+    L.n_blk = (int)((n + PERM_BLOCK - 1) / PERM_BLOCK);
+    L.max_tiles = max_tiles_of(c);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    L.logits = take(T * E * 4);
+    L.topk_idx = take(n * 4);
+    L.topk_w = take(n * 4);
+    L.offsets = take((E + 1) * 4);
+    L.perm_rows = take(n * 4);
+    L.inv_perm = take(n * 4);
+    L.blk_hist = take((size_t)L.n_blk * E * 4);
+    L.blk_base = take((size_t)L.n_blk * E * 4);
+    L.meta = take(META_WORDS * 4);
+    L.active = take(E * 4);
+    L.tiles = take((size_t)L.max_tiles * 8);
+    L.h = take((n + (c->n_shared ? T : 0)) * (size_t)ldh_of(c) * hsz);
+    L.slot_out = take(n * d * 4);
+    L.shared_out = take(c->n_shared ? T * d * 4 : 0);
+    L.total = o;
+    return L;
+}
+
+template <class P>
+P* at(void* ws, size_t off) {
+    return reinterpret_cast<P*>(static_cast<uint8_t*>(ws) + off);
+}
+
+int check_ws(const moe_config* c, const void* ws, size_t ws_bytes) {
+    if (!ws || !aligned16(ws)) return MOE_ERR_INVALID;
+    if (ws_bytes < make_layout(c).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+bool mat_ok(const moe_config* c, const moe_mat& m) {
+    if (!ptr_ok(m.q)) return false;
+    if (c->w_dtype == MOE_DT_Q8B32 && (m.scale == nullptr || ((uintptr_t)m.scale & 3u))) return false;
+    return true;
+}
+
+int check_weights(const moe_config* c, const moe_weights* w, bool router) {
+    if (!w) return MOE_ERR_INVALID;
+    if (router && (!ptr_ok(w->w_router) || !opt_ptr_ok(w->bias))) return MOE_ERR_INVALID;
+    if (!mat_ok(c, w->gate) || !mat_ok(c, w->up) || !mat_ok(c, w->down)) return MOE_ERR_INVALID;
+    if (c->n_shared && (!mat_ok(c, w->s_gate) || !mat_ok(c, w->s_up) || !mat_ok(c, w->s_down)))
+        return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+int device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+MatRef ref(const moe_mat& m) { return MatRef{m.q, m.scale}; }
+
+PermArgs perm_args(const moe_config* c, const Layout& L, void* ws, const int32_t* idx, int32_t* off,
+                   int32_t* perm, int32_t* inv) {
+    PermArgs p;
+    p.topk_idx = idx;
+    p.T = c->n_tokens;
+    p.k = c->top_k;
+    p.E = c->n_expert;
+    p.n_shared = c->n_shared;
+    p.offsets = off;
+    p.perm_rows = perm;
+    p.inv_perm = inv;
+    p.blk_hist = at<int32_t>(ws, L.blk_hist);
+    p.blk_base = at<int32_t>(ws, L.blk_base);
+    p.meta = at<int32_t>(ws, L.meta);
+    p.active = at<int32_t>(ws, L.active);
+    p.tiles = at<int2>(ws, L.tiles);
+    p.n_blk = L.n_blk;
+    p.bm = GEMM_BM;
+    return p;
+}
+
+FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, const moe_weights* w,
+                 const int32_t* off, const int32_t* perm, const float* topk_w) {
+    FfnArgs f;
+    f.x = x;
+    f.gate = ref(w->gate);
+    f.up = ref(w->up);
+    f.down = ref(w->down);
+    f.s_gate = ref(w->s_gate);
+    f.s_up = ref(w->s_up);
+    f.s_down = ref(w->s_down);
+    f.offsets = off;
+    f.perm_rows = perm;
+    f.topk_w = topk_w;
+    f.meta = at<int32_t>(ws, L.meta);
+    f.active = at<int32_t>(ws, L.active);
+    f.tiles = at<int2>(ws, L.tiles);
+    f.T = c->n_tokens;
+    f.d = c->d_model;
+    f.E = c->n_expert;
+    f.k = c->top_k;
+    f.F = c->d_ff;
+    f.Fs = c->n_shared ? c->d_ff_shared : 0;
+    f.n_shared = c->n_shared;
+    f.act = c->act_dtype;
+    f.wdt = c->w_dtype;
+    f.h = at<void>(ws, L.h);
+    f.ldh = ldh_of(c);
+    f.slot_out = at<float>(ws, L.slot_out);
+    f.shared_out = c->n_shared ? at<float>(ws, L.shared_out) : nullptr;
+    f.y = nullptr;
+    f.max_tiles = L.max_tiles;
+    return f;
+}
+
+// Experts of the prefill path: MFMA for bf16 weights, GEMVs otherwise.
+hipError_t run_expert_kernels(const FfnArgs& f, hipStream_t st) {
+    hipError_t e;
+    if (f.wdt == MOE_DT_BF16) {
+        if ((e = launch_gateup_mfma(f, st)) != hipSuccess) return e;
+        return launch_down_mfma(f, st);
+    }
+    if ((e = launch_gateup_gemv(f, st)) != hipSuccess) return e;
+    return launch_down_slots_gemv(f, st);
+}
+
+SelectArgs select_args(const moe_config* c, const float* logits, const float* bias, int32_t* idx,
+                       float* w) {
+    SelectArgs s;
+    s.logits = logits;
+    s.bias = bias;
+    s.T = c->n_tokens;
+    s.E = c->n_expert;
+    s.k = c->top_k;
+    s.score = c->score;
+    s.route_scale = c->route_scale;
+    s.topk_idx = idx;
+    s.topk_w = w;
+    s.generic_only = false;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+    if (validate_config(cfg) != MOE_OK) return 0;
+    return make_layout(cfg).total;
+}
+
+const char* moe_status_str(int status) {
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_DEVICE: return "device launch failed";
+    default: return "unknown status";
+    }
+}
+
+int moe_route(const moe_config* cfg, const void* x, const float* w_router, const float* bias,
+              float* logits, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if (!ptr_ok(x) || !ptr_ok(w_router) || !opt_ptr_ok(bias) || !opt_ptr_ok(logits) || !ptr_ok(topk_idx) ||
+        !ptr_ok(topk_w))
+        return MOE_ERR_INVALID;
+    if (!logits && (s = check_ws(cfg, ws, ws_bytes))) return s;
+    const Layout L = make_layout(cfg);
+    float* lg = logits ? logits : at<float>(ws, L.logits);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    RouteArgs r{x, w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, lg,
+                cfg->path == MOE_PATH_PREFILL};
+    hipError_t e = launch_router_logits(r, st);
+    if (e == hipSuccess) e = launch_topk(select_args(cfg, lg, bias, topk_idx, topk_w), st);
+    return device_status(e);
+}
+
+int moe_select(const moe_config* cfg, const float* logits, const float* bias, int32_t* topk_idx,
+               float* topk_w, void* stream) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if (!ptr_ok(logits) || !opt_ptr_ok(bias) || !ptr_ok(topk_idx) || !ptr_ok(topk_w)) return MOE_ERR_INVALID;
+    SelectArgs a = select_args(cfg, logits, bias, topk_idx, topk_w);
+    a.generic_only = cfg->path == MOE_PATH_PREFILL;  // lets tests reach the generic kernel at E = 256
+    return device_status(launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* offsets, int32_t* perm_rows,
+                int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if (!ptr_ok(topk_idx) || !ptr_ok(offsets) || !ptr_ok(perm_rows) || !ptr_ok(inv_perm)) return MOE_ERR_INVALID;
+    if ((s = check_ws(cfg, ws, ws_bytes))) return s;
+    const Layout L = make_layout(cfg);
+    PermArgs p = perm_args(cfg, L, ws, topk_idx, offsets, perm_rows, inv_perm);
+    return device_status(launch_permute(p, static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn(const moe_config* cfg, const void* x, const moe_weights* w, const int32_t* offsets,
+                   const int32_t* perm_rows, const float* topk_w, float* slot_out, float* shared_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if ((s = check_weights(cfg, w, false))) return s;
+    if (!ptr_ok(x) || !ptr_ok(offsets) || !ptr_ok(perm_rows) || !ptr_ok(topk_w) || !ptr_ok(slot_out))
+        return MOE_ERR_INVALID;
+    if (cfg->n_shared && !ptr_ok(shared_out)) return MOE_ERR_INVALID;
+    if ((s = check_ws(cfg, ws, ws_bytes))) return s;
+    const Layout L = make_layout(cfg);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    PermArgs p = perm_args(cfg, L, ws, nullptr, const_cast<int32_t*>(offsets), const_cast<int32_t*>(perm_rows),
+                           nullptr);
+    hipError_t e = launch_lists_from_offsets(p, st);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    FfnArgs f = ffn_args(cfg, L, ws, x, w, offsets, perm_rows, topk_w);
+    f.slot_out = slot_out;
+    f.shared_out = cfg->n_shared ? shared_out : nullptr;
+    return device_status(run_expert_kernels(f, st));
+}
+
+int moe_combine(const moe_config* cfg, const float* slot_out, const float* shared_out, float* y, void* stream) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if (!ptr_ok(slot_out) || !opt_ptr_ok(shared_out) || !ptr_ok(y)) return MOE_ERR_INVALID;
+    CombineArgs c{slot_out, shared_out, y, cfg->n_tokens, cfg->top_k, cfg->d_model};
+    return device_status(launch_combine(c, static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w, float* y, moe_debug* dbg,
+                      void* ws, size_t ws_bytes, void* stream) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if ((s = check_weights(cfg, w, true))) return s;
+    if (!ptr_ok(x) || !ptr_ok(y)) return MOE_ERR_INVALID;
+    if (dbg && (!opt_ptr_ok(dbg->logits) || !opt_ptr_ok(dbg->topk_idx) || !opt_ptr_ok(dbg->topk_w) ||
+                !opt_ptr_ok(dbg->offsets) || !opt_ptr_ok(dbg->perm_rows) || !opt_ptr_ok(dbg->inv_perm)))
+        return MOE_ERR_INVALID;
+    const bool decode = cfg->path == MOE_PATH_DECODE ||
+                        (cfg->path == MOE_PATH_AUTO && cfg->n_tokens <= MOE_DECODE_MAX_TOKENS);
+    if (decode && cfg->n_tokens > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    if ((s = check_ws(cfg, ws, ws_bytes))) return s;
+    const Layout L = make_layout(cfg);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    float* logits = dbg && dbg->logits ? dbg->logits : at<float>(ws, L.logits);
+    int32_t* idx = dbg && dbg->topk_idx ? dbg->topk_idx : at<int32_t>(ws, L.topk_idx);
+    float* wts = dbg && dbg->topk_w ? dbg->topk_w : at<float>(ws, L.topk_w);
+    int32_t* off = dbg && dbg->offsets ? dbg->offsets : at<int32_t>(ws, L.offsets);
+    int32_t* perm = dbg && dbg->perm_rows ? dbg->perm_rows : at<int32_t>(ws, L.perm_rows);
+    int32_t* inv = dbg && dbg->inv_perm ? dbg->inv_perm : at<int32_t>(ws, L.inv_perm);
+
+    RouteArgs r{x, w->w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, logits, !decode};
+    hipError_t e = launch_router_logits(r, st);
+    if (e == hipSuccess) e = launch_topk(select_args(cfg, logits, w->bias, idx, wts), st);
+    if (e == hipSuccess) e = launch_permute(perm_args(cfg, L, ws, idx, off, perm, inv), st);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    FfnArgs f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
+    if (decode) {
+        f.y = y;
+        e = launch_gateup_gemv(f, st);
+        if (e == hipSuccess) e = launch_down_combine_gemv(f, st);
+        return device_status(e);
+    }
+    e = run_expert_kernels(f, st);
+    if (e == hipSuccess) {
+        CombineArgs c{f.slot_out, f.shared_out, y, cfg->n_tokens, cfg->top_k, cfg->d_model};
+        e = launch_combine(c, st);
+    }
+    return device_status(e);
+}
+
+}  // extern "C"

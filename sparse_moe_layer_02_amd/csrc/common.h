@@ -1,0 +1,148 @@
+// common.h - device helpers shared by the gfx950 kernels of the MoE layer:
+// storage-format conversions, wavefront (64-lane) reductions built from DPP
+// and LDS-crossbar swizzles, and the workspace layout the host code hands to
+// the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------------------
+// Formats
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// IEEE binary16 bits -> fp32 (hardware conversion; subnormals preserved).
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions.  Butterfly order: xor 1, xor 2 (quad permutes), half-
+// row mirror, row mirror (DPP), then xor 16 and xor 32 through the LDS
+// crossbar.  Every lane ends with the same value; the order of operations is
+// fixed, so the result is deterministic.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+    // ds_swizzle bitmask mode: and 0x1F, xor 0x10 (swaps lanes 16 apart inside each 32)
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+    return (uint32_t)__shfl_xor((int)v, 32);
+}
+
+template <class Op>
+__device__ __forceinline__ float wave_reduce_f32(float v, Op op) {
+    v = op(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(xor16_u32(__float_as_uint(v))));
+    v = op(v, __uint_as_float(xor32_u32(__float_as_uint(v))));
+    return v;
+}
+struct AddF { __device__ float operator()(float a, float b) const { return a + b; } };
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce_f32(v, AddF()); }
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    uint64_t u = __double_as_longlong(v);
+    uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double xor16_f64(double v) {
+    uint64_t u = __double_as_longlong(v);
+    uint32_t lo = xor16_u32((uint32_t)u), hi = xor16_u32((uint32_t)(u >> 32));
+    return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double xor32_f64(double v) {
+    uint64_t u = __double_as_longlong(v);
+    uint32_t lo = xor32_u32((uint32_t)u), hi = xor32_u32((uint32_t)(u >> 32));
+    return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64<DPP_XOR1>(v);
+    v += dpp_f64<DPP_XOR2>(v);
+    v += dpp_f64<DPP_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_MIRROR>(v);
+    v += xor16_f64(v);
+    v += xor32_f64(v);
+    return v;
+}
+
+// Wave-wide maximum of an unsigned 64-bit key.
+__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = u64_max(v, dpp_u64<DPP_XOR1>(v));
+    v = u64_max(v, dpp_u64<DPP_XOR2>(v));
+    v = u64_max(v, dpp_u64<DPP_HALF_MIRROR>(v));
+    v = u64_max(v, dpp_u64<DPP_MIRROR>(v));
+    v = u64_max(v, ((uint64_t)xor16_u32((uint32_t)(v >> 32)) << 32) | xor16_u32((uint32_t)v));
+    v = u64_max(v, ((uint64_t)xor32_u32((uint32_t)(v >> 32)) << 32) | xor32_u32((uint32_t)v));
+    return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Lanes below this one, as a 64-bit mask.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout.  Computed on the host (api.cpp) from the config; every
+// region is 256-byte aligned.  Kernels receive the individual pointers.
+// ---------------------------------------------------------------------------
+struct Layout {
+    size_t logits, topk_idx, topk_w, offsets, perm_rows, inv_perm;
+    size_t blk_hist, blk_base, meta, active, tiles, h, slot_out, shared_out, total;
+    int n_blk;       // permutation blocks of PERM_BLOCK assignments
+    int max_tiles;   // capacity of the grouped-GEMM tile list
+};
+
+// Meta words at ws + meta: [0] n_active experts, [1] n_tiles, [2] valid
+// assignments, [3..15] reserved (sync counters, kept zero between calls).
+constexpr int META_WORDS = 16;
+constexpr int PERM_BLOCK = 256;     // assignments per permutation block (one wave)
+constexpr int GEMM_BM = 64;         // rows per grouped-GEMM tile (tile list granularity)
+
+}  // namespace moe

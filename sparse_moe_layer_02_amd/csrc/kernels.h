@@ -1,0 +1,93 @@
+// kernels.h - internal launch interface between the C-ABI host code (api.hip)
+// and the kernel files.  Every launcher enqueues on the given stream and
+// returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+struct RouteArgs {
+    const void* x;
+    const float* wr;
+    int T, d, E, act;
+    float* logits;
+    bool force_gemm;  // use the tiled prefill kernel even for few tokens
+};
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st);
+
+struct SelectArgs {
+    const float* logits;
+    const float* bias;
+    int T, E, k, score;
+    float route_scale;
+    int32_t* topk_idx;
+    float* topk_w;
+    bool generic_only;  // skip the compile-time 256-expert instantiation
+};
+hipError_t launch_topk(const SelectArgs& a, hipStream_t st);
+
+struct PermArgs {
+    const int32_t* topk_idx;
+    int T, k, E;
+    int n_shared;
+    int32_t* offsets;    // [E+1] (read-only for launch_lists_from_offsets)
+    int32_t* perm_rows;  // [T*k]
+    int32_t* inv_perm;   // [T*k]
+    int32_t* blk_hist;   // [n_blk, E]
+    int32_t* blk_base;   // [n_blk, E]
+    int32_t* meta;       // META_WORDS
+    int32_t* active;     // [E] experts with rows, ascending
+    int2* tiles;         // [max_tiles] (group, first row) for the grouped GEMM
+    int n_blk;
+    int bm;              // tile rows for the tile list
+};
+hipError_t launch_permute(const PermArgs& a, hipStream_t st);
+// active / tile lists from existing offsets (offsets and perm_rows untouched)
+hipError_t launch_lists_from_offsets(const PermArgs& a, hipStream_t st);
+
+// One set of expert weights for the FFN kernels.
+struct MatRef {
+    const void* q;
+    const uint16_t* scale;
+};
+
+struct FfnArgs {
+    const void* x;          // [T, d]
+    MatRef gate, up, down;  // routed [E, F, d], [E, F, d], [E, d, F]
+    MatRef s_gate, s_up, s_down;
+    const int32_t* offsets;
+    const int32_t* perm_rows;
+    const float* topk_w;
+    const int32_t* meta;    // n_active at [0], n_tiles at [1]
+    const int32_t* active;  // active experts, ascending
+    const int2* tiles;
+    int T, d, E, k, F, Fs, n_shared, act, wdt;
+    void* h;                // [T*k + T*n_shared, ldh] in the activation format
+    int ldh;                // max(F, Fs)
+    float* slot_out;        // [T*k, d]
+    float* shared_out;      // [T, d]
+    float* y;               // [T, d] (fused combine)
+    int max_tiles;
+};
+// gate/up GEMV over the active experts (and the shared one) -> h
+hipError_t launch_gateup_gemv(const FfnArgs& a, hipStream_t st);
+// down GEMV + weighted combine straight into y (T <= MOE_DECODE_MAX_TOKENS)
+hipError_t launch_down_combine_gemv(const FfnArgs& a, hipStream_t st);
+// down GEMV writing weighted slot rows and the shared rows
+hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st);
+// grouped bf16 MFMA GEMMs (prefill)
+hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st);
+hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st);
+
+struct CombineArgs {
+    const float* slot_out;
+    const float* shared_out;
+    float* y;
+    int T, k, d;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,124 @@
+"""The C-ABI boundary on the CPU: the built library loads, exports every entry
+point include/moe.h declares, and rejects invalid arguments before touching
+the device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import sparse_moe_layer_02_amd as m
+    if not os.path.exists(m.binding.LIB_PATH):
+        from sparse_moe_layer_02_amd import build
+        build.build()
+    m.load()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(moe):
+    names = declared_functions()
+    assert len(names) >= 8, names
+    lib = ctypes.CDLL(moe.binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+    assert set(moe.binding.EXPORTS) == set(names)
+
+
+def test_binding_has_same_names(moe):
+    for n in declared_functions():
+        assert callable(getattr(moe, n)), n
+
+
+def test_status_strings(moe):
+    assert moe.moe_status_str(0) == "ok"
+    assert "workspace" in moe.moe_status_str(3)
+    assert moe.moe_status_str(99) == "unknown status"
+
+
+def _cfg(moe, **kw):
+    base = dict(T=4, d=512, E=32, k=4, F=256, n_shared=1, Fs=256, score="sigmoid", route_scale=1.0,
+                act="bf16", w="bf16", path="auto")
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+BAD = [
+    (dict(T=0), 1), (dict(E=0), 1), (dict(E=1025), 1), (dict(k=0), 1), (dict(k=33, E=64), 1),
+    (dict(k=5, E=4), 1), (dict(n_shared=2), 1), (dict(score=7), 1), (dict(route_scale=0.0), 1),
+    (dict(route_scale=float("inf")), 1), (dict(route_scale=float("nan")), 1), (dict(act=5), 1),
+    (dict(path=9), 1), (dict(act="f32", w="bf16"), 2), (dict(act="bf16", w="f32"), 2),
+    (dict(act="f32", w="q8b32"), 2), (dict(d=500), 2), (dict(F=100), 2), (dict(Fs=96), 2),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD)
+def test_invalid_configs(moe, over, code):
+    c = _cfg(moe, **over)
+    lib = moe.load()
+    assert lib.moe_workspace_bytes(ctypes.byref(c)) == 0
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+    assert lib.moe_select(ctypes.byref(c), fake, None, fake, fake, None) == code
+    assert lib.moe_combine(ctypes.byref(c), fake, None, fake, None) == code
+    assert lib.moe_permute(ctypes.byref(c), fake, fake, fake, fake, fake, 1 << 40, None) == code
+    assert lib.moe_layer_forward(ctypes.byref(c), fake, None, fake, None, fake, 1 << 40, None) == code
+
+
+def test_null_and_misaligned_pointers(moe):
+    lib = moe.load()
+    c = _cfg(moe)
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.moe_select(ctypes.byref(c), None, None, fake, fake, None) == 1
+    assert lib.moe_select(ctypes.byref(c), odd, None, fake, fake, None) == 1
+    assert lib.moe_combine(ctypes.byref(c), fake, odd, fake, None) == 1
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, fake, fake, None, 0, None) == 1
+    assert lib.moe_permute(ctypes.byref(c), fake, fake, None, fake, fake, 1 << 40, None) == 1
+    assert lib.moe_layer_forward(None, fake, None, fake, None, fake, 1 << 40, None) == 1
+    # weights struct with a NULL matrix
+    w = moe.binding.moe_weights()
+    w.w_router = fake.value
+    assert lib.moe_layer_forward(ctypes.byref(c), fake, ctypes.byref(w), fake, None, fake, 1 << 40, None) == 1
+
+
+def test_workspace_too_small(moe):
+    lib = moe.load()
+    c = _cfg(moe)
+    need = lib.moe_workspace_bytes(ctypes.byref(c))
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.moe_permute(ctypes.byref(c), fake, fake, fake, fake, fake, need - 1, None) == 3
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, fake, fake, fake, need - 1, None) == 3
+
+
+def test_decode_path_token_limit(moe):
+    lib = moe.load()
+    c = _cfg(moe, T=9, path="decode")
+    fake = ctypes.c_void_p(1 << 20)
+    m = moe.binding.moe_mat(fake.value, None)
+    w = moe.binding.moe_weights(fake.value, None, m, m, m, m, m, m)
+    assert lib.moe_layer_forward(ctypes.byref(c), fake, ctypes.byref(w), fake, None, fake, 1 << 40, None) == 2
+
+
+def test_workspace_monotone(moe):
+    lib = moe.load()
+    base = dict(T=64, d=512, E=32, k=4, F=256, Fs=256)
+    b0 = lib.moe_workspace_bytes(ctypes.byref(_cfg(moe, **base)))
+    assert b0 > 0
+    for key, bigger in (("T", 65), ("d", 576), ("E", 40), ("k", 5), ("F", 320), ("Fs", 320)):
+        c = _cfg(moe, **dict(base, **{key: bigger}))
+        assert lib.moe_workspace_bytes(ctypes.byref(c)) >= b0, key
+    # c5-sized layer: the workspace holds slot rows, h and the lists (~1 GB)
+    c5 = _cfg(moe, T=4096, d=6144, E=256, k=8, F=2048, Fs=2048)
+    n = lib.moe_workspace_bytes(ctypes.byref(c5))
+    assert 0.9e9 < n < 1.2e9
