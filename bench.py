@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X.
+
+One step = one moe_layer_forward (router -> top-k -> grouping -> experts ->
+combine) over one batch of seeded synthetic input.  Default workload: c2, the
+DeepSeek-Flash-style decode layer (T = 1, d = 4096, 256 experts, top-6
+sqrt(softplus) x1.5, F = 2048 + a shared expert, int8 blocks of 32 with an
+fp16 scale, bf16 activations).
+
+Decode steps walk 1024 distinct tokens and rotate over several full copies of
+the layer's weights (27 GB for c2), so the 256 MB Infinity Cache cannot serve
+one step's expert weights to the next: every step reads its experts from HBM.
+Prefill workloads (--workload c4 / c5) run one layer copy (19 GB, far beyond
+any cache) on a fixed batch.
+
+Output: one JSON line.  `value` = tokens per second of the whole timed region
+(inputs resident in HBM).  `roofline` describes the dominant kernel (the
+gate/up stage): algorithmic bytes per launch divided by its average duration,
+measured live with HIP events recorded on the library's stream.  `traffic` is
+the HBM byte count from rocprofv3 counters recorded in profiles/traffic.json,
+or null when that record was taken on a different version of the kernel
+source.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFS = 2500.0
+
+WORKLOADS = {
+    "c2": dict(base="c2", T=1, copies=4, steps=200, warmup=20),
+    "c3": dict(base="c3", T=1, copies=4, steps=200, warmup=20),
+    "c3t2": dict(base="c3", T=2, copies=4, steps=200, warmup=20),
+    "c4": dict(base="c4", T=512, copies=1, steps=20, warmup=5),
+    "c5": dict(base="c5", T=4096, copies=1, steps=10, warmup=3),
+}
+N_DECODE_TOKENS = 1024
+
+
+def describe(cfg):
+    w = {"q8b32": "int8 blocks of 32 + fp16 scale", "bf16": "bf16", "f32": "fp32"}[cfg["w"]]
+    score = "sqrt(softplus) x%.1f" % cfg["scale"] if cfg["score"] == "sqrt_softplus" else "sigmoid+bias"
+    return ("%s: T=%d d=%d E=%d top-%d %s F=%d + shared F=%d, %s weights, %s activations"
+            % (cfg["name"], cfg["T"], cfg["d"], cfg["E"], cfg["k"], score, cfg["F"], cfg["Fs"], w, cfg["act"]))
+
+
+class Hip:
+    """The few HIP runtime calls bench needs (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+    def sync(self, e):
+        assert self.lib.hipEventSynchronize(e) == 0
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def gen_weights_host(cfg):
+    from synth import configs
+    L = {w: configs.gen_mat(cfg, w) for w in ("gate", "up", "down", "s_gate", "s_up", "s_down")}
+    L["w_router"] = configs.gen_router(cfg)
+    L["bias"] = configs.gen_bias(cfg)
+    return L
+
+
+def upload_copies(L, n, torch):
+    import numpy as np
+
+    def dev(a):
+        if a is None:
+            return None
+        if isinstance(a, tuple):
+            return tuple(dev(p) for p in a)
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+    first = {k: dev(v) for k, v in L.items()}
+    copies = [first]
+    for _ in range(n - 1):
+        copies.append({k: (None if v is None else tuple(p.clone() for p in v) if isinstance(v, tuple) else v.clone())
+                       for k, v in first.items()})
+    return copies
+
+
+def expert_bytes(cfg, n_mats=3):
+    per = cfg["F"] * cfg["d"]
+    b = {"q8b32": per + per // 16, "bf16": 2 * per, "f32": 4 * per}[cfg["w"]]
+    return n_mats * b
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+DOMINANT = {  # kernel name prefix and the sources it is built from
+    "decode": ("gateup_gemv_kernel", ["sparse_moe_layer_02_amd/csrc/gemv_ffn.hip",
+                                      "sparse_moe_layer_02_amd/csrc/common.h"]),
+    "prefill": ("gateup_mfma_kernel", ["sparse_moe_layer_02_amd/csrc/grouped_gemm.hip",
+                                       "sparse_moe_layer_02_amd/csrc/common.h"]),
+}
+
+
+def traffic_record(path_kind, workload):
+    """HBM bytes per launch of the dominant kernel from profiles/traffic.json,
+    if it was measured on the current kernel source."""
+    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(rec_path):
+        return None
+    with open(rec_path) as f:
+        recs = json.load(f)
+    kname, srcs = DOMINANT[path_kind]
+    r = recs.get(workload)
+    if not r or r.get("kernel") != kname or r.get("source_sha") != source_sha(srcs):
+        return None
+    return r.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, L, x_rows, T_unit):
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    from oracle import Oracle
+    orc = Oracle()
+    threads = orc.threads()
+    n = x_rows.shape[0]
+    Ls = dict(L)
+    Ls["x"] = np.ascontiguousarray(x_rows)
+    t0 = time.perf_counter()
+    orc.layer_forward(cfg, Ls, debug=False)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d tokens of the same workload in one call (token-major fp64 oracle, %d OpenMP threads),"
+                      " %.1f s wall" % (n, threads, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=None, help="weight copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the MoE layer on a single MI355X "
+              "(see DESIGN.md for how it would shard); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sparse_moe_layer_02_amd as moe
+    from synth import configs
+
+    spec = WORKLOADS[args.workload]
+    steps = args.steps or spec["steps"]
+    warmup = spec["warmup"] if args.warmup is None else args.warmup
+    cfg = configs.get(spec["base"], T=spec["T"])
+    T = cfg["T"]
+    decode = T <= moe.DECODE_MAX_TOKENS
+    n_copies = args.copies or spec["copies"]
+    torch.cuda.init()
+    moe.load()
+    hip = Hip()
+
+    t_gen = time.perf_counter()
+    L = gen_weights_host(cfg)
+    copies = upload_copies(L, n_copies, torch)
+    if decode:
+        x_all = configs.gen_x(cfg, N_DECODE_TOKENS, stream=configs.S_DECODE)
+    else:
+        x_all = configs.gen_x(cfg)
+    x_dev = torch.from_numpy(x_all.view(np.int16) if x_all.dtype == np.uint16 else x_all).cuda()
+    t_gen = time.perf_counter() - t_gen
+
+    c = moe.config_from(cfg)
+    ws = moe.workspace(c)
+    y = torch.empty((T, cfg["d"]), dtype=torch.float32, device="cuda")
+    Wc = [moe.make_weights(cp) for cp in copies]
+    stream = torch.cuda.current_stream().cuda_stream
+    n_tok_rows = x_dev.shape[0]
+
+    def step(i, events=None, dbg=None):
+        r = (i * T) % n_tok_rows if decode else 0
+        moe.moe_layer_forward(c, x_dev[r:r + T], Wc[i % n_copies], y, ws, debug=dbg, stream=stream,
+                              stage_events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region ----------------------------------------------------
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    hip.record(e0, stream)
+    for i in range(steps):
+        step(warmup + i)
+    hip.record(e1, stream)
+    hip.sync(e1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = hip.ms(e0, e1)
+    ms_per_step = total_ms / steps
+
+    # ---- stage pass: the same steps with HIP events at every stage boundary --
+    ev = [[hip.event() for _ in range(moe.binding.STAGE_EVENTS)] for _ in range(steps)]
+    idx_log = torch.empty((steps, T, cfg["k"]), dtype=torch.int32, device="cuda")
+    for i in range(steps):
+        arr = (ctypes.c_void_p * moe.binding.STAGE_EVENTS)(*[e.value for e in ev[i]])
+        step(warmup + i, events=arr, dbg={"topk_idx": idx_log[i]})
+    torch.cuda.synchronize()
+    stage_ms = np.zeros((steps, len(moe.binding.STAGES)))
+    for i in range(steps):
+        for s in range(len(moe.binding.STAGES)):
+            stage_ms[i, s] = hip.ms(ev[i][s], ev[i][s + 1])
+    for row in ev:
+        for e in row:
+            hip.destroy(e)
+    stages_us = {name: round(float(stage_ms[:, s].mean()) * 1e3, 2) for s, name in enumerate(moe.binding.STAGES)}
+
+    # ---- algorithmic work -------------------------------------------------
+    idx_np = idx_log.cpu().numpy()
+    unions = np.array([len(np.unique(idx_np[i])) for i in range(steps)])
+    n_exp = unions.astype(np.float64) + cfg["n_shared"]       # experts whose weights a step must read
+    router_bytes = cfg["E"] * cfg["d"] * 4
+    act_bytes = 2 if cfg["act"] == "bf16" else 4
+    layer_bytes = n_exp * expert_bytes(cfg) + router_bytes + T * cfg["d"] * (act_bytes + 4)
+    gu_bytes = n_exp * expert_bytes(cfg, 2)
+    flops_gu = 2.0 * (T * cfg["k"] + T * cfg["n_shared"]) * cfg["d"] * 2 * cfg["F"]
+    if not decode:  # the GEMM also reads the gathered rows of x and writes h
+        gu_bytes = gu_bytes + T * cfg["d"] * act_bytes + (T * cfg["k"] + T) * cfg["F"] * act_bytes
+    gu_us = stages_us["gate_up"]
+    achieved = float(np.mean(gu_bytes)) / (gu_us * 1e-6) / 1e9
+    path_kind = "decode" if decode else "prefill"
+    traffic = traffic_record(path_kind, args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": DOMINANT[path_kind][0], "bytes_per_launch": float(np.mean(gu_bytes)),
+                "avg_launch_us": gu_us}
+
+    value = T * steps / (total_ms * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if decode else "bf16",
+        "data": "synthetic (seeded counter-based generator; random-init weights of the layer's shape)",
+        "config": {"workload": describe(cfg), "T": T, "d_model": cfg["d"], "n_expert": cfg["E"],
+                   "top_k": cfg["k"], "d_ff": cfg["F"], "weights": cfg["w"], "activations": cfg["act"],
+                   "path": path_kind, "weight_copies": n_copies,
+                   "distinct_tokens": n_tok_rows if decode else T},
+        "roofline": roofline,
+        "layer_hbm_GBs": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
+        "layer_hbm_frac": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_bytes": float(np.mean(layer_bytes)),
+        "expert_union_mean": float(unions.mean()),
+        "stages_us": stages_us,
+        "gate_up_tflops": round(flops_gu / (gu_us * 1e-6) / 1e12, 2),
+        "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "setup_s": round(t_gen, 1),
+    }
+    if not decode:
+        out["mfma_frac_gate_up"] = round(out["gate_up_tflops"] / BF16_PEAK_TFS, 4)
+
+    # ---- the oracle on the host cores -----------------------------------
+    if not args.no_cpu_baseline:
+        from oracle import Oracle
+        thr = Oracle().threads()
+        n = args.cpu_tokens or (max(8, min(64, 2 * thr)) if decode else max(4, min(32, thr)))
+        Lh = dict(L)
+        out["cpu_baseline"] = cpu_baseline(cfg, Lh, x_all[:n], T)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

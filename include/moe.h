@@ -34,7 +34,10 @@
  *    nonzero moe_status and enqueues nothing.  MOE_ERR_DEVICE reports a launch
  *    error seen right after enqueueing; faults inside kernels surface at the
  *    caller's next synchronisation.
- *  - Device pointers must be 16-byte aligned; sizes are element counts.
+ *  - Activations (x), weight tensors, router weights, slot_out, shared_out,
+ *    y and the workspace must be 16-byte aligned; the per-element arrays
+ *    (bias, logits, topk_idx, topk_w, offsets, perm_rows, inv_perm) need
+ *    4-byte alignment.  Sizes are element counts.
  *  - Layouts are row-major.  Weight tensors are [n, rows, cols] with cols the
  *    reduction dimension.  bf16 and fp16 values are passed as their bit
  *    patterns (uint16).  Q8B32 = int8 quants [n, rows, cols] plus one fp16
@@ -102,6 +105,11 @@ typedef struct {
     moe_mat s_down;         /* [1, d, Fs] */
 } moe_weights;
 
+/* Stage boundaries at which moe_layer_forward can record caller events:
+ * 0 start, 1 logits, 2 top-k, 3 permutation, 4 gate/up (SwiGLU), 5 down,
+ * 6 combine (the decode path fuses down and combine: 5 and 6 coincide). */
+#define MOE_STAGE_EVENTS 7
+
 /* Optional outputs of moe_layer_forward; any field may be NULL. */
 typedef struct {
     float *logits;      /* [T, E] */
@@ -110,6 +118,8 @@ typedef struct {
     int32_t *offsets;   /* [E+1] */
     int32_t *perm_rows; /* [T*k] */
     int32_t *inv_perm;  /* [T*k] */
+    void **stage_events; /* NULL, or MOE_STAGE_EVENTS hipEvent_t created by the caller; each
+                            non-NULL one is recorded on the stream at its stage boundary */
 } moe_debug;
 
 /* Bytes of workspace every entry point below may use for this config

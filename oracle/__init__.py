@@ -79,6 +79,7 @@ def load(path: str | None = None):
     lib.moe_ref_status_str.argtypes = [ctypes.c_int]
     lib.moe_ref_status_str.restype = ctypes.c_char_p
     lib.moe_ref_mutant.restype = ctypes.c_int
+    lib.moe_ref_threads.restype = ctypes.c_int
     if path == _build.LIB:
         _lib, _lib_path = lib, path
     return lib
@@ -215,3 +216,6 @@ class Oracle:
 
     def mutant(self):
         return self.lib.moe_ref_mutant()
+
+    def threads(self):
+        return self.lib.moe_ref_threads()

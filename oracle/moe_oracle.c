@@ -18,12 +18,23 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0
 #endif
 
 int moe_ref_mutant(void) { return ORACLE_MUTANT; }
+
+int moe_ref_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 const char *moe_ref_status_str(int status) {
     switch (status) {

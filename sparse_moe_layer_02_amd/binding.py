@@ -46,10 +46,15 @@ class moe_weights(ctypes.Structure):
                 ("s_gate", moe_mat), ("s_up", moe_mat), ("s_down", moe_mat)]
 
 
+STAGE_EVENTS = 7
+STAGES = ("router", "topk", "permute", "gate_up", "down", "combine")
+
+
 class moe_debug(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
                 ("topk_w", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
-                ("perm_rows", ctypes.c_void_p), ("inv_perm", ctypes.c_void_p)]
+                ("perm_rows", ctypes.c_void_p), ("inv_perm", ctypes.c_void_p),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_permute", "moe_expert_ffn",
@@ -185,12 +190,17 @@ def moe_combine(cfg, slot_out, shared_out, y, stream=None):
                                   _stream(stream)), lib)
 
 
-def moe_layer_forward(cfg, x, weights: moe_weights, y, ws, debug: dict | None = None, stream=None):
+def moe_layer_forward(cfg, x, weights: moe_weights, y, ws, debug: dict | None = None, stream=None,
+                      stage_events=None):
+    """``stage_events``: optional ctypes array of STAGE_EVENTS hipEvent_t handles."""
     lib = load()
     dbg = None
-    if debug:
+    if debug or stage_events is not None:
+        debug = debug or {}
         dbg = moe_debug(*(ptr(debug.get(k)) for k in
                           ("logits", "topk_idx", "topk_w", "offsets", "perm_rows", "inv_perm")))
+        if stage_events is not None:
+            dbg.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
     return _check(lib.moe_layer_forward(ctypes.byref(cfg), ptr(x), ctypes.byref(weights), ptr(y),
                                         ctypes.byref(dbg) if dbg else None, ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)), lib)

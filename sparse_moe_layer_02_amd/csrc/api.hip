@@ -17,9 +17,16 @@ constexpr int MAX_TOKENS = 1 << 20;
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Arrays read with 16-byte vector loads (activations, weights, the fp32 rows
+// of slot/shared/y, the workspace) must be 16-byte aligned; per-element
+// arrays (logits, indices, weights of the routing, offsets, permutation,
+// bias) need only their element alignment.
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool opt_ptr_ok(const void* p) { return p == nullptr || aligned16(p); }
+bool elt_ok(const void* p) { return p != nullptr && aligned4(p); }
+bool opt_elt_ok(const void* p) { return p == nullptr || aligned4(p); }
 
 int validate_config(const moe_config* c) {
     if (!c) return MOE_ERR_INVALID;
@@ -105,7 +112,7 @@ bool mat_ok(const moe_config* c, const moe_mat& m) {
 
 int check_weights(const moe_config* c, const moe_weights* w, bool router) {
     if (!w) return MOE_ERR_INVALID;
-    if (router && (!ptr_ok(w->w_router) || !opt_ptr_ok(w->bias))) return MOE_ERR_INVALID;
+    if (router && (!ptr_ok(w->w_router) || !opt_elt_ok(w->bias))) return MOE_ERR_INVALID;
     if (!mat_ok(c, w->gate) || !mat_ok(c, w->up) || !mat_ok(c, w->down)) return MOE_ERR_INVALID;
     if (c->n_shared && (!mat_ok(c, w->s_gate) || !mat_ok(c, w->s_up) || !mat_ok(c, w->s_down)))
         return MOE_ERR_INVALID;
@@ -182,6 +189,12 @@ hipError_t run_expert_kernels(const FfnArgs& f, hipStream_t st) {
     return launch_down_slots_gemv(f, st);
 }
 
+// Record the caller's stage event i (if any) on the stream.
+hipError_t mark(const moe_debug* dbg, int i, hipStream_t st) {
+    if (!dbg || !dbg->stage_events || !dbg->stage_events[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(dbg->stage_events[i]), st);
+}
+
 SelectArgs select_args(const moe_config* c, const float* logits, const float* bias, int32_t* idx,
                        float* w) {
     SelectArgs s;
@@ -222,8 +235,8 @@ int moe_route(const moe_config* cfg, const void* x, const float* w_router, const
               float* logits, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
     int s = validate_config(cfg);
     if (s) return s;
-    if (!ptr_ok(x) || !ptr_ok(w_router) || !opt_ptr_ok(bias) || !opt_ptr_ok(logits) || !ptr_ok(topk_idx) ||
-        !ptr_ok(topk_w))
+    if (!ptr_ok(x) || !ptr_ok(w_router) || !opt_elt_ok(bias) || !opt_elt_ok(logits) || !elt_ok(topk_idx) ||
+        !elt_ok(topk_w))
         return MOE_ERR_INVALID;
     if (!logits && (s = check_ws(cfg, ws, ws_bytes))) return s;
     const Layout L = make_layout(cfg);
@@ -240,7 +253,7 @@ int moe_select(const moe_config* cfg, const float* logits, const float* bias, in
                float* topk_w, void* stream) {
     int s = validate_config(cfg);
     if (s) return s;
-    if (!ptr_ok(logits) || !opt_ptr_ok(bias) || !ptr_ok(topk_idx) || !ptr_ok(topk_w)) return MOE_ERR_INVALID;
+    if (!elt_ok(logits) || !opt_elt_ok(bias) || !elt_ok(topk_idx) || !elt_ok(topk_w)) return MOE_ERR_INVALID;
     SelectArgs a = select_args(cfg, logits, bias, topk_idx, topk_w);
     a.generic_only = cfg->path == MOE_PATH_PREFILL;  // lets tests reach the generic kernel at E = 256
     return device_status(launch_topk(a, static_cast<hipStream_t>(stream)));
@@ -250,7 +263,7 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* offsets
                 int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
     int s = validate_config(cfg);
     if (s) return s;
-    if (!ptr_ok(topk_idx) || !ptr_ok(offsets) || !ptr_ok(perm_rows) || !ptr_ok(inv_perm)) return MOE_ERR_INVALID;
+    if (!elt_ok(topk_idx) || !elt_ok(offsets) || !elt_ok(perm_rows) || !elt_ok(inv_perm)) return MOE_ERR_INVALID;
     if ((s = check_ws(cfg, ws, ws_bytes))) return s;
     const Layout L = make_layout(cfg);
     PermArgs p = perm_args(cfg, L, ws, topk_idx, offsets, perm_rows, inv_perm);
@@ -263,7 +276,7 @@ int moe_expert_ffn(const moe_config* cfg, const void* x, const moe_weights* w, c
     int s = validate_config(cfg);
     if (s) return s;
     if ((s = check_weights(cfg, w, false))) return s;
-    if (!ptr_ok(x) || !ptr_ok(offsets) || !ptr_ok(perm_rows) || !ptr_ok(topk_w) || !ptr_ok(slot_out))
+    if (!ptr_ok(x) || !elt_ok(offsets) || !elt_ok(perm_rows) || !elt_ok(topk_w) || !ptr_ok(slot_out))
         return MOE_ERR_INVALID;
     if (cfg->n_shared && !ptr_ok(shared_out)) return MOE_ERR_INVALID;
     if ((s = check_ws(cfg, ws, ws_bytes))) return s;
@@ -293,8 +306,8 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     if (s) return s;
     if ((s = check_weights(cfg, w, true))) return s;
     if (!ptr_ok(x) || !ptr_ok(y)) return MOE_ERR_INVALID;
-    if (dbg && (!opt_ptr_ok(dbg->logits) || !opt_ptr_ok(dbg->topk_idx) || !opt_ptr_ok(dbg->topk_w) ||
-                !opt_ptr_ok(dbg->offsets) || !opt_ptr_ok(dbg->perm_rows) || !opt_ptr_ok(dbg->inv_perm)))
+    if (dbg && (!opt_elt_ok(dbg->logits) || !opt_elt_ok(dbg->topk_idx) || !opt_elt_ok(dbg->topk_w) ||
+                !opt_elt_ok(dbg->offsets) || !opt_elt_ok(dbg->perm_rows) || !opt_elt_ok(dbg->inv_perm)))
         return MOE_ERR_INVALID;
     const bool decode = cfg->path == MOE_PATH_DECODE ||
                         (cfg->path == MOE_PATH_AUTO && cfg->n_tokens <= MOE_DECODE_MAX_TOKENS);
@@ -311,22 +324,39 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     int32_t* inv = dbg && dbg->inv_perm ? dbg->inv_perm : at<int32_t>(ws, L.inv_perm);
 
     RouteArgs r{x, w->w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, logits, !decode};
-    hipError_t e = launch_router_logits(r, st);
+    hipError_t e = mark(dbg, 0, st);
+    if (e == hipSuccess) e = launch_router_logits(r, st);
+    if (e == hipSuccess) e = mark(dbg, 1, st);
     if (e == hipSuccess) e = launch_topk(select_args(cfg, logits, w->bias, idx, wts), st);
+    if (e == hipSuccess) e = mark(dbg, 2, st);
     if (e == hipSuccess) e = launch_permute(perm_args(cfg, L, ws, idx, off, perm, inv), st);
+    if (e == hipSuccess) e = mark(dbg, 3, st);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     FfnArgs f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
     if (decode) {
         f.y = y;
         e = launch_gateup_gemv(f, st);
+        if (e == hipSuccess) e = mark(dbg, 4, st);
         if (e == hipSuccess) e = launch_down_combine_gemv(f, st);
+        if (e == hipSuccess) e = mark(dbg, 5, st);
+        if (e == hipSuccess) e = mark(dbg, 6, st);
         return device_status(e);
     }
-    e = run_expert_kernels(f, st);
+    if (f.wdt == MOE_DT_BF16) {
+        e = launch_gateup_mfma(f, st);
+        if (e == hipSuccess) e = mark(dbg, 4, st);
+        if (e == hipSuccess) e = launch_down_mfma(f, st);
+    } else {
+        e = launch_gateup_gemv(f, st);
+        if (e == hipSuccess) e = mark(dbg, 4, st);
+        if (e == hipSuccess) e = launch_down_slots_gemv(f, st);
+    }
+    if (e == hipSuccess) e = mark(dbg, 5, st);
     if (e == hipSuccess) {
         CombineArgs c{f.slot_out, f.shared_out, y, cfg->n_tokens, cfg->top_k, cfg->d_model};
         e = launch_combine(c, st);
     }
+    if (e == hipSuccess) e = mark(dbg, 6, st);
     return device_status(e);
 }
 

@@ -81,7 +81,8 @@ def test_null_and_misaligned_pointers(moe):
     fake = ctypes.c_void_p(1 << 20)
     odd = ctypes.c_void_p((1 << 20) + 4)
     assert lib.moe_select(ctypes.byref(c), None, None, fake, fake, None) == 1
-    assert lib.moe_select(ctypes.byref(c), odd, None, fake, fake, None) == 1
+    odd1 = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.moe_select(ctypes.byref(c), odd1, None, fake, fake, None) == 1
     assert lib.moe_combine(ctypes.byref(c), fake, odd, fake, None) == 1
     assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, fake, fake, None, 0, None) == 1
     assert lib.moe_permute(ctypes.byref(c), fake, fake, None, fake, fake, 1 << 40, None) == 1
