@@ -129,15 +129,20 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-DOMINANT = {  # kernel name prefix and the sources it is built from
-    "decode": ("gateup_gemv_kernel", ["sparse_moe_layer_02_amd/csrc/gemv_ffn.hip",
-                                      "sparse_moe_layer_02_amd/csrc/common.h"]),
-    "prefill": ("gateup_mfma_kernel", ["sparse_moe_layer_02_amd/csrc/grouped_gemm.hip",
-                                       "sparse_moe_layer_02_amd/csrc/common.h"]),
+_CSRC = "sparse_moe_layer_02_amd/csrc/"
+DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it is built from
+    ("decode", "any"): ("decode_gateup_kernel", [_CSRC + f for f in (
+        "decode.hip", "gemv_dev.h", "route_dev.h", "permute_dev.h", "common.h")]),
+    ("prefill", "bf16"): ("gateup_mfma_kernel", [_CSRC + f for f in ("grouped_gemm.hip", "common.h")]),
+    ("prefill", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
 }
 
 
-def traffic_record(path_kind, workload):
+def dominant(path_kind, w):
+    return DOMINANT.get((path_kind, w)) or DOMINANT[(path_kind, "any")]
+
+
+def traffic_record(path_kind, w, workload):
     """HBM bytes per launch of the dominant kernel from profiles/traffic.json,
     if it was measured on the current kernel source."""
     rec_path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -145,7 +150,7 @@ def traffic_record(path_kind, workload):
         return None
     with open(rec_path) as f:
         recs = json.load(f)
-    kname, srcs = DOMINANT[path_kind]
+    kname, srcs = dominant(path_kind, w)
     r = recs.get(workload)
     if not r or r.get("kernel") != kname or r.get("source_sha") != source_sha(srcs):
         return None
@@ -176,6 +181,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated across steps")
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"],
+                    help="force the decode (GEMV) or prefill (grouped GEMM) path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     args = ap.parse_args()
@@ -196,7 +203,7 @@ def main():
     warmup = spec["warmup"] if args.warmup is None else args.warmup
     cfg = configs.get(spec["base"], T=spec["T"])
     T = cfg["T"]
-    decode = T <= moe.DECODE_MAX_TOKENS
+    decode = args.path == "decode" or (args.path == "auto" and T <= moe.DECODE_MAX_TOKENS)
     n_copies = args.copies or spec["copies"]
     torch.cuda.init()
     moe.load()
@@ -205,14 +212,14 @@ def main():
     t_gen = time.perf_counter()
     L = gen_weights_host(cfg)
     copies = upload_copies(L, n_copies, torch)
-    if decode:
+    if T <= moe.DECODE_MAX_TOKENS:
         x_all = configs.gen_x(cfg, N_DECODE_TOKENS, stream=configs.S_DECODE)
     else:
         x_all = configs.gen_x(cfg)
     x_dev = torch.from_numpy(x_all.view(np.int16) if x_all.dtype == np.uint16 else x_all).cuda()
     t_gen = time.perf_counter() - t_gen
 
-    c = moe.config_from(cfg)
+    c = moe.config_from(cfg, path=args.path)
     ws = moe.workspace(c)
     y = torch.empty((T, cfg["d"]), dtype=torch.float32, device="cuda")
     Wc = [moe.make_weights(cp) for cp in copies]
@@ -220,7 +227,7 @@ def main():
     n_tok_rows = x_dev.shape[0]
 
     def step(i, events=None, dbg=None):
-        r = (i * T) % n_tok_rows if decode else 0
+        r = (i * T) % n_tok_rows if n_tok_rows > T else 0
         moe.moe_layer_forward(c, x_dev[r:r + T], Wc[i % n_copies], y, ws, debug=dbg, stream=stream,
                               stage_events=events)
 
@@ -272,10 +279,10 @@ def main():
     gu_us = stages_us["gate_up"]
     achieved = float(np.mean(gu_bytes)) / (gu_us * 1e-6) / 1e9
     path_kind = "decode" if decode else "prefill"
-    traffic = traffic_record(path_kind, args.workload)
+    traffic = traffic_record(path_kind, cfg["w"], args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": DOMINANT[path_kind][0], "bytes_per_launch": float(np.mean(gu_bytes)),
+                "kernel": dominant(path_kind, cfg["w"])[0], "bytes_per_launch": float(np.mean(gu_bytes)),
                 "avg_launch_us": gu_us}
 
     value = T * steps / (total_ms * 1e-3)

@@ -89,6 +89,7 @@ Layout make_layout(const moe_config* c) {
     L.h = take((n + (c->n_shared ? T : 0)) * (size_t)ldh_of(c) * hsz);
     L.slot_out = take(n * d * 4);
     L.shared_out = take(c->n_shared ? T * d * 4 : 0);
+    L.scores = take(T * E * 4);
     L.total = o;
     return L;
 }
@@ -175,6 +176,8 @@ FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, 
     f.shared_out = c->n_shared ? at<float>(ws, L.shared_out) : nullptr;
     f.y = nullptr;
     f.max_tiles = L.max_tiles;
+    f.shared_done = 0;
+    f.grid_has_shared = 0;
     return f;
 }
 
@@ -325,6 +328,18 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
 
     RouteArgs r{x, w->w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, logits, !decode};
     hipError_t e = mark(dbg, 0, st);
+    if (decode) {
+        // router + shared gate/up | selection + routed gate/up | down with the combine
+        DecodeRouteArgs dr;
+        dr.r = r;
+        dr.s = select_args(cfg, logits, w->bias, idx, wts);
+        dr.p = perm_args(cfg, L, ws, idx, off, perm, inv);
+        dr.f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
+        dr.f.y = y;
+        dr.scores = at<float>(ws, L.scores);
+        if (e == hipSuccess) e = launch_decode(dr, dbg, mark, st);
+        return device_status(e);
+    }
     if (e == hipSuccess) e = launch_router_logits(r, st);
     if (e == hipSuccess) e = mark(dbg, 1, st);
     if (e == hipSuccess) e = launch_topk(select_args(cfg, logits, w->bias, idx, wts), st);
@@ -333,15 +348,6 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     if (e == hipSuccess) e = mark(dbg, 3, st);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     FfnArgs f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
-    if (decode) {
-        f.y = y;
-        e = launch_gateup_gemv(f, st);
-        if (e == hipSuccess) e = mark(dbg, 4, st);
-        if (e == hipSuccess) e = launch_down_combine_gemv(f, st);
-        if (e == hipSuccess) e = mark(dbg, 5, st);
-        if (e == hipSuccess) e = mark(dbg, 6, st);
-        return device_status(e);
-    }
     if (f.wdt == MOE_DT_BF16) {
         e = launch_gateup_mfma(f, st);
         if (e == hipSuccess) e = mark(dbg, 4, st);

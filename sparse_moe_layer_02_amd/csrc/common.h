@@ -41,86 +41,77 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 
 // ---------------------------------------------------------------------------
-// Wavefront reductions.  Butterfly order: xor 1, xor 2 (quad permutes), half-
-// row mirror, row mirror (DPP), then xor 16 and xor 32 through the LDS
-// crossbar.  Every lane ends with the same value; the order of operations is
-// fixed, so the result is deterministic.
+// Wavefront reductions, all on the VALU (no LDS-crossbar round trips): an
+// inclusive scan inside each 16-lane row with DPP row_shr 1, 2, 4, 8 (lanes
+// shifted in from outside the row read 0), then row_bcast15 (rows 1 and 3 add
+// the last lane of the row below) and row_bcast31 (rows 2 and 3 add lane 31),
+// which leaves the wavefront total in lane 63; v_readlane makes it uniform.
+// The order of operations is fixed, so the result is deterministic.
 // ---------------------------------------------------------------------------
-template <int CTRL>
+template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
 }
-constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int DPP_HALF_MIRROR = 0x141;
-constexpr int DPP_MIRROR = 0x140;
-
-__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
-    // ds_swizzle bitmask mode: and 0x1F, xor 0x10 (swaps lanes 16 apart inside each 32)
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-}
-__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
-    return (uint32_t)__shfl_xor((int)v, 32);
-}
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
 
 template <class Op>
 __device__ __forceinline__ float wave_reduce_f32(float v, Op op) {
-    v = op(v, __uint_as_float(dpp_u32<DPP_XOR1>(__float_as_uint(v))));
-    v = op(v, __uint_as_float(dpp_u32<DPP_XOR2>(__float_as_uint(v))));
-    v = op(v, __uint_as_float(dpp_u32<DPP_HALF_MIRROR>(__float_as_uint(v))));
-    v = op(v, __uint_as_float(dpp_u32<DPP_MIRROR>(__float_as_uint(v))));
-    v = op(v, __uint_as_float(xor16_u32(__float_as_uint(v))));
-    v = op(v, __uint_as_float(xor32_u32(__float_as_uint(v))));
-    return v;
+    v = op(v, __uint_as_float(dpp_u32<DPP_ROW_SHR1>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_ROW_SHR2>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_ROW_SHR4>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_ROW_SHR8>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_ROW_BCAST15, 0xA>(__float_as_uint(v))));
+    v = op(v, __uint_as_float(dpp_u32<DPP_ROW_BCAST31, 0xC>(__float_as_uint(v))));
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 struct AddF { __device__ float operator()(float a, float b) const { return a + b; } };
 
+// Sum over the 64 lanes; every lane receives the same total.
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce_f32(v, AddF()); }
 
-template <int CTRL>
+template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ double dpp_f64(double v) {
-    uint64_t u = __double_as_longlong(v);
-    uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
-    return __longlong_as_double(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ double xor16_f64(double v) {
-    uint64_t u = __double_as_longlong(v);
-    uint32_t lo = xor16_u32((uint32_t)u), hi = xor16_u32((uint32_t)(u >> 32));
-    return __longlong_as_double(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ double xor32_f64(double v) {
-    uint64_t u = __double_as_longlong(v);
-    uint32_t lo = xor32_u32((uint32_t)u), hi = xor32_u32((uint32_t)(u >> 32));
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)u), hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(u >> 32));
     return __longlong_as_double(((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-    v += dpp_f64<DPP_XOR1>(v);
-    v += dpp_f64<DPP_XOR2>(v);
-    v += dpp_f64<DPP_HALF_MIRROR>(v);
-    v += dpp_f64<DPP_MIRROR>(v);
-    v += xor16_f64(v);
-    v += xor32_f64(v);
-    return v;
+    v += dpp_f64<DPP_ROW_SHR1>(v);
+    v += dpp_f64<DPP_ROW_SHR2>(v);
+    v += dpp_f64<DPP_ROW_SHR4>(v);
+    v += dpp_f64<DPP_ROW_SHR8>(v);
+    v += dpp_f64<DPP_ROW_BCAST15, 0xA>(v);
+    v += dpp_f64<DPP_ROW_BCAST31, 0xC>(v);
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, 63), hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), 63);
+    return __longlong_as_double(((uint64_t)hi << 32) | lo);
 }
 
-// Wave-wide maximum of an unsigned 64-bit key.
+// Wave-wide maximum of an unsigned 64-bit key (0 is the neutral element).
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
-template <int CTRL>
+template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)v), hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = u64_max(v, dpp_u64<DPP_XOR1>(v));
-    v = u64_max(v, dpp_u64<DPP_XOR2>(v));
-    v = u64_max(v, dpp_u64<DPP_HALF_MIRROR>(v));
-    v = u64_max(v, dpp_u64<DPP_MIRROR>(v));
-    v = u64_max(v, ((uint64_t)xor16_u32((uint32_t)(v >> 32)) << 32) | xor16_u32((uint32_t)v));
-    v = u64_max(v, ((uint64_t)xor32_u32((uint32_t)(v >> 32)) << 32) | xor32_u32((uint32_t)v));
-    return v;
+    v = u64_max(v, dpp_u64<DPP_ROW_SHR1>(v));
+    v = u64_max(v, dpp_u64<DPP_ROW_SHR2>(v));
+    v = u64_max(v, dpp_u64<DPP_ROW_SHR4>(v));
+    v = u64_max(v, dpp_u64<DPP_ROW_SHR8>(v));
+    v = u64_max(v, dpp_u64<DPP_ROW_BCAST15, 0xA>(v));
+    v = u64_max(v, dpp_u64<DPP_ROW_BCAST31, 0xC>(v));
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Index of this wavefront in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_index() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
+}
 
 // Lanes below this one, as a 64-bit mask.
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -134,13 +125,13 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // ---------------------------------------------------------------------------
 struct Layout {
     size_t logits, topk_idx, topk_w, offsets, perm_rows, inv_perm;
-    size_t blk_hist, blk_base, meta, active, tiles, h, slot_out, shared_out, total;
+    size_t blk_hist, blk_base, meta, active, tiles, h, slot_out, shared_out, scores, total;
     int n_blk;       // permutation blocks of PERM_BLOCK assignments
     int max_tiles;   // capacity of the grouped-GEMM tile list
 };
 
 // Meta words at ws + meta: [0] n_active experts, [1] n_tiles, [2] valid
-// assignments, [3..15] reserved (sync counters, kept zero between calls).
+// assignments, the rest reserved.
 constexpr int META_WORDS = 16;
 constexpr int PERM_BLOCK = 256;     // assignments per permutation block (one wave)
 constexpr int GEMM_BM = 64;         // rows per grouped-GEMM tile (tile list granularity)

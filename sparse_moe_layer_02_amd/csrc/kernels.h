@@ -71,16 +71,29 @@ struct FfnArgs {
     float* shared_out;      // [T, d]
     float* y;               // [T, d] (fused combine)
     int max_tiles;
+    int shared_done;        // the shared expert's h rows were already produced (decode route kernel)
+    int grid_has_shared;    // set by the launchers: the last grid slot is the shared expert
 };
 // gate/up GEMV over the active experts (and the shared one) -> h
 hipError_t launch_gateup_gemv(const FfnArgs& a, hipStream_t st);
-// down GEMV + weighted combine straight into y (T <= MOE_DECODE_MAX_TOKENS)
-hipError_t launch_down_combine_gemv(const FfnArgs& a, hipStream_t st);
 // down GEMV writing weighted slot rows and the shared rows
 hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st);
 // grouped bf16 MFMA GEMMs (prefill)
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st);
 hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st);
+
+// The decode path (T <= MOE_DECODE_MAX_TOKENS) in three launches: router +
+// shared gate/up; selection + grouping + routed gate/up; down + combine into
+// f.y.  `mark` records the caller's stage events between launches.
+struct DecodeRouteArgs {
+    RouteArgs r;
+    SelectArgs s;
+    PermArgs p;
+    FfnArgs f;
+    float* scores;  // [T, E] fp32 router scores (workspace)
+};
+hipError_t launch_decode(const DecodeRouteArgs& a, const moe_debug* dbg,
+                         hipError_t (*mark)(const moe_debug*, int, hipStream_t), hipStream_t st);
 
 struct CombineArgs {
     const float* slot_out;

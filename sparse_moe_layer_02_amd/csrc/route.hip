@@ -19,6 +19,7 @@
 // sum rounds to the same fp32 value except in vanishingly rare cases.
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 #pragma clang fp contract(off)
 
@@ -165,31 +166,8 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wavefront per token.  Lane l holds experts l, l+64, ... as packed
-// 64-bit keys  (orderable fp32 key) << 32 | (0xFFFFFFFF - e)  so that one
-// unsigned maximum picks the larger key and, on equal keys, the lower index.
-// NaN keys map below every number; -0 is folded onto +0.  k rounds of a
-// wave-wide DPP maximum select the experts in rank order; the selected scores
-// are summed in fp64 in that order and the weights formed in fp64.
+// Top-k: one wavefront per token (topk_token in route_dev.h).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float router_score(int kind, float logit) {
-    const double l = (double)logit;
-    if (kind == MOE_SCORE_SIGMOID) return (float)(1.0 / (1.0 + exp(-l)));
-    const double sp = l > 0.0 ? l + log1p(exp(-l)) : log1p(exp(l));
-    return (float)sqrt(sp);
-}
-
-__device__ __forceinline__ uint64_t pack_key(float key, int e) {
-    uint32_t u = __float_as_uint(key);
-    uint32_t ord;
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) ord = 0u;  // NaN: below -inf
-    else {
-        if (u == 0x80000000u) u = 0u;  // -0 == +0
-        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
 template <int KPL, int EFIX>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ bias, int T, int E_rt,
@@ -197,54 +175,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w) {
     const int E = EFIX ? EFIX : E_rt;
-    const int lane = lane_id();
     const int t = blockIdx.x * 4 + threadIdx.x / WAVE;
     if (t >= T) return;
-    const float* lrow = logits + (size_t)t * E;
-    uint64_t key[KPL];
-    float sc[KPL];
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-        const int e = lane + WAVE * j;
-        if (e < E) {
-            const float s = router_score(score_kind, lrow[e]);
-            const float kf = bias ? s + bias[e] : s;
-            sc[j] = s;
-            key[j] = pack_key(kf, e);
-        } else {
-            sc[j] = 0.0f;
-            key[j] = 0ull;
-        }
-    }
-    int my_idx = 0;
-    float my_s = 0.0f;
-    double S = 0.0;
-    for (int r = 0; r < k; ++r) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int j = 1; j < KPL; ++j) best = u64_max(best, key[j]);
-        best = wave_max_u64(best);
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-        const int owner = e % WAVE, slot = e / WAVE;
-        float s_owned = 0.0f;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-            if (lane == owner && j == slot) {
-                s_owned = sc[j];
-                key[j] = 0ull;
-            }
-        }
-        const float s_sel = __shfl(s_owned, owner);
-        S += (double)s_sel;
-        if (lane == r) {
-            my_idx = e;
-            my_s = s_sel;
-        }
-    }
-    if (lane < k) {
-        topk_idx[(size_t)t * k + lane] = my_idx;
-        topk_w[(size_t)t * k + lane] = S > 0.0 ? (float)(((double)my_s / S) * (double)route_scale) : 0.0f;
-    }
+    topk_token<KPL, EFIX>(logits + (size_t)t * E, bias, E, k, score_kind, route_scale,
+                          topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
 
 // ---------------------------------------------------------------------------
