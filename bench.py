@@ -183,6 +183,8 @@ def main():
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated across steps")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"],
                     help="force the decode (GEMV) or prefill (grouped GEMM) path")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the steps in a HIP graph (64 steps per graph) and replay it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     args = ap.parse_args()
@@ -226,22 +228,45 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     n_tok_rows = x_dev.shape[0]
 
-    def step(i, events=None, dbg=None):
+    def step(i, events=None, dbg=None, strm=None):
         r = (i * T) % n_tok_rows if n_tok_rows > T else 0
-        moe.moe_layer_forward(c, x_dev[r:r + T], Wc[i % n_copies], y, ws, debug=dbg, stream=stream,
-                              stage_events=events)
+        moe.moe_layer_forward(c, x_dev[r:r + T], Wc[i % n_copies], y, ws, debug=dbg,
+                              stream=stream if strm is None else strm, stage_events=events)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        G = 64
+        steps = max(G, (steps + G - 1) // G * G)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                step(i, strm=side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(G):
+                step(warmup + i, strm=cap)
+        graph.replay()
+        torch.cuda.synchronize()
 
     # ---- timed region ----------------------------------------------------
     e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     hip.record(e0, stream)
-    for i in range(steps):
-        step(warmup + i)
+    if graph is not None:
+        for _ in range(steps // 64):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(warmup + i)
     hip.record(e1, stream)
     hip.sync(e1)
     torch.cuda.synchronize()
@@ -294,7 +319,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; random-init weights of the layer's shape)",
         "config": {"workload": describe(cfg), "T": T, "d_model": cfg["d"], "n_expert": cfg["E"],
                    "top_k": cfg["k"], "d_ff": cfg["F"], "weights": cfg["w"], "activations": cfg["act"],
-                   "path": path_kind, "weight_copies": n_copies,
+                   "path": path_kind, "weight_copies": n_copies, "hip_graph": bool(args.graph),
                    "distinct_tokens": n_tok_rows if decode else T},
         "roofline": roofline,
         "layer_hbm_GBs": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),

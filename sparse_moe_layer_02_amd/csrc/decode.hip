@@ -6,14 +6,14 @@
 //   1. decode_router_kernel: one workgroup per expert computes that expert's
 //      router logit and score for every token (fp64, rounded once).
 //   2. decode_select_kernel: workgroup 0 runs the top-k of every token (one
-//      wavefront each) and the stable grouping, and publishes indices,
-//      weights, offsets, permutation and the active-expert list; the other
-//      workgroups compute the shared expert's gate/up rows meanwhile (they do
-//      not depend on the routing).
+//      wavefront each), then one wavefront builds the stable grouping and
+//      publishes indices, weights, offsets, permutation and the active-expert
+//      list; the other workgroups compute the shared expert's gate/up rows
+//      meanwhile (they do not depend on the routing).
 //   3. the routed experts' gate/up GEMV over the active list (gemv_ffn.hip).
 //   4. decode_down_kernel: a workgroup owns a tile of rows of y; its
 //      wavefronts take the expert slots (slot 0 the shared expert, then the
-//      active experts in ascending order), stream each slot's down-projection
+//      active experts in ascending index), stream each slot's down-projection
 //      rows once and leave per-slot partial results in LDS, which are then
 //      added in slot order - y is written once, deterministically, without
 //      atomics and without a separate combine launch.
@@ -89,6 +89,33 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeRouteArgs a) {
 constexpr int DS_THREADS = 1024;
 constexpr int DS_WAVES = DS_THREADS / WAVE;  // shared gate/up row pairs per workgroup
 
+// Exclusive prefix sum of arr[0..n) in place by one wavefront (n <= 1024);
+// returns the total.  Lane l owns the 16 consecutive entries from 16*l.
+__device__ int wave_excl_scan_array(int* arr, int n) {
+    const int lane = lane_id();
+    int loc[16], s = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int i = lane * 16 + j;
+        loc[j] = i < n ? arr[i] : 0;
+        s += loc[j];
+    }
+    int inc = s;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+    }
+    int run = inc - s;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int i = lane * 16 + j;
+        if (i < n) arr[i] = run;
+        run += loc[j];
+    }
+    return __builtin_amdgcn_readlane(inc, WAVE - 1);
+}
+
 template <int KPL, int EFIX, int WF, int AF, int MT>
 __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteArgs a) {
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_index();
@@ -101,7 +128,6 @@ __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteAr
     }
     __shared__ int32_t s_idx[MOE_DECODE_MAX_TOKENS * 32];
     __shared__ int cnt[1024];
-    __shared__ int smem[17];
     const int E = a.r.E, T = a.r.T, k = a.s.k, n = T * k;
     if (wave < T) {
         const int my = topk_token<KPL, EFIX, true>(a.scores + (size_t)wave * E, a.s.bias, E, k, a.s.score,
@@ -109,18 +135,30 @@ __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteAr
                                                    a.s.topk_w + (size_t)wave * k);
         if (lane < k) s_idx[wave * k + lane] = my;
     }
-    cnt[tid] = 0;
     __syncthreads();
-    if (tid < n) atomicAdd(&cnt[s_idx[tid]], 1);
-    __syncthreads();
+    if (wave != 0) return;
+    // one wavefront: counts, active list, offsets, stable scatter
+    for (int e = lane; e < E; e += WAVE) cnt[e] = 0;
+    for (int f = lane; f < n; f += WAVE) atomicAdd(&cnt[s_idx[f]], 1);
+    int na = 0;
+    for (int base = 0; base < E; base += WAVE) {
+        const int e = base + lane;
+        const bool act = e < E && cnt[e] > 0;
+        const uint64_t b = __ballot(act);
+        if (act) a.p.active[na + __popcll(b & lanemask_lt())] = e;
+        na += __popcll(b);
+    }
+    const int total = wave_excl_scan_array(cnt, E);
+    for (int e = lane; e < E; e += WAVE) a.p.offsets[e] = cnt[e];
+    if (lane == 0) {
+        a.p.offsets[E] = total;
+        a.p.meta[0] = na;
+        a.p.meta[1] = 0;
+        a.p.meta[2] = total;
+    }
     PermArgs p = a.p;
     p.topk_idx = s_idx;
-    p.bm = 0;  // no GEMM tile list on this path
-    int off;
-    emit_lists(p, cnt[tid], smem, &off);
-    cnt[tid] = off;
-    __syncthreads();
-    if (tid < WAVE) scatter_range(p, 0, n, cnt);
+    scatter_range(p, 0, n, cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -138,7 +176,7 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(FfnArgs a) {
     const int T = a.T, d = a.d, k = a.k;
     const int row0 = blockIdx.x * DD_R;
     const int n_sh = a.n_shared ? 1 : 0;
-    const int n_slots = n_sh + a.meta[0];
+    const int n_slots = n_sh + a.meta[0];  // slot 0: the shared expert, then the active experts
     for (int q = tid; q < n_slots * MOE_DECODE_MAX_TOKENS * DD_R; q += DD_THREADS) (&part[0][0][0])[q] = 0.0f;
     __syncthreads();
     const int hsz = AF == MOE_DT_BF16 ? 2 : 4;

@@ -300,3 +300,47 @@ def test_permute_caller_indices(torch_cuda, orc):
         assert np.array_equal(off.cpu().numpy(), r_off)
         assert np.array_equal(perm.cpu().numpy(), r_perm)
         assert np.array_equal(inv.cpu().numpy(), r_inv)
+
+
+def test_graph_capture_replay(torch_cuda, orc):
+    """The decode and prefill paths captured in a HIP graph: every replay (with
+    eager work and synchronisations in between) reproduces the eager result."""
+    import torch
+    import sparse_moe_layer_02_amd as moe
+    for spec in (dict(T=1, d=256, E=64, k=6, F=128, w="q8b32", score="sqrt_softplus", scale=1.5, bias="none"),
+                 dict(T=2, d=256, E=48, k=8, F=128), dict(T=70, d=256, E=32, k=4, F=128)):
+        cfg = _custom(**spec)
+        say("case graph", spec)
+        L = configs.make_layer(cfg)
+        dev = H.upload_layer(L)
+        c = moe.config_from(cfg)
+        ws = moe.workspace(c)
+        W = moe.make_weights(dev)
+        xs = [H.to_dev(configs.gen_x(cfg, cfg["T"], stream=configs.S_DECODE, token0=i * cfg["T"])) for i in range(3)]
+        ys = [torch.empty((cfg["T"], cfg["d"]), dtype=torch.float32, device="cuda") for _ in range(3)]
+        eager = []
+        for x, y in zip(xs, ys):
+            moe.moe_layer_forward(c, x, W, y, ws)
+            torch.cuda.synchronize()
+            eager.append(y.clone())
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            moe.moe_layer_forward(c, xs[0], W, ys[0], ws, stream=side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream().cuda_stream
+            for x, y in zip(xs, ys):
+                moe.moe_layer_forward(c, x, W, y, ws, stream=cap)
+        for rep in range(4):
+            for y in ys:
+                y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            for y, ref in zip(ys, eager):
+                assert torch.equal(y, ref), "replay %d differs" % rep
+            # eager work between replays
+            moe.moe_layer_forward(c, xs[1], W, ys[1], ws)
+            torch.cuda.synchronize()
