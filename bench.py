@@ -131,8 +131,7 @@ def source_sha(paths):
 
 _CSRC = "sparse_moe_layer_02_amd/csrc/"
 DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it is built from
-    ("decode", "any"): ("decode_gateup_kernel", [_CSRC + f for f in (
-        "decode.hip", "gemv_dev.h", "route_dev.h", "permute_dev.h", "common.h")]),
+    ("decode", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
     ("prefill", "bf16"): ("gateup_mfma_kernel", [_CSRC + f for f in ("grouped_gemm.hip", "common.h")]),
     ("prefill", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
 }
@@ -157,18 +156,82 @@ def traffic_record(path_kind, w, workload):
     return r.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, L, x_rows, T_unit):
-    """The oracle, as it stands, on a bounded sample of the workload."""
+def _counter_rows(path):
+    """(dispatch id, kernel name, counter, value) per dispatch from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    out = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) into HBM bytes per launch of the dominant kernel.  Each counter is
+    scaled by the factor that makes it read right on the plain device copy of
+    ``copy_bytes`` (read and written once) that the same command ran."""
+    kname, srcs = dominant(path_kind, w)
+    res = {"kernel": kname, "source_sha": source_sha(srcs), "copy_bytes": copy_bytes}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(path) if r[2] == counter]
+        kern = [v for _, n, _, v in rows if ("moe::" + kname + "<") in n or ("moe::" + kname + "(") in n]
+        # the probe's three copies are the last copy dispatches of the run
+        copy = [v for _, n, _, v in sorted(rows) if "copy" in n.lower()][-3:]
+        if not kern or len(copy) < 3:
+            raise SystemExit("no %s dispatches of %s or of the copy probe in %s" % (counter, kname, path))
+        copy_kib = sum(copy) / len(copy)
+        factor = copy_bytes / (copy_kib * 1024.0)
+        kib = sum(kern) / len(kern)
+        res[key + "_kib_per_launch"] = kib
+        res[key + "_copy_kib"] = copy_kib
+        res[key + "_factor"] = factor
+        res[key + "_bytes_per_launch"] = kib * 1024.0 * factor
+        res[key + "_launches"] = len(kern)
+    res["hbm_bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
+    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    recs = {}
+    if os.path.exists(rec_path):
+        with open(rec_path) as f:
+            recs = json.load(f)
+    recs[workload] = res
+    with open(rec_path, "w") as f:
+        json.dump(recs, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({workload: res}))
+
+
+def copy_probe(torch, mib):
+    """A plain device copy of known size (the counters' calibration kernel)."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def cpu_baseline(cfg, L, x_all, target_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the workload: a short
+    call on 4 tokens sizes the sample for about ``target_s`` seconds, then the
+    sample is timed in one call."""
     import numpy as np
     from oracle import Oracle
     orc = Oracle()
     threads = orc.threads()
-    n = x_rows.shape[0]
-    Ls = dict(L)
-    Ls["x"] = np.ascontiguousarray(x_rows)
-    t0 = time.perf_counter()
-    orc.layer_forward(cfg, Ls, debug=False)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        Ls = dict(L)
+        Ls["x"] = np.ascontiguousarray(x_all[:n])
+        t0 = time.perf_counter()
+        orc.layer_forward(cfg, Ls, debug=False)
+        return time.perf_counter() - t0
+
+    rate = 4 / run(4)
+    n = int(max(8, min(x_all.shape[0], rate * target_s)))
+    dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d tokens of the same workload in one call (token-major fp64 oracle, %d OpenMP threads),"
                       " %.1f s wall" % (n, threads, dt)}
@@ -186,8 +249,22 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the steps in a HIP graph (64 steps per graph) and replay it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv "
+                         "files of a run made with --copy-probe-mib")
     args = ap.parse_args()
+    if args.record_traffic:
+        from synth import configs as _cf
+        from sparse_moe_layer_02_amd.binding import DECODE_MAX_TOKENS
+        spec = WORKLOADS[args.workload]
+        cfg = _cf.get(spec["base"], T=spec["T"])
+        dec = args.path == "decode" or (args.path == "auto" and cfg["T"] <= DECODE_MAX_TOKENS)
+        record_traffic(args.workload, "decode" if dec else "prefill", cfg["w"], args.record_traffic[0],
+                       args.record_traffic[1], (args.copy_probe_mib or 1024) * (1 << 20))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build runs the MoE layer on a single MI355X "
@@ -297,10 +374,13 @@ def main():
     router_bytes = cfg["E"] * cfg["d"] * 4
     act_bytes = 2 if cfg["act"] == "bf16" else 4
     layer_bytes = n_exp * expert_bytes(cfg) + router_bytes + T * cfg["d"] * (act_bytes + 4)
-    gu_bytes = n_exp * expert_bytes(cfg, 2)
-    flops_gu = 2.0 * (T * cfg["k"] + T * cfg["n_shared"]) * cfg["d"] * 2 * cfg["F"]
-    if not decode:  # the GEMM also reads the gathered rows of x and writes h
-        gu_bytes = gu_bytes + T * cfg["d"] * act_bytes + (T * cfg["k"] + T) * cfg["F"] * act_bytes
+    if decode:  # the routed gate/up launch; the shared expert's gate/up runs beside the selection
+        gu_bytes = unions.astype(np.float64) * expert_bytes(cfg, 2)
+        flops_gu = 2.0 * T * cfg["k"] * cfg["d"] * 2 * cfg["F"]
+    else:  # routed + shared gate/up; the GEMM also reads the gathered rows of x and writes h
+        gu_bytes = (n_exp * expert_bytes(cfg, 2) + T * cfg["d"] * act_bytes
+                    + (T * cfg["k"] + T * cfg["n_shared"]) * cfg["F"] * act_bytes)
+        flops_gu = 2.0 * (T * cfg["k"] + T * cfg["n_shared"]) * cfg["d"] * 2 * cfg["F"]
     gu_us = stages_us["gate_up"]
     achieved = float(np.mean(gu_bytes)) / (gu_us * 1e-6) / 1e9
     path_kind = "decode" if decode else "prefill"
@@ -334,13 +414,13 @@ def main():
     if not decode:
         out["mfma_frac_gate_up"] = round(out["gate_up_tflops"] / BF16_PEAK_TFS, 4)
 
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
+        out["copy_probe_bytes"] = args.copy_probe_mib * (1 << 20)
+
     # ---- the oracle on the host cores -----------------------------------
     if not args.no_cpu_baseline:
-        from oracle import Oracle
-        thr = Oracle().threads()
-        n = args.cpu_tokens or (max(8, min(64, 2 * thr)) if decode else max(4, min(32, thr)))
-        Lh = dict(L)
-        out["cpu_baseline"] = cpu_baseline(cfg, Lh, x_all[:n], T)
+        out["cpu_baseline"] = cpu_baseline(cfg, L, x_all, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

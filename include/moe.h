@@ -19,8 +19,8 @@
  * expert) and section "The constant that always said 256" (sqrt(softplus)
  * scores, top-6, the 1.5 scale, logits addressed with stride n_expert and
  * n_expert a runtime value, a parallel top-k rather than a serial one);
- * NeutronStar README, main branch - Hy3 paragraph (192-expert top-8 sigmoid
- * router with expert bias, shared expert); NeutronStar README - "The model"
+ * NeutronStar README, main branch - Hy3 paragraph (sigmoid scores plus a
+ * per-expert bias choosing 8 of 192 experts, and a shared expert); NeutronStar README - "The model"
  * (decision tensors kept at Q8_0/F32), "GLM-5.2 CUDA port" (gate/up and down
  * projection kernels) and the MTP paragraph (only the selected experts' weights
  * are read for small batches; batch kernels address whole [E, rows, cols]

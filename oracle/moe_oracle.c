@@ -526,7 +526,7 @@ int moe_ref_layer_forward(const moe_ref_config *cfg, const void *x, const moe_re
 
 /* ------------------------------------------------------------------------ */
 /* Dense SwiGLU through one expert, written out separately for the identity  */
-/* "one expert, top-1, no shared expert = dense SwiGLU".                      */
+/* (with one expert, top-1 and no shared expert the layer reduces to it).     */
 /* ------------------------------------------------------------------------ */
 
 int moe_ref_dense_swiglu(int32_t n_tokens, int32_t d_model, int32_t d_ff, int32_t act_dtype,

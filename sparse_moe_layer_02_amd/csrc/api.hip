@@ -329,7 +329,7 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     RouteArgs r{x, w->w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, logits, !decode};
     hipError_t e = mark(dbg, 0, st);
     if (decode) {
-        // router + shared gate/up | selection + routed gate/up | down with the combine
+        // router | selection + shared gate/up | routed gate/up | down with the combine
         DecodeRouteArgs dr;
         dr.r = r;
         dr.s = select_args(cfg, logits, w->bias, idx, wts);

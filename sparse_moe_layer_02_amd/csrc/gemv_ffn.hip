@@ -1,14 +1,16 @@
 // gemv_ffn.hip - expert FFN as bandwidth-bound GEMVs over only the selected
 // experts' weights (the decode path), on gfx950.
 //
-//   h[row, :]  = silu(Wg[e] x_t) * (Wu[e] x_t)        (rounded to the act format)
-//   y[t, i]   += w_f * (Wd[e] h_row)[i]   (shared expert: weight 1, added first)
+//   h[row, :]      = silu(Wg[e] x_t) * (Wu[e] x_t)     (rounded to the act format)
+//   slot[f, i]     = w_f * (Wd[e] h_row)[i]            (prefill GEMV fallback)
 //
-// The pages: decode reads only the selected experts (NeutronStar README, MTP
-// paragraph: "only the selected experts load, per token"); the bottleneck is
-// memory bandwidth, not compute (main branch, closing paragraph); decision
-// tensors stay at Q8_0/F32 and experts are gate/up + down projections
-// ("The model", "GLM-5.2 CUDA port").
+// The decode down projection and the combine are fused in decode.hip.
+//
+// The pages: a small batch reads the weights of its selected experts and no
+// others (NeutronStar README, MTP paragraph); the limit is memory bandwidth
+// rather than arithmetic (main branch, closing paragraph); decision tensors
+// stay at Q8_0/F32 and experts are gate/up + down projections ("The model",
+// "GLM-5.2 CUDA port").
 //
 // Mapping: a workgroup is 4 wavefronts; each wavefront owns a few weight rows
 // and streams them once with 16-byte loads (lane l reads columns

@@ -82,9 +82,9 @@ hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st);
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st);
 hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st);
 
-// The decode path (T <= MOE_DECODE_MAX_TOKENS) in three launches: router +
-// shared gate/up; selection + grouping + routed gate/up; down + combine into
-// f.y.  `mark` records the caller's stage events between launches.
+// The decode path (T <= MOE_DECODE_MAX_TOKENS) in four launches: router;
+// selection + grouping beside the shared gate/up; routed gate/up; down +
+// combine into f.y.  `mark` records the caller's stage events between launches.
 struct DecodeRouteArgs {
     RouteArgs r;
     SelectArgs s;

@@ -9,8 +9,8 @@ Each workload stands in for one MoE layer of a model the pages discuss:
 * ``c3`` Hy3-style decode/verify: 192 experts, sigmoid + per-expert bias top-8
   (NeutronStar README, main branch, Hy3 paragraph), T in {1, 2};
 * ``c4`` prefill chunk, 512 tokens, near-uniform routing;
-* ``c5`` long prefill, 4096 tokens, expert bias skewed so that the hottest ~4%
-  of experts receive ~30% of the selections (the popularity skew the pages
+* ``c5`` long prefill, 4096 tokens, expert bias skewed so that the ten most
+  popular experts (3.9% of 256) take 30% of the selections (the popularity skew the pages
   report for the host expert cache: NeutronStar README, "SSD streaming
   optimizations").
 

@@ -3,9 +3,10 @@
 The c5 workload's expert bias is b_e = -beta * ln(rank_e) over a seeded
 popularity ranking.  beta is chosen by bisection so that, on a separate
 4096-token calibration batch (stream 11), the 10 hottest experts (3.9% of
-256) receive 30% of the top-8 selections: the skew the pages report for
-expert popularity ("the hottest ~4% of experts serve ~30% of lookups",
-NeutronStar README, "SSD streaming optimizations").  Routing is computed by
+256) receive 30% of the top-8 selections.  That matches the expert
+popularity skew the pages measured for their host-side expert cache (about
+one expert in 25 takes close to a third of the lookups; NeutronStar README,
+"SSD streaming optimizations").  Routing is computed by
 the CPU oracle only.
 
 Run from the repository root:  python tests/golden/calibrate_skew.py
