@@ -15,8 +15,12 @@ any cache) on a fixed batch.
 
 Output: one JSON line.  `value` = tokens per second of the whole timed region
 (inputs resident in HBM).  `roofline` describes the dominant kernel (the
-gate/up stage): algorithmic bytes per launch divided by its average duration,
-measured live with HIP events recorded on the library's stream.  `traffic` is
+gate/up stage): algorithmic bytes per launch divided by its average duration.
+The durations come from HIP events that the library attaches to its own
+kernel dispatches on its stream (hipExtLaunchKernel start/stop timestamps, the
+same ones a kernel trace reads): during the timed steps for prefill, in a
+second eager pass of the same steps for decode, whose ~50 us steps those
+per-dispatch timestamps would slow by ~40 us.  `traffic` is
 the HBM byte count from rocprofv3 counters recorded in profiles/traffic.json,
 or null when that record was taken on a different version of the kernel
 source.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
@@ -249,6 +253,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the steps in a HIP graph (64 steps per graph) and replay it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-times", default="auto", choices=["auto", "live", "pass"],
+                    help="take the per-stage kernel times in the timed steps (live) or in a second eager pass "
+                         "(pass); auto: live for prefill, pass for decode, whose 50 us steps the per-dispatch "
+                         "timestamps would slow")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (counter calibration)")
@@ -334,6 +342,16 @@ def main():
         torch.cuda.synchronize()
 
     # ---- timed region ----------------------------------------------------
+    # Eager steps carry per-stage kernel events (the dispatches' own start and
+    # end timestamps) and log the selected experts; graph replays carry none,
+    # so their stage times come from an eager pass afterwards.
+    stage_names = moe.binding.DECODE_STAGES if decode else moe.binding.STAGES
+    stage_ids = [moe.binding.STAGES.index(n) for n in stage_names]
+    n_ev = moe.binding.STAGE_EVENTS
+    ev = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    ev_arr = [(ctypes.c_void_p * n_ev)(*[e.value for e in row]) for row in ev]
+    idx_log = torch.empty((steps, T, cfg["k"]), dtype=torch.int32, device="cuda")
+    live = graph is None and (args.stage_times == "live" or (args.stage_times == "auto" and not decode))
     e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -341,6 +359,9 @@ def main():
     if graph is not None:
         for _ in range(steps // 64):
             graph.replay()
+    elif live:
+        for i in range(steps):
+            step(warmup + i, events=ev_arr[i], dbg={"topk_idx": idx_log[i]})
     else:
         for i in range(steps):
             step(warmup + i)
@@ -351,21 +372,18 @@ def main():
     total_ms = hip.ms(e0, e1)
     ms_per_step = total_ms / steps
 
-    # ---- stage pass: the same steps with HIP events at every stage boundary --
-    ev = [[hip.event() for _ in range(moe.binding.STAGE_EVENTS)] for _ in range(steps)]
-    idx_log = torch.empty((steps, T, cfg["k"]), dtype=torch.int32, device="cuda")
+    if not live:  # the same steps again, eagerly, for the stage times and the expert log
+        for i in range(steps):
+            step(warmup + i, events=ev_arr[i], dbg={"topk_idx": idx_log[i]})
+        torch.cuda.synchronize()
+    stage_ms = np.zeros((steps, len(stage_names)))
     for i in range(steps):
-        arr = (ctypes.c_void_p * moe.binding.STAGE_EVENTS)(*[e.value for e in ev[i]])
-        step(warmup + i, events=arr, dbg={"topk_idx": idx_log[i]})
-    torch.cuda.synchronize()
-    stage_ms = np.zeros((steps, len(moe.binding.STAGES)))
-    for i in range(steps):
-        for s in range(len(moe.binding.STAGES)):
-            stage_ms[i, s] = hip.ms(ev[i][s], ev[i][s + 1])
+        for c, s in enumerate(stage_ids):
+            stage_ms[i, c] = hip.ms(ev[i][2 * s], ev[i][2 * s + 1])
     for row in ev:
         for e in row:
             hip.destroy(e)
-    stages_us = {name: round(float(stage_ms[:, s].mean()) * 1e3, 2) for s, name in enumerate(moe.binding.STAGES)}
+    stages_us = {name: round(float(stage_ms[:, c].mean()) * 1e3, 2) for c, name in enumerate(stage_names)}
 
     # ---- algorithmic work -------------------------------------------------
     idx_np = idx_log.cpu().numpy()
@@ -400,6 +418,7 @@ def main():
         "config": {"workload": describe(cfg), "T": T, "d_model": cfg["d"], "n_expert": cfg["E"],
                    "top_k": cfg["k"], "d_ff": cfg["F"], "weights": cfg["w"], "activations": cfg["act"],
                    "path": path_kind, "weight_copies": n_copies, "hip_graph": bool(args.graph),
+                   "stage_times": "live" if live else "second eager pass",
                    "distinct_tokens": n_tok_rows if decode else T},
         "roofline": roofline,
         "layer_hbm_GBs": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),

@@ -105,10 +105,14 @@ typedef struct {
     moe_mat s_down;         /* [1, d, Fs] */
 } moe_weights;
 
-/* Stage boundaries at which moe_layer_forward can record caller events:
- * 0 start, 1 logits, 2 top-k, 3 permutation, 4 gate/up (SwiGLU), 5 down,
- * 6 combine (the decode path fuses down and combine: 5 and 6 coincide). */
-#define MOE_STAGE_EVENTS 7
+/* Stages of moe_layer_forward whose kernels a caller can time: 0 router
+ * logits, 1 top-k selection, 2 permutation, 3 gate/up (SwiGLU), 4 down
+ * projection, 5 combine.  The decode path (n_tokens <= MOE_DECODE_MAX_TOKENS)
+ * builds the permutation inside the selection kernel and the combine inside
+ * the down kernel: it launches no kernel for stages 2 and 5 and leaves their
+ * events unrecorded. */
+#define MOE_STAGES 6
+#define MOE_STAGE_EVENTS (2 * MOE_STAGES)
 
 /* Optional outputs of moe_layer_forward; any field may be NULL. */
 typedef struct {
@@ -118,8 +122,11 @@ typedef struct {
     int32_t *offsets;   /* [E+1] */
     int32_t *perm_rows; /* [T*k] */
     int32_t *inv_perm;  /* [T*k] */
-    void **stage_events; /* NULL, or MOE_STAGE_EVENTS hipEvent_t created by the caller; each
-                            non-NULL one is recorded on the stream at its stage boundary */
+    void **stage_events; /* NULL, or MOE_STAGE_EVENTS hipEvent_t created by the caller (entries
+                            may be NULL): [2s] receives the start timestamp of stage s's first
+                            kernel dispatch, [2s+1] the end timestamp of its last (the dispatch's
+                            own timestamps, via hipExtLaunchKernel), so the elapsed time between
+                            them is the stage's kernel time without the launch gaps around it */
 } moe_debug;
 
 /* Bytes of workspace every entry point below may use for this config

@@ -46,8 +46,9 @@ class moe_weights(ctypes.Structure):
                 ("s_gate", moe_mat), ("s_up", moe_mat), ("s_down", moe_mat)]
 
 
-STAGE_EVENTS = 7
-STAGES = ("router", "topk", "permute", "gate_up", "down", "combine")
+STAGES = ("router", "select", "permute", "gate_up", "down", "combine")
+STAGE_EVENTS = 2 * len(STAGES)  # [2s] start of stage s's first kernel, [2s+1] end of its last
+DECODE_STAGES = ("router", "select", "gate_up", "down")  # stages the decode path launches kernels for
 
 
 class moe_debug(ctypes.Structure):
@@ -192,7 +193,8 @@ def moe_combine(cfg, slot_out, shared_out, y, stream=None):
 
 def moe_layer_forward(cfg, x, weights: moe_weights, y, ws, debug: dict | None = None, stream=None,
                       stage_events=None):
-    """``stage_events``: optional ctypes array of STAGE_EVENTS hipEvent_t handles."""
+    """``stage_events``: optional ctypes array of STAGE_EVENTS hipEvent_t handles
+    (start and end timestamps of each stage's kernels)."""
     lib = load()
     dbg = None
     if debug or stage_events is not None:

@@ -192,10 +192,15 @@ hipError_t run_expert_kernels(const FfnArgs& f, hipStream_t st) {
     return launch_down_slots_gemv(f, st);
 }
 
-// Record the caller's stage event i (if any) on the stream.
-hipError_t mark(const moe_debug* dbg, int i, hipStream_t st) {
-    if (!dbg || !dbg->stage_events || !dbg->stage_events[i]) return hipSuccess;
-    return hipEventRecord(static_cast<hipEvent_t>(dbg->stage_events[i]), st);
+// The caller's stage events (if any) as per-stage kernel timings.
+void stage_timings(const moe_debug* dbg, KTime* kt) {
+    for (int s = 0; s < MOE_STAGES; ++s) {
+        kt[s] = KTime();
+        if (dbg && dbg->stage_events) {
+            kt[s].start = static_cast<hipEvent_t>(dbg->stage_events[2 * s]);
+            kt[s].stop = static_cast<hipEvent_t>(dbg->stage_events[2 * s + 1]);
+        }
+    }
 }
 
 SelectArgs select_args(const moe_config* c, const float* logits, const float* bias, int32_t* idx,
@@ -327,7 +332,8 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     int32_t* inv = dbg && dbg->inv_perm ? dbg->inv_perm : at<int32_t>(ws, L.inv_perm);
 
     RouteArgs r{x, w->w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, logits, !decode};
-    hipError_t e = mark(dbg, 0, st);
+    KTime kt[MOE_STAGES];
+    stage_timings(dbg, kt);
     if (decode) {
         // router | selection + shared gate/up | routed gate/up | down with the combine
         DecodeRouteArgs dr;
@@ -337,32 +343,24 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
         dr.f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
         dr.f.y = y;
         dr.scores = at<float>(ws, L.scores);
-        if (e == hipSuccess) e = launch_decode(dr, dbg, mark, st);
-        return device_status(e);
+        return device_status(launch_decode(dr, kt, st));
     }
-    if (e == hipSuccess) e = launch_router_logits(r, st);
-    if (e == hipSuccess) e = mark(dbg, 1, st);
-    if (e == hipSuccess) e = launch_topk(select_args(cfg, logits, w->bias, idx, wts), st);
-    if (e == hipSuccess) e = mark(dbg, 2, st);
-    if (e == hipSuccess) e = launch_permute(perm_args(cfg, L, ws, idx, off, perm, inv), st);
-    if (e == hipSuccess) e = mark(dbg, 3, st);
+    hipError_t e = launch_router_logits(r, st, kt[0]);
+    if (e == hipSuccess) e = launch_topk(select_args(cfg, logits, w->bias, idx, wts), st, kt[1]);
+    if (e == hipSuccess) e = launch_permute(perm_args(cfg, L, ws, idx, off, perm, inv), st, kt[2]);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     FfnArgs f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
     if (f.wdt == MOE_DT_BF16) {
-        e = launch_gateup_mfma(f, st);
-        if (e == hipSuccess) e = mark(dbg, 4, st);
-        if (e == hipSuccess) e = launch_down_mfma(f, st);
+        e = launch_gateup_mfma(f, st, kt[3]);
+        if (e == hipSuccess) e = launch_down_mfma(f, st, kt[4]);
     } else {
-        e = launch_gateup_gemv(f, st);
-        if (e == hipSuccess) e = mark(dbg, 4, st);
-        if (e == hipSuccess) e = launch_down_slots_gemv(f, st);
+        e = launch_gateup_gemv(f, st, kt[3]);
+        if (e == hipSuccess) e = launch_down_slots_gemv(f, st, kt[4]);
     }
-    if (e == hipSuccess) e = mark(dbg, 5, st);
     if (e == hipSuccess) {
         CombineArgs c{f.slot_out, f.shared_out, y, cfg->n_tokens, cfg->top_k, cfg->d_model};
-        e = launch_combine(c, st);
+        e = launch_combine(c, st, kt[5]);
     }
-    if (e == hipSuccess) e = mark(dbg, 6, st);
     return device_status(e);
 }
 

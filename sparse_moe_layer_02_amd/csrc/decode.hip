@@ -243,65 +243,60 @@ static int mt_for(int T, int wdt) {
 }
 
 template <int WF, int AF>
-static void down_launch(const FfnArgs& a, int mt, dim3 grid, hipStream_t st) {
-    if (mt == 1) decode_down_kernel<WF, AF, 1><<<grid, DD_THREADS, 0, st>>>(a);
-    else if (mt == 2) decode_down_kernel<WF, AF, 2><<<grid, DD_THREADS, 0, st>>>(a);
-    else if (mt == 4) decode_down_kernel<WF, AF, 4><<<grid, DD_THREADS, 0, st>>>(a);
-    else decode_down_kernel<WF, AF, 8><<<grid, DD_THREADS, 0, st>>>(a);
+static void down_launch(const FfnArgs& a, int mt, dim3 grid, hipStream_t st, const KTime& kt) {
+    if (mt == 1) launch_kernel(decode_down_kernel<WF, AF, 1>, grid, DD_THREADS, st, kt, a);
+    else if (mt == 2) launch_kernel(decode_down_kernel<WF, AF, 2>, grid, DD_THREADS, st, kt, a);
+    else if (mt == 4) launch_kernel(decode_down_kernel<WF, AF, 4>, grid, DD_THREADS, st, kt, a);
+    else launch_kernel(decode_down_kernel<WF, AF, 8>, grid, DD_THREADS, st, kt, a);
 }
 
 template <int KPL, int EFIX, int WF, int AF>
-static void select_launch_mt(const DecodeRouteArgs& a, int mt, dim3 grid, hipStream_t st) {
-    if (mt == 1) decode_select_kernel<KPL, EFIX, WF, AF, 1><<<grid, DS_THREADS, 0, st>>>(a);
-    else if (mt == 2) decode_select_kernel<KPL, EFIX, WF, AF, 2><<<grid, DS_THREADS, 0, st>>>(a);
-    else if (mt == 4) decode_select_kernel<KPL, EFIX, WF, AF, 4><<<grid, DS_THREADS, 0, st>>>(a);
-    else decode_select_kernel<KPL, EFIX, WF, AF, 8><<<grid, DS_THREADS, 0, st>>>(a);
+static void select_launch_mt(const DecodeRouteArgs& a, int mt, dim3 grid, hipStream_t st, const KTime& kt) {
+    if (mt == 1) launch_kernel(decode_select_kernel<KPL, EFIX, WF, AF, 1>, grid, DS_THREADS, st, kt, a);
+    else if (mt == 2) launch_kernel(decode_select_kernel<KPL, EFIX, WF, AF, 2>, grid, DS_THREADS, st, kt, a);
+    else if (mt == 4) launch_kernel(decode_select_kernel<KPL, EFIX, WF, AF, 4>, grid, DS_THREADS, st, kt, a);
+    else launch_kernel(decode_select_kernel<KPL, EFIX, WF, AF, 8>, grid, DS_THREADS, st, kt, a);
 }
 
 template <int KPL, int EFIX>
-static void select_launch_fmt(const DecodeRouteArgs& a, int mt, dim3 grid, hipStream_t st) {
-    if (a.f.wdt == MOE_DT_F32) select_launch_mt<KPL, EFIX, MOE_DT_F32, MOE_DT_F32>(a, mt, grid, st);
-    else if (a.f.wdt == MOE_DT_BF16) select_launch_mt<KPL, EFIX, MOE_DT_BF16, MOE_DT_BF16>(a, mt, grid, st);
-    else select_launch_mt<KPL, EFIX, MOE_DT_Q8B32, MOE_DT_BF16>(a, mt, grid, st);
+static void select_launch_fmt(const DecodeRouteArgs& a, int mt, dim3 grid, hipStream_t st, const KTime& kt) {
+    if (a.f.wdt == MOE_DT_F32) select_launch_mt<KPL, EFIX, MOE_DT_F32, MOE_DT_F32>(a, mt, grid, st, kt);
+    else if (a.f.wdt == MOE_DT_BF16) select_launch_mt<KPL, EFIX, MOE_DT_BF16, MOE_DT_BF16>(a, mt, grid, st, kt);
+    else select_launch_mt<KPL, EFIX, MOE_DT_Q8B32, MOE_DT_BF16>(a, mt, grid, st, kt);
 }
 
-hipError_t launch_decode(const DecodeRouteArgs& a, const moe_debug* dbg,
-                         hipError_t (*mark)(const moe_debug*, int, hipStream_t), hipStream_t st) {
+hipError_t launch_decode(const DecodeRouteArgs& a, const KTime* kt, hipStream_t st) {
     const int T = a.r.T, E = a.r.E;
     const int mt = mt_for(T, a.f.wdt);
     // 1. router
-    if (a.r.act == MOE_DT_BF16) decode_router_kernel<MOE_DT_BF16><<<E, 256, 0, st>>>(a);
-    else decode_router_kernel<MOE_DT_F32><<<E, 256, 0, st>>>(a);
+    if (a.r.act == MOE_DT_BF16) launch_kernel(decode_router_kernel<MOE_DT_BF16>, E, 256, st, kt[0], a);
+    else launch_kernel(decode_router_kernel<MOE_DT_F32>, E, 256, st, kt[0], a);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess) e = mark(dbg, 1, st);
     // 2. selection + grouping, shared gate/up
     if (e == hipSuccess) {
         dim3 grid(1 + (a.f.n_shared ? (a.f.Fs + DS_WAVES - 1) / DS_WAVES : 0));
         const int kpl = (E + WAVE - 1) / WAVE;
-        if (E == 256) select_launch_fmt<4, 256>(a, mt, grid, st);
-        else if (kpl <= 1) select_launch_fmt<1, 0>(a, mt, grid, st);
-        else if (kpl <= 2) select_launch_fmt<2, 0>(a, mt, grid, st);
-        else if (kpl <= 3) select_launch_fmt<3, 0>(a, mt, grid, st);
-        else if (kpl <= 4) select_launch_fmt<4, 0>(a, mt, grid, st);
-        else if (kpl <= 8) select_launch_fmt<8, 0>(a, mt, grid, st);
-        else select_launch_fmt<16, 0>(a, mt, grid, st);
+        if (E == 256) select_launch_fmt<4, 256>(a, mt, grid, st, kt[1]);
+        else if (kpl <= 1) select_launch_fmt<1, 0>(a, mt, grid, st, kt[1]);
+        else if (kpl <= 2) select_launch_fmt<2, 0>(a, mt, grid, st, kt[1]);
+        else if (kpl <= 3) select_launch_fmt<3, 0>(a, mt, grid, st, kt[1]);
+        else if (kpl <= 4) select_launch_fmt<4, 0>(a, mt, grid, st, kt[1]);
+        else if (kpl <= 8) select_launch_fmt<8, 0>(a, mt, grid, st, kt[1]);
+        else select_launch_fmt<16, 0>(a, mt, grid, st, kt[1]);
         e = hipGetLastError();
     }
-    for (int i = 2; i <= 3 && e == hipSuccess; ++i) e = mark(dbg, i, st);
     // 3. routed gate/up
     FfnArgs f = a.f;
     f.shared_done = 1;
-    if (e == hipSuccess) e = launch_gateup_gemv(f, st);
-    if (e == hipSuccess) e = mark(dbg, 4, st);
+    if (e == hipSuccess) e = launch_gateup_gemv(f, st, kt[3]);
     // 4. down + combine
     if (e == hipSuccess) {
         dim3 grid((f.d + DD_R - 1) / DD_R);
-        if (f.wdt == MOE_DT_F32) down_launch<MOE_DT_F32, MOE_DT_F32>(f, mt, grid, st);
-        else if (f.wdt == MOE_DT_BF16) down_launch<MOE_DT_BF16, MOE_DT_BF16>(f, mt, grid, st);
-        else down_launch<MOE_DT_Q8B32, MOE_DT_BF16>(f, mt, grid, st);
+        if (f.wdt == MOE_DT_F32) down_launch<MOE_DT_F32, MOE_DT_F32>(f, mt, grid, st, kt[4]);
+        else if (f.wdt == MOE_DT_BF16) down_launch<MOE_DT_BF16, MOE_DT_BF16>(f, mt, grid, st, kt[4]);
+        else down_launch<MOE_DT_Q8B32, MOE_DT_BF16>(f, mt, grid, st, kt[4]);
         e = hipGetLastError();
     }
-    for (int i = 5; i <= 6 && e == hipSuccess; ++i) e = mark(dbg, i, st);
     return e;
 }
 

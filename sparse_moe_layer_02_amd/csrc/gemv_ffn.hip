@@ -93,50 +93,51 @@ constexpr int RD_ROWS = 4;  // down rows per wavefront
 
 static int pick_mt(int max_rows) { return max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8; }
 
-#define MOE_DISPATCH_MT(KERNEL, WF, AF, R, MTV, GRID, ARGS, ST)                                    \
-    do {                                                                                           \
-        if ((MTV) == 1) KERNEL<WF, AF, R, 1><<<GRID, 256, 0, ST>>>(ARGS);                          \
-        else if ((MTV) == 2) KERNEL<WF, AF, R, 2><<<GRID, 256, 0, ST>>>(ARGS);                     \
-        else if ((MTV) == 4 || (WF) == MOE_DT_Q8B32) KERNEL<WF, AF, R, 4><<<GRID, 256, 0, ST>>>(ARGS); \
-        else KERNEL<WF, AF, R, 8><<<GRID, 256, 0, ST>>>(ARGS);                                     \
+#define MOE_DISPATCH_MT(KERNEL, WF, AF, R, MTV, GRID, ARGS, ST, KT)                                  \
+    do {                                                                                          \
+        if ((MTV) == 1) launch_kernel(KERNEL<WF, AF, R, 1>, GRID, 256, ST, KT, ARGS);             \
+        else if ((MTV) == 2) launch_kernel(KERNEL<WF, AF, R, 2>, GRID, 256, ST, KT, ARGS);        \
+        else if ((MTV) == 4 || (WF) == MOE_DT_Q8B32)                                              \
+            launch_kernel(KERNEL<WF, AF, R, 4>, GRID, 256, ST, KT, ARGS);                         \
+        else launch_kernel(KERNEL<WF, AF, R, 8>, GRID, 256, ST, KT, ARGS);                        \
     } while (0)
 
-#define MOE_DISPATCH_FMT(KERNEL, R, MTV, GRID, ARGS, ST)                                   \
-    do {                                                                                   \
-        if ((ARGS).wdt == MOE_DT_F32)                                                      \
-            MOE_DISPATCH_MT(KERNEL, MOE_DT_F32, MOE_DT_F32, R, MTV, GRID, ARGS, ST);       \
-        else if ((ARGS).wdt == MOE_DT_BF16)                                                \
-            MOE_DISPATCH_MT(KERNEL, MOE_DT_BF16, MOE_DT_BF16, R, MTV, GRID, ARGS, ST);     \
-        else                                                                               \
-            MOE_DISPATCH_MT(KERNEL, MOE_DT_Q8B32, MOE_DT_BF16, R, MTV, GRID, ARGS, ST);    \
+#define MOE_DISPATCH_FMT(KERNEL, R, MTV, GRID, ARGS, ST, KT)                                   \
+    do {                                                                                       \
+        if ((ARGS).wdt == MOE_DT_F32)                                                          \
+            MOE_DISPATCH_MT(KERNEL, MOE_DT_F32, MOE_DT_F32, R, MTV, GRID, ARGS, ST, KT);       \
+        else if ((ARGS).wdt == MOE_DT_BF16)                                                    \
+            MOE_DISPATCH_MT(KERNEL, MOE_DT_BF16, MOE_DT_BF16, R, MTV, GRID, ARGS, ST, KT);     \
+        else                                                                                   \
+            MOE_DISPATCH_MT(KERNEL, MOE_DT_Q8B32, MOE_DT_BF16, R, MTV, GRID, ARGS, ST, KT);    \
     } while (0)
 
-hipError_t launch_gateup_gemv(const FfnArgs& a0, hipStream_t st) {
+hipError_t launch_gateup_gemv(const FfnArgs& a0, hipStream_t st, const KTime& kt) {
     FfnArgs a = a0;
     a.grid_has_shared = a.n_shared && !a.shared_done;
     const int fmax = a.grid_has_shared && a.Fs > a.F ? a.Fs : a.F;
     const int slots = (a.E < a.T * a.k ? a.E : a.T * a.k) + (a.grid_has_shared ? 1 : 0);
     dim3 grid((fmax + 4 * RG_ROWS - 1) / (4 * RG_ROWS), slots);
     const int mt = pick_mt(a.T);
-    MOE_DISPATCH_FMT(gateup_gemv_kernel, RG_ROWS, mt, grid, a, st);
+    MOE_DISPATCH_FMT(gateup_gemv_kernel, RG_ROWS, mt, grid, a, st, kt);
     return hipGetLastError();
 }
 
-hipError_t launch_down_slots_gemv(const FfnArgs& a0, hipStream_t st) {
+hipError_t launch_down_slots_gemv(const FfnArgs& a0, hipStream_t st, const KTime& kt) {
     FfnArgs a = a0;
     a.grid_has_shared = a.n_shared && !a.shared_done;
     const int slots = (a.E < a.T * a.k ? a.E : a.T * a.k) + (a.grid_has_shared ? 1 : 0);
     dim3 grid((a.d + 4 * RD_ROWS - 1) / (4 * RD_ROWS), slots);
     const int mt = pick_mt(a.T);
-    MOE_DISPATCH_FMT(down_slots_kernel, RD_ROWS, mt, grid, a, st);
+    MOE_DISPATCH_FMT(down_slots_kernel, RD_ROWS, mt, grid, a, st, kt);
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st, const KTime& kt) {
     const size_t n4 = (size_t)a.T * a.d / 4;
     const size_t want = (n4 + 255) / 256;
     const int blocks = (int)(want < 4096 ? want : 4096);
-    combine_kernel<<<blocks, 256, 0, st>>>(a);
+    launch_kernel(combine_kernel, blocks, 256, st, kt, a);
     return hipGetLastError();
 }
 

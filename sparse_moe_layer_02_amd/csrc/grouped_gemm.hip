@@ -276,16 +276,16 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a) {
     }
 }
 
-hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st) {
+hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
     dim3 grid(a.max_tiles, (fmax + GU_BN - 1) / GU_BN);
-    gateup_mfma_kernel<<<grid, 256, 0, st>>>(a);
+    launch_kernel(gateup_mfma_kernel, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 
-hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st) {
+hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     dim3 grid(a.max_tiles, (a.d + DN_BN - 1) / DN_BN);
-    down_mfma_kernel<<<grid, 256, 0, st>>>(a);
+    launch_kernel(down_mfma_kernel, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 

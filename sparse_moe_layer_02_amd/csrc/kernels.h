@@ -2,12 +2,30 @@
 // and the kernel files.  Every launcher enqueues on the given stream and
 // returns hipGetLastError().
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.h"
 
 namespace moe {
+
+// Kernel timing of one stage: `start` receives the start timestamp of the
+// stage's first kernel dispatch, `stop` the end timestamp of its last
+// (hipExtLaunchKernel events, taken from the dispatch itself, so launch gaps
+// before and after the stage are not counted).  Either may be null.
+struct KTime {
+    hipEvent_t start = nullptr, stop = nullptr;
+    KTime first() const { return KTime{start, nullptr}; }
+    KTime last() const { return KTime{nullptr, stop}; }
+};
+
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t st, const KTime& kt,
+                          Args... args) {
+    if (kt.start || kt.stop) hipExtLaunchKernelGGL(kern, grid, block, 0, st, kt.start, kt.stop, 0, args...);
+    else kern<<<grid, block, 0, st>>>(args...);
+}
 
 struct RouteArgs {
     const void* x;
@@ -16,7 +34,7 @@ struct RouteArgs {
     float* logits;
     bool force_gemm;  // use the tiled prefill kernel even for few tokens
 };
-hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st);
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 struct SelectArgs {
     const float* logits;
@@ -27,7 +45,7 @@ struct SelectArgs {
     float* topk_w;
     bool generic_only;  // skip the compile-time 256-expert instantiation
 };
-hipError_t launch_topk(const SelectArgs& a, hipStream_t st);
+hipError_t launch_topk(const SelectArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 struct PermArgs {
     const int32_t* topk_idx;
@@ -44,9 +62,9 @@ struct PermArgs {
     int n_blk;
     int bm;              // tile rows for the tile list
 };
-hipError_t launch_permute(const PermArgs& a, hipStream_t st);
+hipError_t launch_permute(const PermArgs& a, hipStream_t st, const KTime& kt = KTime());
 // active / tile lists from existing offsets (offsets and perm_rows untouched)
-hipError_t launch_lists_from_offsets(const PermArgs& a, hipStream_t st);
+hipError_t launch_lists_from_offsets(const PermArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 // One set of expert weights for the FFN kernels.
 struct MatRef {
@@ -75,16 +93,17 @@ struct FfnArgs {
     int grid_has_shared;    // set by the launchers: the last grid slot is the shared expert
 };
 // gate/up GEMV over the active experts (and the shared one) -> h
-hipError_t launch_gateup_gemv(const FfnArgs& a, hipStream_t st);
+hipError_t launch_gateup_gemv(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 // down GEMV writing weighted slot rows and the shared rows
-hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st);
+hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 // grouped bf16 MFMA GEMMs (prefill)
-hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st);
-hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st);
+hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 // The decode path (T <= MOE_DECODE_MAX_TOKENS) in four launches: router;
 // selection + grouping beside the shared gate/up; routed gate/up; down +
-// combine into f.y.  `mark` records the caller's stage events between launches.
+// combine into f.y.  kt[s] times stage s (MOE_STAGES entries); the decode
+// path launches nothing for the permutation and combine stages.
 struct DecodeRouteArgs {
     RouteArgs r;
     SelectArgs s;
@@ -92,8 +111,7 @@ struct DecodeRouteArgs {
     FfnArgs f;
     float* scores;  // [T, E] fp32 router scores (workspace)
 };
-hipError_t launch_decode(const DecodeRouteArgs& a, const moe_debug* dbg,
-                         hipError_t (*mark)(const moe_debug*, int, hipStream_t), hipStream_t st);
+hipError_t launch_decode(const DecodeRouteArgs& a, const KTime* kt, hipStream_t st);
 
 struct CombineArgs {
     const float* slot_out;
@@ -101,6 +119,6 @@ struct CombineArgs {
     float* y;
     int T, k, d;
 };
-hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 }  // namespace moe

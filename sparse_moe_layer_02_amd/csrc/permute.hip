@@ -102,19 +102,19 @@ __global__ __launch_bounds__(1024) void lists_from_offsets_kernel(PermArgs a) {
     emit_lists(a, c, smem, &off, false);
 }
 
-hipError_t launch_lists_from_offsets(const PermArgs& a, hipStream_t st) {
-    lists_from_offsets_kernel<<<1, 1024, 0, st>>>(a);
+hipError_t launch_lists_from_offsets(const PermArgs& a, hipStream_t st, const KTime& kt) {
+    launch_kernel(lists_from_offsets_kernel, 1, 1024, st, kt, a);
     return hipGetLastError();
 }
 
-hipError_t launch_permute(const PermArgs& a, hipStream_t st) {
+hipError_t launch_permute(const PermArgs& a, hipStream_t st, const KTime& kt) {
     const int n = a.T * a.k;
     if (n <= 1024) {
-        permute_small_kernel<<<1, 1024, 0, st>>>(a);
+        launch_kernel(permute_small_kernel, 1, 1024, st, kt, a);
     } else {
-        perm_hist_kernel<<<a.n_blk, 256, 0, st>>>(a);
-        perm_scan_kernel<<<1, 1024, 0, st>>>(a);
-        perm_scatter_kernel<<<a.n_blk, 64, 0, st>>>(a);
+        launch_kernel(perm_hist_kernel, a.n_blk, 256, st, kt.first(), a);
+        launch_kernel(perm_scan_kernel, 1, 1024, st, KTime(), a);
+        launch_kernel(perm_scatter_kernel, a.n_blk, 64, st, kt.last(), a);
     }
     return hipGetLastError();
 }

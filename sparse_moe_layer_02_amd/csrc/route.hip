@@ -184,39 +184,39 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st) {
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st, const KTime& kt) {
     if (a.T <= MOE_DECODE_MAX_TOKENS && !a.force_gemm) {
         dim3 grid(a.E);
         if (a.act == MOE_DT_BF16)
-            router_gemv_kernel<MOE_DT_BF16><<<grid, 256, 0, st>>>(a.x, a.wr, a.T, a.d, a.E, a.logits);
+            launch_kernel(router_gemv_kernel<MOE_DT_BF16>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
         else
-            router_gemv_kernel<MOE_DT_F32><<<grid, 256, 0, st>>>(a.x, a.wr, a.T, a.d, a.E, a.logits);
+            launch_kernel(router_gemv_kernel<MOE_DT_F32>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
     } else {
         dim3 grid((a.T + RG_TM - 1) / RG_TM, (a.E + RG_TE - 1) / RG_TE);
         if (a.act == MOE_DT_BF16)
-            router_gemm_kernel<MOE_DT_BF16><<<grid, 256, 0, st>>>(a.x, a.wr, a.T, a.d, a.E, a.logits);
+            launch_kernel(router_gemm_kernel<MOE_DT_BF16>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
         else
-            router_gemm_kernel<MOE_DT_F32><<<grid, 256, 0, st>>>(a.x, a.wr, a.T, a.d, a.E, a.logits);
+            launch_kernel(router_gemm_kernel<MOE_DT_F32>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
     }
     return hipGetLastError();
 }
 
 template <int KPL, int EFIX>
-static void topk_launch(const SelectArgs& a, hipStream_t st) {
+static void topk_launch(const SelectArgs& a, hipStream_t st, const KTime& kt) {
     dim3 grid((a.T + 3) / 4);
-    topk_kernel<KPL, EFIX><<<grid, 256, 0, st>>>(a.logits, a.bias, a.T, a.E, a.k, a.score,
-                                                  a.route_scale, a.topk_idx, a.topk_w);
+    launch_kernel(topk_kernel<KPL, EFIX>, grid, 256, st, kt, a.logits, a.bias, a.T, a.E, a.k, a.score,
+                  a.route_scale, a.topk_idx, a.topk_w);
 }
 
-hipError_t launch_topk(const SelectArgs& a, hipStream_t st) {
+hipError_t launch_topk(const SelectArgs& a, hipStream_t st, const KTime& kt) {
     const int kpl = (a.E + WAVE - 1) / WAVE;
-    if (a.E == 256 && !a.generic_only) topk_launch<4, 256>(a, st);  // the common 256-expert router
-    else if (kpl <= 1) topk_launch<1, 0>(a, st);
-    else if (kpl <= 2) topk_launch<2, 0>(a, st);
-    else if (kpl <= 3) topk_launch<3, 0>(a, st);
-    else if (kpl <= 4) topk_launch<4, 0>(a, st);
-    else if (kpl <= 8) topk_launch<8, 0>(a, st);
-    else topk_launch<16, 0>(a, st);
+    if (a.E == 256 && !a.generic_only) topk_launch<4, 256>(a, st, kt);  // the common 256-expert router
+    else if (kpl <= 1) topk_launch<1, 0>(a, st, kt);
+    else if (kpl <= 2) topk_launch<2, 0>(a, st, kt);
+    else if (kpl <= 3) topk_launch<3, 0>(a, st, kt);
+    else if (kpl <= 4) topk_launch<4, 0>(a, st, kt);
+    else if (kpl <= 8) topk_launch<8, 0>(a, st, kt);
+    else topk_launch<16, 0>(a, st, kt);
     return hipGetLastError();
 }
 
