@@ -206,15 +206,24 @@ def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes):
     print(json.dumps({workload: res}))
 
 
-def copy_probe(torch, mib):
-    """A plain device copy of known size (the counters' calibration kernel)."""
+def copy_probe(torch, hip, stream, mib):
+    """A plain device copy of known size, three times: the counters' calibration
+    kernel and the practical HBM ceiling (bytes read + written per second)."""
     n = mib * (1 << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(e0, stream)
     for _ in range(3):
         b.copy_(a)
-    torch.cuda.synchronize()
+    hip.record(e1, stream)
+    hip.sync(e1)
+    ms = hip.ms(e0, e1)
+    hip.destroy(e0)
+    hip.destroy(e1)
     del a, b
+    return round(3 * 2 * n * 4 / (ms * 1e-3) / 1e9, 1)
 
 
 def cpu_baseline(cfg, L, x_all, target_s=12.0):
@@ -434,7 +443,7 @@ def main():
         out["mfma_frac_gate_up"] = round(out["gate_up_tflops"] / BF16_PEAK_TFS, 4)
 
     if args.copy_probe_mib:
-        copy_probe(torch, args.copy_probe_mib)
+        out["copy_probe_GBs"] = copy_probe(torch, hip, stream, args.copy_probe_mib)
         out["copy_probe_bytes"] = args.copy_probe_mib * (1 << 20)
 
     # ---- the oracle on the host cores -----------------------------------

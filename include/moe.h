@@ -47,9 +47,9 @@
  *    once to fp32; the SwiGLU intermediate is rounded to the activation format
  *    (bf16, or fp32 for fp32 layers); y is fp32.
  *  - The workspace (`ws`, `ws_bytes`) is caller-owned scratch of at least
- *    moe_workspace_bytes(cfg) bytes.  It must be zero-filled before its first
- *    use; every call leaves its synchronisation counters zero again.  Calls
- *    that share a workspace must not overlap.
+ *    moe_workspace_bytes(cfg) bytes.  It needs no initialisation: every call
+ *    writes each workspace word before reading it.  Calls that share a
+ *    workspace must not overlap.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

@@ -209,8 +209,8 @@ def moe_layer_forward(cfg, x, weights: moe_weights, y, ws, debug: dict | None = 
 
 
 def workspace(cfg: moe_config, device="cuda"):
-    """A zero-filled workspace tensor of moe_workspace_bytes(cfg) bytes (the library
-    requires zero-filled memory before first use)."""
+    """A workspace tensor of moe_workspace_bytes(cfg) bytes (zero-filled, although
+    the library needs no initialisation)."""
     import torch
     n = moe_workspace_bytes(cfg)
     if n == 0:

@@ -70,13 +70,17 @@ def upload_weights_chunked(cfg, device="cuda", chunk=16):
     return W
 
 
-def layer_outputs(cfg, x_dev, W_dev, path="auto", stream=None):
-    """Run moe_layer_forward with every debug output requested; numpy results."""
+def layer_outputs(cfg, x_dev, W_dev, path="auto", stream=None, ws_fill=None, debug=True):
+    """Run moe_layer_forward with every debug output requested (or only y, with
+    ``debug=False``); numpy results.  ``ws_fill`` fills the workspace with that
+    byte value first."""
     import torch
     import sparse_moe_layer_02_amd as moe
     T = x_dev.shape[0]
     c = moe.config_from(cfg, T=T, path=path)
     ws = moe.workspace(c)
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
     dev = x_dev.device
     out = dict(y=torch.empty((T, cfg["d"]), dtype=torch.float32, device=dev),
                logits=torch.empty((T, cfg["E"]), dtype=torch.float32, device=dev),
@@ -85,8 +89,10 @@ def layer_outputs(cfg, x_dev, W_dev, path="auto", stream=None):
                offsets=torch.empty(cfg["E"] + 1, dtype=torch.int32, device=dev),
                perm_rows=torch.empty(T * cfg["k"], dtype=torch.int32, device=dev),
                inv_perm=torch.empty(T * cfg["k"], dtype=torch.int32, device=dev))
+    if not debug:
+        out = dict(y=out["y"])
     moe.moe_layer_forward(c, x_dev, moe.make_weights(W_dev), out["y"], ws,
-                          debug={k: v for k, v in out.items() if k != "y"}, stream=stream)
+                          debug={k: v for k, v in out.items() if k != "y"} or None, stream=stream)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 

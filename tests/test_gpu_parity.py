@@ -189,6 +189,26 @@ def test_decode_path_identity(torch_cuda, orc):
             assert np.array_equal(a[key], b[key])
 
 
+def test_uninitialised_workspace(torch_cuda, orc):
+    """The library writes every workspace word before reading it: a workspace
+    full of 0xFF bytes gives the same bits as a zeroed one, with the routing
+    kept in the workspace (no debug outputs) and with it exported."""
+    for path, spec in (("decode", dict(T=3, d=256, E=40, k=5, F=128)),
+                       ("prefill", dict(T=300, d=256, E=40, k=5, F=128)),
+                       ("prefill", dict(T=40, d=256, E=24, k=4, F=128, w="q8b32"))):
+        cfg = _custom(**spec)
+        L = configs.make_layer(cfg)
+        dev = H.upload_layer(L)
+        ref = oracle_full(orc, cfg, L)
+        for debug in (False, True):
+            a = H.layer_outputs(cfg, dev["x"], dev, path=path, ws_fill=0, debug=debug)
+            b = H.layer_outputs(cfg, dev["x"], dev, path=path, ws_fill=0xFF, debug=debug)
+            for key in a:
+                assert np.array_equal(a[key], b[key]), (path, spec, debug, key)
+            H.check_y(b["y"], ref["y"], cfg, "ws 0xFF %s T=%d" % (path, spec["T"]))
+        say("   ok: %s T=%d" % (path, spec["T"]))
+
+
 def test_deterministic(torch_cuda, orc):
     cfg = _custom(T=70, d=256, E=32, k=4, F=128)
     L = configs.make_layer(cfg)
