@@ -79,87 +79,125 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Prefill router: 64 tokens x 64 experts per workgroup, each thread owns 4x4
-// logits and adds x*Wr in ascending i (fp64 FMA; the product is exact so the
-// FMA equals multiply-then-add).  K is staged through LDS in chunks of 32.
+// Prefill router: a workgroup computes a TM-token x TE-expert tile of logits;
+// each of its 256 threads owns RT tokens x RE experts and adds x*Wr in
+// ascending i with fp64 FMA (the product is exact, so the FMA equals
+// multiply-then-add, and the sum follows the definition's order).  K is staged
+// through LDS in chunks of KC columns, widened to fp64 once at staging; the
+// next chunk's global loads are issued before the current chunk is consumed,
+// so their latency overlaps the arithmetic.  The inner loop reads two columns
+// per 16-byte LDS read; the row pitch of KC + 2 doubles staggers consecutive
+// rows by 4 dwords across the LDS banks.
 // ---------------------------------------------------------------------------
-constexpr int RG_TM = 64, RG_TE = 64, RG_KC = 32;
-
-template <int AF>
+template <int AF, int TM, int TE, int RT, int RE, int KC>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict__ x,
                                                           const float* __restrict__ wr, int T, int d,
                                                           int E, float* __restrict__ logits) {
-    __shared__ float xs[RG_KC][RG_TM + 1];
-    __shared__ float ws[RG_KC][RG_TE + 4];
+    constexpr int NTX = TE / RE, NTY = TM / RT, PITCH = KC + 2;
+    constexpr int NXQ = TM * KC / 8, NWQ = TE * KC / 4;  // staging items: 8 x values, 4 Wr values
+    constexpr int NXI = (NXQ + 255) / 256, NWI = (NWQ + 255) / 256;  // items per thread
+    static_assert(NTX * NTY == 256, "256 threads per tile");
+    __shared__ __attribute__((aligned(16))) double xs[TM * PITCH];
+    __shared__ __attribute__((aligned(16))) double ws[TE * PITCH];
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * RG_TM, e0 = blockIdx.y * RG_TE;
-    const int tx = tid % 16, ty = tid / 16;
-    double acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
+    const int tx = tid % NTX, ty = tid / NTX;
 
-    for (int k0 = 0; k0 < d; k0 += RG_KC) {
-        // x tile: 64 rows x 32 columns; thread loads 8 consecutive columns of one row
-        {
-            const int r = tid / 4, c = (tid % 4) * 8;
+    uint4 rx[NXI];  // 8 bf16 (or the first 4 of 8 fp32: rx2 holds the rest)
+    uint4 rx2[NXI];
+    float4 rw[NWI];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int it = 0; it < NXI; ++it) {
+            const int q = tid + 256 * it, r = q / (KC / 8), c = (q % (KC / 8)) * 8;
             const int t = t0 + r;
-            float v[8];
-            if (t < T) {
+            rx[it] = make_uint4(0, 0, 0, 0);
+            rx2[it] = make_uint4(0, 0, 0, 0);
+            if (q < NXQ && t < T) {
                 if (AF == MOE_DT_BF16) {
-                    const uint4 q = *reinterpret_cast<const uint4*>(
-                        static_cast<const uint16_t*>(x) + (size_t)t * d + k0 + c);
-                    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-                    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+                    rx[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + (size_t)t * d + k0 + c);
                 } else {
                     const float* p = static_cast<const float*>(x) + (size_t)t * d + k0 + c;
-                    const float4 a = *reinterpret_cast<const float4*>(p);
-                    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+                    rx[it] = *reinterpret_cast<const uint4*>(p);
+                    rx2[it] = *reinterpret_cast<const uint4*>(p + 4);
                 }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = 0.0f;
             }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xs[c + j][r] = v[j];
         }
-        // Wr tile: 64 experts x 32 columns; two float4 per thread
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int r = tid / 8 + 32 * p, c = (tid % 8) * 4;
+        for (int it = 0; it < NWI; ++it) {
+            const int q = tid + 256 * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
             const int e = e0 + r;
-            float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < E) w4 = *reinterpret_cast<const float4*>(wr + (size_t)e * d + k0 + c);
-            ws[c + 0][r] = w4.x;
-            ws[c + 1][r] = w4.y;
-            ws[c + 2][r] = w4.z;
-            ws[c + 3][r] = w4.w;
+            rw[it] = (q < NWQ && e < E) ? *reinterpret_cast<const float4*>(wr + (size_t)e * d + k0 + c)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int it = 0; it < NXI; ++it) {
+            const int q = tid + 256 * it, r = q / (KC / 8), c = (q % (KC / 8)) * 8;
+            if (q >= NXQ) break;
+            double* dst = &xs[r * PITCH + c];
+            if (AF == MOE_DT_BF16) {
+                const uint4 u = rx[it];
+                dst[0] = bf16_lo(u.x); dst[1] = bf16_hi(u.x); dst[2] = bf16_lo(u.y); dst[3] = bf16_hi(u.y);
+                dst[4] = bf16_lo(u.z); dst[5] = bf16_hi(u.z); dst[6] = bf16_lo(u.w); dst[7] = bf16_hi(u.w);
+            } else {
+                const uint4 a = rx[it], b = rx2[it];
+                dst[0] = __uint_as_float(a.x); dst[1] = __uint_as_float(a.y);
+                dst[2] = __uint_as_float(a.z); dst[3] = __uint_as_float(a.w);
+                dst[4] = __uint_as_float(b.x); dst[5] = __uint_as_float(b.y);
+                dst[6] = __uint_as_float(b.z); dst[7] = __uint_as_float(b.w);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NWI; ++it) {
+            const int q = tid + 256 * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
+            if (q >= NWQ) break;
+            double* dst = &ws[r * PITCH + c];
+            dst[0] = rw[it].x;
+            dst[1] = rw[it].y;
+            dst[2] = rw[it].z;
+            dst[3] = rw[it].w;
+        }
+    };
+
+    double acc[RT][RE];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < RE; ++j) acc[i][j] = 0.0;
+
+    gload(0);
+    for (int k0 = 0; k0 < d; k0 += KC) {
+        lstore();
         __syncthreads();
+        if (k0 + KC < d) gload(k0 + KC);
 #pragma unroll 4
-        for (int kk = 0; kk < RG_KC; ++kk) {
-            double xv[4], wv[4];
+        for (int kk = 0; kk < KC; kk += 2) {
+            double2 xv[RT], wv[RE];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = (double)xs[kk][ty + 16 * i];
+            for (int i = 0; i < RT; ++i)
+                xv[i] = *reinterpret_cast<const double2*>(&xs[(ty + NTY * i) * PITCH + kk]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wv[j] = (double)ws[kk][tx + 16 * j];
+            for (int j = 0; j < RE; ++j)
+                wv[j] = *reinterpret_cast<const double2*>(&ws[(tx + NTX * j) * PITCH + kk]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < RT; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __fma_rn(xv[i], wv[j], acc[i][j]);
+                for (int j = 0; j < RE; ++j) {
+                    acc[i][j] = __fma_rn(xv[i].x, wv[j].x, acc[i][j]);
+                    acc[i][j] = __fma_rn(xv[i].y, wv[j].y, acc[i][j]);
+                }
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + ty + 16 * i;
+    for (int i = 0; i < RT; ++i) {
+        const int t = t0 + ty + NTY * i;
         if (t >= T) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + tx + 16 * j;
+        for (int j = 0; j < RE; ++j) {
+            const int e = e0 + tx + NTX * j;
             if (e < E) logits[(size_t)t * E + e] = (float)acc[i][j];
         }
     }
@@ -184,6 +222,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
+template <int AF, int TM, int TE, int RT, int RE, int KC>
+static void router_gemm_tile(const RouteArgs& a, hipStream_t st, const KTime& kt) {
+    dim3 grid((a.T + TM - 1) / TM, (a.E + TE - 1) / TE);
+    launch_kernel(router_gemm_kernel<AF, TM, TE, RT, RE, KC>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E,
+                  a.logits);
+}
+
+// The largest tile that still gives every compute unit two workgroups; the
+// smallest when none does (few tokens).
+template <int AF>
+static void router_gemm_launch(const RouteArgs& a, hipStream_t st, const KTime& kt) {
+    auto blocks = [&](int tm, int te) { return (long)((a.T + tm - 1) / tm) * ((a.E + te - 1) / te); };
+    if (a.d % 64 == 0 && blocks(64, 64) >= 512) router_gemm_tile<AF, 64, 64, 4, 4, 32>(a, st, kt);
+    else if (a.d % 64 == 0 && blocks(32, 64) >= 512) router_gemm_tile<AF, 32, 64, 2, 4, 64>(a, st, kt);
+    else if (a.d % 128 == 0) router_gemm_tile<AF, 16, 32, 1, 2, 128>(a, st, kt);
+    else router_gemm_tile<AF, 16, 32, 1, 2, 64>(a, st, kt);
+}
+
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st, const KTime& kt) {
     if (a.T <= MOE_DECODE_MAX_TOKENS && !a.force_gemm) {
         dim3 grid(a.E);
@@ -191,12 +247,10 @@ hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st, const KTime&
             launch_kernel(router_gemv_kernel<MOE_DT_BF16>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
         else
             launch_kernel(router_gemv_kernel<MOE_DT_F32>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
+    } else if (a.act == MOE_DT_BF16) {
+        router_gemm_launch<MOE_DT_BF16>(a, st, kt);
     } else {
-        dim3 grid((a.T + RG_TM - 1) / RG_TM, (a.E + RG_TE - 1) / RG_TE);
-        if (a.act == MOE_DT_BF16)
-            launch_kernel(router_gemm_kernel<MOE_DT_BF16>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
-        else
-            launch_kernel(router_gemm_kernel<MOE_DT_F32>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
+        router_gemm_launch<MOE_DT_F32>(a, st, kt);
     }
     return hipGetLastError();
 }
