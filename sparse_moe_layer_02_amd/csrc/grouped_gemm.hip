@@ -58,6 +58,28 @@ __device__ __forceinline__ bool tile_rows(const FfnArgs& a, int tile, TileRows& 
     return true;
 }
 
+// The dispatcher deals consecutive workgroups to the 8 XCDs in turn, and each
+// XCD has its own L2.  Remap the linear workgroup index so that every XCD
+// receives one contiguous range of the logical work order (M tile fastest,
+// then N tile): the M tiles of one expert, which read the same weight tile,
+// then run side by side on one XCD and share its L2.
+constexpr int N_XCD = 8;
+constexpr bool TILE_FASTEST = true;
+
+__device__ __forceinline__ void work_item(int& tile, int& ntile) {
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int L = blockIdx.x + blockIdx.y * gx, N = gx * gy;
+    const int q = N / N_XCD, r = N % N_XCD, xcd = L % N_XCD, loc = L / N_XCD;
+    const int logical = xcd < r ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
+    if (TILE_FASTEST) {
+        tile = logical % gx;
+        ntile = logical / gx;
+    } else {
+        tile = logical / gy;
+        ntile = logical % gy;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gate/up
 // ---------------------------------------------------------------------------
@@ -66,11 +88,13 @@ constexpr int GU_BN = 64;  // columns of gate (and of up) per workgroup
 __global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + 2 * GU_BN) * ROWB];
     __shared__ int src_row[BM];
+    int tile, ntile;
+    work_item(tile, ntile);
     TileRows tr;
-    if (!tile_rows(a, blockIdx.x, tr)) return;
+    if (!tile_rows(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
     const int F = shared ? a.Fs : a.F;
-    const int n0 = blockIdx.y * GU_BN;
+    const int n0 = ntile * GU_BN;
     if (n0 >= F) return;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     const int K = a.d;
@@ -176,12 +200,14 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + DN_BN) * ROWB];
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
+    int tile, ntile;
+    work_item(tile, ntile);
     TileRows tr;
-    if (!tile_rows(a, blockIdx.x, tr)) return;
+    if (!tile_rows(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
     const int K = shared ? a.Fs : a.F;
     const int N = a.d;
-    const int n0 = blockIdx.y * DN_BN;
+    const int n0 = ntile * DN_BN;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     if (tid < BM) {
         int dst = -1;
