@@ -49,15 +49,24 @@ WORKLOADS = {
     "c3t2": dict(base="c3", T=2, copies=4, steps=200, warmup=20),
     "c4": dict(base="c4", T=512, copies=1, steps=20, warmup=5),
     "c5": dict(base="c5", T=4096, copies=1, steps=10, warmup=3),
+    # Compute-bound supplements for the matrix cores: s1 is c5's shared-expert
+    # shape alone (one dense SwiGLU over 4096 tokens: one expert, top-1, no
+    # shared expert); s2 is c4 with 16384 tokens (about 512 rows per expert).
+    "s1": dict(base="c5", T=4096, over=dict(label="s1", E=1, k=1, n_shared=0, bias="none"), copies=1,
+               steps=10, warmup=3, bound="mfma"),
+    "s2": dict(base="c4", T=16384, over=dict(label="s2"), copies=1, steps=5, warmup=2, bound="mfma"),
 }
 N_DECODE_TOKENS = 1024
 
 
 def describe(cfg):
     w = {"q8b32": "int8 blocks of 32 + fp16 scale", "bf16": "bf16", "f32": "fp32"}[cfg["w"]]
-    score = "sqrt(softplus) x%.1f" % cfg["scale"] if cfg["score"] == "sqrt_softplus" else "sigmoid+bias"
-    return ("%s: T=%d d=%d E=%d top-%d %s F=%d + shared F=%d, %s weights, %s activations"
-            % (cfg["name"], cfg["T"], cfg["d"], cfg["E"], cfg["k"], score, cfg["F"], cfg["Fs"], w, cfg["act"]))
+    score = "sqrt(softplus) x%.1f" % cfg["scale"] if cfg["score"] == "sqrt_softplus" else "sigmoid"
+    if cfg.get("bias", "none") != "none":
+        score += "+bias"
+    shared = " + shared F=%d" % cfg["Fs"] if cfg["n_shared"] else ", no shared expert"
+    return ("%s: T=%d d=%d E=%d top-%d %s F=%d%s, %s weights, %s activations"
+            % (cfg["name"], cfg["T"], cfg["d"], cfg["E"], cfg["k"], score, cfg["F"], shared, w, cfg["act"]))
 
 
 class Hip:
@@ -277,7 +286,7 @@ def main():
         from synth import configs as _cf
         from sparse_moe_layer_02_amd.binding import DECODE_MAX_TOKENS
         spec = WORKLOADS[args.workload]
-        cfg = _cf.get(spec["base"], T=spec["T"])
+        cfg = _cf.get(spec["base"], T=spec["T"], **spec.get("over", {}))
         dec = args.path == "decode" or (args.path == "auto" and cfg["T"] <= DECODE_MAX_TOKENS)
         record_traffic(args.workload, "decode" if dec else "prefill", cfg["w"], args.record_traffic[0],
                        args.record_traffic[1], (args.copy_probe_mib or 1024) * (1 << 20))
@@ -297,7 +306,7 @@ def main():
     spec = WORKLOADS[args.workload]
     steps = args.steps or spec["steps"]
     warmup = spec["warmup"] if args.warmup is None else args.warmup
-    cfg = configs.get(spec["base"], T=spec["T"])
+    cfg = configs.get(spec["base"], T=spec["T"], **spec.get("over", {}))
     T = cfg["T"]
     decode = args.path == "decode" or (args.path == "auto" and T <= moe.DECODE_MAX_TOKENS)
     n_copies = args.copies or spec["copies"]
@@ -412,10 +421,17 @@ def main():
     achieved = float(np.mean(gu_bytes)) / (gu_us * 1e-6) / 1e9
     path_kind = "decode" if decode else "prefill"
     traffic = traffic_record(path_kind, cfg["w"], args.workload)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dominant(path_kind, cfg["w"])[0], "bytes_per_launch": float(np.mean(gu_bytes)),
-                "avg_launch_us": gu_us}
+    if spec.get("bound") == "mfma":
+        tfs = flops_gu / (gu_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
+                    "frac": round(tfs / BF16_PEAK_TFS, 4), "traffic": traffic,
+                    "kernel": dominant(path_kind, cfg["w"])[0], "flops_per_launch": flops_gu,
+                    "bytes_per_launch": float(np.mean(gu_bytes)), "avg_launch_us": gu_us}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": dominant(path_kind, cfg["w"])[0], "bytes_per_launch": float(np.mean(gu_bytes)),
+                    "avg_launch_us": gu_us}
 
     value = T * steps / (total_ms * 1e-3)
     out = {

@@ -55,10 +55,18 @@ int ldh_of(const moe_config* c) {
     return c->n_shared ? (c->d_ff > c->d_ff_shared ? c->d_ff : c->d_ff_shared) : c->d_ff;
 }
 
-int max_tiles_of(const moe_config* c) {
+// Rows per grouped-GEMM tile: 128 once experts average 96 rows or more
+// (fewer re-reads of each weight tile, more MFMA work per LDS byte), else 64.
+int gemm_bm(const moe_config* c) {
     const long n = (long)c->n_tokens * c->top_k;
-    long t = (n + GEMM_BM - 1) / GEMM_BM + (n < c->n_expert ? n : c->n_expert);
-    if (c->n_shared) t += (c->n_tokens + GEMM_BM - 1) / GEMM_BM;
+    return n >= 96L * c->n_expert ? 128 : 64;
+}
+
+// Upper bound on the tiles of bm rows: every expert's last tile may be partial.
+int max_tiles_of(const moe_config* c, int bm) {
+    const long n = (long)c->n_tokens * c->top_k;
+    long t = (n + bm - 1) / bm + (n < c->n_expert ? n : c->n_expert);
+    if (c->n_shared) t += (c->n_tokens + bm - 1) / bm;
     return (int)t;
 }
 
@@ -68,7 +76,7 @@ Layout make_layout(const moe_config* c) {
     const size_t d = (size_t)c->d_model, n = T * k;
     const size_t hsz = c->act_dtype == MOE_DT_BF16 ? 2 : 4;
     L.n_blk = (int)((n + PERM_BLOCK - 1) / PERM_BLOCK);
-    L.max_tiles = max_tiles_of(c);
+    L.max_tiles = max_tiles_of(c, GEMM_BM);  // the smallest tile: capacity for any bm
     size_t o = 0;
     auto take = [&](size_t bytes) {
         size_t at = o;
@@ -141,7 +149,7 @@ PermArgs perm_args(const moe_config* c, const Layout& L, void* ws, const int32_t
     p.active = at<int32_t>(ws, L.active);
     p.tiles = at<int2>(ws, L.tiles);
     p.n_blk = L.n_blk;
-    p.bm = GEMM_BM;
+    p.bm = gemm_bm(c);
     return p;
 }
 
@@ -175,7 +183,8 @@ FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, 
     f.slot_out = at<float>(ws, L.slot_out);
     f.shared_out = c->n_shared ? at<float>(ws, L.shared_out) : nullptr;
     f.y = nullptr;
-    f.max_tiles = L.max_tiles;
+    f.bm = gemm_bm(c);
+    f.max_tiles = max_tiles_of(c, f.bm);
     f.shared_done = 0;
     f.grid_has_shared = 0;
     return f;

@@ -13,20 +13,23 @@
 // are expert tiles over gate/up then down (the LUT bug note and "GLM-5.2 CUDA
 // port").
 //
-// Work list: the permutation step writes tiles (group, first row) of GEMM_BM
-// rows; the grid is (tile slot, N tile) and slots past the device-side count
-// exit at once.  Tiles: 64 rows x 64 N columns (gate/up: 64 gate + 64 up
-// columns; down: 128 columns), K staged through LDS in 64-wide double-buffered
-// chunks; 16-byte chunks are XOR-swizzled by row so the MFMA operand reads are
-// free of bank conflicts.  Each wavefront owns a 32-row half and 32 (gate/up)
-// or 64 (down) columns, so gate and up for the same output columns meet in one
+// Work list: the permutation step writes tiles (group, first row) of bm rows
+// (128 when experts average 96 rows or more, else 64); the grid is (tile
+// slot, N tile), remapped per XCD (work_item), and slots past the
+// device-side count exit at once.  A workgroup computes bm rows by 64 gate
+// + 64 up columns (gate/up) or by 128 output columns (down), K staged
+// through LDS in 64-wide double-buffered chunks.  Global loads run two chunks
+// ahead through two register sets and are unconditional (addresses clamped
+// into the tensors, out-of-tile rows zeroed on the way into LDS).  16-byte
+// chunks are XOR-swizzled by row so the MFMA operand reads do not pile onto
+// the same banks.  Each wavefront owns bm/2 rows and 32 (gate/up) or 64
+// (down) columns, so gate and up for the same output columns meet in one
 // wavefront's registers for the SiLU*mul epilogue.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int BM = GEMM_BM;  // 64
 constexpr int BK = 64;
 constexpr int ROWB = BK * 2;  // bytes per LDS tile row (128)
 
@@ -44,6 +47,7 @@ struct TileRows {
     int nrows;    // valid rows (<= BM)
 };
 
+template <int BM>
 __device__ __forceinline__ bool tile_rows(const FfnArgs& a, int tile, TileRows& tr) {
     if (tile >= a.meta[1]) return false;
     const int2 t = a.tiles[tile];
@@ -57,27 +61,34 @@ __device__ __forceinline__ bool tile_rows(const FfnArgs& a, int tile, TileRows& 
     }
     return true;
 }
+// A 16-byte value, or zero when !keep; a select, not a branch, so the loads
+// that feed it stay unconditional (callers clamp their addresses into the
+// tensor) and the compiler can count them exactly in its load waits.
+__device__ __forceinline__ uint4 keep_or_zero(uint4 v, bool keep) {
+    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
 
 // The dispatcher deals consecutive workgroups to the 8 XCDs in turn, and each
 // XCD has its own L2.  Remap the linear workgroup index so that every XCD
-// receives one contiguous range of the logical work order (M tile fastest,
-// then N tile): the M tiles of one expert, which read the same weight tile,
-// then run side by side on one XCD and share its L2.
+// receives one contiguous range of the logical work order.  That order walks
+// groups of NG N tiles; inside a group, M tile by M tile, all N tiles of the
+// group.  The workgroups an XCD runs side by side then cover a block of M
+// tiles x NG N tiles: each weight tile is read by the M tiles of its expert
+// and each A tile (rows of x or h) by the group's N tiles, mostly from that
+// XCD's L2.  NG = 4 pays off for 128-row tiles (experts with many rows); with
+// 64-row tiles (few rows per expert, bandwidth-bound) NG = 1 streams best.
 constexpr int N_XCD = 8;
-constexpr bool TILE_FASTEST = true;
 
+template <int NG>
 __device__ __forceinline__ void work_item(int& tile, int& ntile) {
     const int gx = gridDim.x, gy = gridDim.y;
     const int L = blockIdx.x + blockIdx.y * gx, N = gx * gy;
     const int q = N / N_XCD, r = N % N_XCD, xcd = L % N_XCD, loc = L / N_XCD;
     const int logical = xcd < r ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
-    if (TILE_FASTEST) {
-        tile = logical % gx;
-        ntile = logical / gx;
-    } else {
-        tile = logical / gy;
-        ntile = logical % gy;
-    }
+    const int group = logical / (gx * NG), rem = logical % (gx * NG);
+    const int gsize = min(NG, gy - group * NG);
+    tile = rem / gsize;
+    ntile = group * NG + rem % gsize;
 }
 
 // ---------------------------------------------------------------------------
@@ -85,13 +96,18 @@ __device__ __forceinline__ void work_item(int& tile, int& ntile) {
 // ---------------------------------------------------------------------------
 constexpr int GU_BN = 64;  // columns of gate (and of up) per workgroup
 
-__global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a) {
+// BM rows x (64 gate + 64 up) columns per workgroup; wavefront (mh, nh) owns
+// rows [BM/2 * mh, BM/2 * (mh + 1)) and columns [32 nh, 32 nh + 32) of both
+// gate and up, as MT = BM/64 blocks of 32 rows.
+template <int BM>
+__global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
+    constexpr int MT = BM / 64, AP = BM / 32;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + 2 * GU_BN) * ROWB];
     __shared__ int src_row[BM];
     int tile, ntile;
-    work_item(tile, ntile);
+    work_item<BM == 128 ? 4 : 1>(tile, ntile);
     TileRows tr;
-    if (!tile_rows(a, tile, tr)) return;
+    if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
     const int F = shared ? a.Fs : a.F;
     const int n0 = ntile * GU_BN;
@@ -119,75 +135,112 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a) {
     const uint16_t* ubase = static_cast<const uint16_t*>(U.q) + ((size_t)ge * F + n0) * K;
     const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
 
-    // global -> register staging: each thread moves 2 A chunks, 2 gate, 2 up chunks of 16 B
-    const int ch = tid & 7, r_lo = tid >> 3;  // rows r_lo and r_lo + 32
-    int arow[2];
+    // global -> register staging: each thread moves AP chunks of A and 2 of gate, 2 of up (16 B each)
+    const int ch = tid & 7, r_lo = tid >> 3;  // rows r_lo + 32 p
+    int arow[AP];
     bool bval[2];
 #pragma unroll
+    for (int p = 0; p < AP; ++p) arow[p] = src_row[r_lo + 32 * p];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) bval[p] = n0 + r_lo + 32 * p < F;
+    struct Stage {
+        uint4 a[AP], g[2], u[2];
+    };
+    // row pointers clamped into the tensors; rows past the tile read a valid
+    // row and are zeroed
+    const uint16_t* ap[AP];
+    const uint16_t *gp[2], *up[2];
+#pragma unroll
+    for (int p = 0; p < AP; ++p) ap[p] = xbase + (size_t)(arow[p] >= 0 ? arow[p] : 0) * K + ch * 8;
+#pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const int r = r_lo + 32 * p;
-        arow[p] = src_row[r];
-        bval[p] = n0 + r < F;
+        const int r = bval[p] ? r_lo + 32 * p : 0;
+        gp[p] = gbase + (size_t)r * K + ch * 8;
+        up[p] = ubase + (size_t)r * K + ch * 8;
     }
-    uint4 ra[2], rg[2], ru[2];
-    auto gload = [&](int k0) {
+    auto gload = [&](Stage& R, int k0) {
+#pragma unroll
+        for (int p = 0; p < AP; ++p) R.a[p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int r = r_lo + 32 * p;
-            ra[p] = arow[p] >= 0 ? *reinterpret_cast<const uint4*>(xbase + (size_t)arow[p] * K + k0 + ch * 8)
-                                 : make_uint4(0, 0, 0, 0);
-            rg[p] = bval[p] ? *reinterpret_cast<const uint4*>(gbase + (size_t)r * K + k0 + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
-            ru[p] = bval[p] ? *reinterpret_cast<const uint4*>(ubase + (size_t)r * K + k0 + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
+            R.g[p] = *reinterpret_cast<const uint4*>(gp[p] + k0);
+            R.u[p] = *reinterpret_cast<const uint4*>(up[p] + k0);
         }
     };
-    auto lstore = [&](int s) {
+    auto lstore = [&](const Stage& R, int s) {
+#pragma unroll
+        for (int p = 0; p < AP; ++p)
+            *reinterpret_cast<uint4*>(&lds[s][lds_off(r_lo + 32 * p, ch)]) = keep_or_zero(R.a[p], arow[p] >= 0);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int r = r_lo + 32 * p;
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(r, ch)]) = ra[p];
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + r, ch)]) = rg[p];
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + GU_BN + r, ch)]) = ru[p];
+            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + r, ch)]) = keep_or_zero(R.g[p], bval[p]);
+            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + GU_BN + r, ch)]) = keep_or_zero(R.u[p], bval[p]);
         }
     };
 
     const int mh = wave & 1, nh = wave >> 1;
-    f32x16_t accg = {}, accu = {};
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    int cur = 0;
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        const bool more = k0 + BK < K;
-        if (more) gload(k0 + BK);
-        const uint8_t* L = lds[cur];
+    f32x16_t accg[MT], accu[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        accg[i] = f32x16_t{};
+        accu[i] = f32x16_t{};
+    }
+    // All fragments of a chunk are read before its MFMAs, so the LDS latency
+    // of the later ones overlaps the earlier MFMAs.
+    auto compute = [&](int s) {
+        const uint8_t* L = lds[s];
+        bf16x8_t fg[BK / 16], fu[BK / 16], fa[BK / 16][MT];
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int c = 2 * kk + (lane >> 5);
-            const bf16x8_t fa = lds_frag(L, 32 * mh + (lane & 31), c);
-            const bf16x8_t fg = lds_frag(L, BM + 32 * nh + (lane & 31), c);
-            const bf16x8_t fu = lds_frag(L, BM + GU_BN + 32 * nh + (lane & 31), c);
-            accg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fg, accg, 0, 0, 0);
-            accu = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fu, accu, 0, 0, 0);
+            fg[kk] = lds_frag(L, BM + 32 * nh + (lane & 31), c);
+            fu[kk] = lds_frag(L, BM + GU_BN + 32 * nh + (lane & 31), c);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) fa[kk][i] = lds_frag(L, (BM / 2) * mh + 32 * i + (lane & 31), c);
         }
-        if (more) lstore(cur ^ 1);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                accg[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fg[kk], accg[i], 0, 0, 0);
+                accu[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fu[kk], accu[i], 0, 0, 0);
+            }
+    };
+    // Two register sets: the loads of chunk j + 2 are issued while chunk j is
+    // consumed, and stored to LDS one chunk later, so each load has two
+    // chunks' worth of arithmetic to arrive.
+    Stage R0, R1;
+    gload(R0, 0);
+    if (BK < K) gload(R1, BK);
+    lstore(R0, 0);
+    __syncthreads();
+    for (int k0 = 0; k0 < K; k0 += 2 * BK) {
+        if (k0 + 2 * BK < K) gload(R0, k0 + 2 * BK);
+        compute(0);
+        if (k0 + BK < K) lstore(R1, 1);
         __syncthreads();
-        cur ^= 1;
+        if (k0 + BK >= K) break;
+        if (k0 + 3 * BK < K) gload(R1, k0 + 3 * BK);
+        compute(1);
+        if (k0 + 2 * BK < K) lstore(R0, 0);
+        __syncthreads();
     }
 
-    // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4
+    // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each block
     const int col = n0 + 32 * nh + (lane & 31);
     if (col < F) {
         uint16_t* h = static_cast<uint16_t*>(a.h);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = 32 * mh + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (row < tr.nrows) {
-                const float g = accg[v], u = accu[v];
-                h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = (BM / 2) * mh + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < tr.nrows) {
+                    const float g = accg[i][v], u = accu[i][v];
+                    h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+                }
             }
-        }
     }
 }
 
@@ -196,14 +249,19 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int DN_BN = 128;
 
-__global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a) {
+// BM rows x 128 output columns per workgroup; wavefront (mh, nh) owns rows
+// [BM/2 * mh, BM/2 * (mh + 1)) as MT = BM/64 blocks of 32, and columns
+// [64 nh, 64 nh + 64) as two 32-column blocks.
+template <int BM>
+__global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
+    constexpr int MT = BM / 64, AP = BM / 32;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + DN_BN) * ROWB];
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
     int tile, ntile;
-    work_item(tile, ntile);
+    work_item<BM == 128 ? 4 : 1>(tile, ntile);
     TileRows tr;
-    if (!tile_rows(a, tile, tr)) return;
+    if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
     const int K = shared ? a.Fs : a.F;
     const int N = a.d;
@@ -235,83 +293,106 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a) {
     const uint16_t* hbase = static_cast<const uint16_t*>(a.h);
 
     const int ch = tid & 7, r_lo = tid >> 3;
-    bool aval[2], bval[4];
+    bool aval[AP], bval[4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) aval[p] = r_lo + 32 * p < tr.nrows;
+    for (int p = 0; p < AP; ++p) aval[p] = r_lo + 32 * p < tr.nrows;
 #pragma unroll
     for (int p = 0; p < 4; ++p) bval[p] = n0 + r_lo + 32 * p < N;
-    uint4 ra[2], rb[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int r = r_lo + 32 * p;
-            ra[p] = aval[p] ? *reinterpret_cast<const uint4*>(hbase + (size_t)(tr.rbeg + r) * a.ldh + k0 + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = r_lo + 32 * p;
-            rb[p] = bval[p] ? *reinterpret_cast<const uint4*>(dbase + (size_t)r * K + k0 + ch * 8)
-                            : make_uint4(0, 0, 0, 0);
-        }
+    struct Stage {
+        uint4 a[AP], b[4];
     };
-    auto lstore = [&](int s) {
+    const uint16_t* ap[AP];
+    const uint16_t* bp[4];
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(r_lo + 32 * p, ch)]) = ra[p];
+    for (int p = 0; p < AP; ++p) ap[p] = hbase + (size_t)(tr.rbeg + (aval[p] ? r_lo + 32 * p : 0)) * a.ldh + ch * 8;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) bp[p] = dbase + (size_t)(bval[p] ? r_lo + 32 * p : 0) * K + ch * 8;
+    auto gload = [&](Stage& R, int k0) {
+#pragma unroll
+        for (int p = 0; p < AP; ++p) R.a[p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) R.b[p] = *reinterpret_cast<const uint4*>(bp[p] + k0);
+    };
+    auto lstore = [&](const Stage& R, int s) {
+#pragma unroll
+        for (int p = 0; p < AP; ++p)
+            *reinterpret_cast<uint4*>(&lds[s][lds_off(r_lo + 32 * p, ch)]) = keep_or_zero(R.a[p], aval[p]);
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + r_lo + 32 * p, ch)]) = rb[p];
+            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + r_lo + 32 * p, ch)]) = keep_or_zero(R.b[p], bval[p]);
     };
 
-    const int mh = wave & 1, nh = wave >> 1;  // wave: 32 rows x 64 columns (two 32x32 tiles)
-    f32x16_t acc0 = {}, acc1 = {};
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    int cur = 0;
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        const bool more = k0 + BK < K;
-        if (more) gload(k0 + BK);
-        const uint8_t* L = lds[cur];
+    const int mh = wave & 1, nh = wave >> 1;
+    f32x16_t acc0[MT], acc1[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        acc0[i] = f32x16_t{};
+        acc1[i] = f32x16_t{};
+    }
+    auto compute = [&](int s) {
+        const uint8_t* L = lds[s];
+        bf16x8_t f0[BK / 16], f1[BK / 16], fa[BK / 16][MT];
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int c = 2 * kk + (lane >> 5);
-            const bf16x8_t fa = lds_frag(L, 32 * mh + (lane & 31), c);
-            const bf16x8_t f0 = lds_frag(L, BM + 64 * nh + (lane & 31), c);
-            const bf16x8_t f1 = lds_frag(L, BM + 64 * nh + 32 + (lane & 31), c);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, f0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, f1, acc1, 0, 0, 0);
+            f0[kk] = lds_frag(L, BM + 64 * nh + (lane & 31), c);
+            f1[kk] = lds_frag(L, BM + 64 * nh + 32 + (lane & 31), c);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) fa[kk][i] = lds_frag(L, (BM / 2) * mh + 32 * i + (lane & 31), c);
         }
-        if (more) lstore(cur ^ 1);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], f0[kk], acc0[i], 0, 0, 0);
+                acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], f1[kk], acc1[i], 0, 0, 0);
+            }
+    };
+    Stage R0, R1;
+    gload(R0, 0);
+    if (BK < K) gload(R1, BK);
+    lstore(R0, 0);
+    __syncthreads();
+    for (int k0 = 0; k0 < K; k0 += 2 * BK) {
+        if (k0 + 2 * BK < K) gload(R0, k0 + 2 * BK);
+        compute(0);
+        if (k0 + BK < K) lstore(R1, 1);
         __syncthreads();
-        cur ^= 1;
+        if (k0 + BK >= K) break;
+        if (k0 + 3 * BK < K) gload(R1, k0 + 3 * BK);
+        compute(1);
+        if (k0 + 2 * BK < K) lstore(R0, 0);
+        __syncthreads();
     }
 
     float* out = shared ? a.shared_out : a.slot_out;
     const int c0 = n0 + 64 * nh + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int row = 32 * mh + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < tr.nrows && dst_row[row] >= 0) {
-            const size_t base = (size_t)dst_row[row] * N;
-            const float w = wrow[row];
-            if (c0 < N) out[base + c0] = w * acc0[v];
-            if (c0 + 32 < N) out[base + c0 + 32] = w * acc1[v];
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = (BM / 2) * mh + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row < tr.nrows && dst_row[row] >= 0) {
+                const size_t base = (size_t)dst_row[row] * N;
+                const float w = wrow[row];
+                if (c0 < N) out[base + c0] = w * acc0[i][v];
+                if (c0 + 32 < N) out[base + c0 + 32] = w * acc1[i][v];
+            }
         }
-    }
 }
 
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
     dim3 grid(a.max_tiles, (fmax + GU_BN - 1) / GU_BN);
-    launch_kernel(gateup_mfma_kernel, grid, 256, st, kt, a);
+    if (a.bm == 128) launch_kernel(gateup_mfma_kernel<128>, grid, 256, st, kt, a);
+    else launch_kernel(gateup_mfma_kernel<64>, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     dim3 grid(a.max_tiles, (a.d + DN_BN - 1) / DN_BN);
-    launch_kernel(down_mfma_kernel, grid, 256, st, kt, a);
+    if (a.bm == 128) launch_kernel(down_mfma_kernel<128>, grid, 256, st, kt, a);
+    else launch_kernel(down_mfma_kernel<64>, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 

@@ -88,7 +88,8 @@ struct FfnArgs {
     float* slot_out;        // [T*k, d]
     float* shared_out;      // [T, d]
     float* y;               // [T, d] (fused combine)
-    int max_tiles;
+    int max_tiles;          // grid bound of the grouped GEMMs (tiles of bm rows)
+    int bm;                 // rows per grouped-GEMM tile: 64 or 128
     int shared_done;        // the shared expert's h rows were already produced (decode route kernel)
     int grid_has_shared;    // set by the launchers: the last grid slot is the shared expert
 };

@@ -56,11 +56,12 @@ CONFIGS = {
 }
 
 
-def get(name: str, **over) -> dict:
-    """A copy of workload ``name`` with fields overridden (e.g. ``T=2``)."""
+def get(name: str, label: str | None = None, **over) -> dict:
+    """A copy of workload ``name`` with fields overridden (e.g. ``T=2``),
+    named ``label`` if given."""
     cfg = copy.deepcopy(CONFIGS[name])
     cfg.update(over)
-    cfg["name"] = name
+    cfg["name"] = label or name
     cfg.setdefault("seed", 0)
     return cfg
 
