@@ -61,12 +61,11 @@ __device__ __forceinline__ bool tile_rows(const FfnArgs& a, int tile, TileRows& 
     }
     return true;
 }
-// A 16-byte value, or zero when !keep; a select, not a branch, so the loads
-// that feed it stay unconditional (callers clamp their addresses into the
-// tensor) and the compiler can count them exactly in its load waits.
-__device__ __forceinline__ uint4 keep_or_zero(uint4 v, bool keep) {
-    return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
-}
+// 16 bytes as a vector value (kept in registers; a struct copy of uint4 can
+// end up in scratch memory when staged across a loop).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(uint8_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // The dispatcher deals consecutive workgroups to the 8 XCDs in turn, and each
 // XCD has its own L2.  Remap the linear workgroup index so that every XCD
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) bval[p] = n0 + r_lo + 32 * p < F;
     struct Stage {
-        uint4 a[AP], g[2], u[2];
+        u32x4 a[AP], g[2], u[2];
     };
     // row pointers clamped into the tensors; rows past the tile read a valid
     // row and are zeroed
@@ -160,22 +159,21 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
     }
     auto gload = [&](Stage& R, int k0) {
 #pragma unroll
-        for (int p = 0; p < AP; ++p) R.a[p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
+        for (int p = 0; p < AP; ++p) R.a[p] = ld16(ap[p] + k0);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            R.g[p] = *reinterpret_cast<const uint4*>(gp[p] + k0);
-            R.u[p] = *reinterpret_cast<const uint4*>(up[p] + k0);
+            R.g[p] = ld16(gp[p] + k0);
+            R.u[p] = ld16(up[p] + k0);
         }
     };
     auto lstore = [&](const Stage& R, int s) {
 #pragma unroll
-        for (int p = 0; p < AP; ++p)
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(r_lo + 32 * p, ch)]) = keep_or_zero(R.a[p], arow[p] >= 0);
+        for (int p = 0; p < AP; ++p) st16(&lds[s][lds_off(r_lo + 32 * p, ch)], R.a[p]);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int r = r_lo + 32 * p;
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + r, ch)]) = keep_or_zero(R.g[p], bval[p]);
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + GU_BN + r, ch)]) = keep_or_zero(R.u[p], bval[p]);
+            st16(&lds[s][lds_off(BM + r, ch)], R.g[p]);
+            st16(&lds[s][lds_off(BM + GU_BN + r, ch)], R.u[p]);
         }
     };
 
@@ -186,25 +184,25 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
         accg[i] = f32x16_t{};
         accu[i] = f32x16_t{};
     }
-    // All fragments of a chunk are read before its MFMAs, so the LDS latency
-    // of the later ones overlaps the earlier MFMAs.
-    auto compute = [&](int s) {
+    // Half a chunk (two 16-wide steps of K): fragments first, then MFMAs.
+    auto compute = [&](int s, int half) {
         const uint8_t* L = lds[s];
-        bf16x8_t fg[BK / 16], fu[BK / 16], fa[BK / 16][MT];
+        bf16x8_t fg[2], fu[2], fa[2][MT];
+        auto frags = [&](int j) {
+            const int c = 2 * (2 * half + j) + (lane >> 5);
+            fg[j] = lds_frag(L, BM + 32 * nh + (lane & 31), c);
+            fu[j] = lds_frag(L, BM + GU_BN + 32 * nh + (lane & 31), c);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = 2 * kk + (lane >> 5);
-            fg[kk] = lds_frag(L, BM + 32 * nh + (lane & 31), c);
-            fu[kk] = lds_frag(L, BM + GU_BN + 32 * nh + (lane & 31), c);
+            for (int i = 0; i < MT; ++i) fa[j][i] = lds_frag(L, (BM / 2) * mh + 32 * i + (lane & 31), c);
+        };
+        frags(0);
+        frags(1);
 #pragma unroll
-            for (int i = 0; i < MT; ++i) fa[kk][i] = lds_frag(L, (BM / 2) * mh + 32 * i + (lane & 31), c);
-        }
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
-                accg[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fg[kk], accg[i], 0, 0, 0);
-                accu[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fu[kk], accu[i], 0, 0, 0);
+                accg[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j][i], fg[j], accg[i], 0, 0, 0);
+                accu[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j][i], fu[j], accu[i], 0, 0, 0);
             }
     };
     // Two register sets: the loads of chunk j + 2 are issued while chunk j is
@@ -217,12 +215,14 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
     __syncthreads();
     for (int k0 = 0; k0 < K; k0 += 2 * BK) {
         if (k0 + 2 * BK < K) gload(R0, k0 + 2 * BK);
-        compute(0);
+        compute(0, 0);
+        compute(0, 1);
         if (k0 + BK < K) lstore(R1, 1);
         __syncthreads();
         if (k0 + BK >= K) break;
         if (k0 + 3 * BK < K) gload(R1, k0 + 3 * BK);
-        compute(1);
+        compute(1, 0);
+        compute(1, 1);
         if (k0 + 2 * BK < K) lstore(R0, 0);
         __syncthreads();
     }
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) bval[p] = n0 + r_lo + 32 * p < N;
     struct Stage {
-        uint4 a[AP], b[4];
+        u32x4 a[AP], b[4];
     };
     const uint16_t* ap[AP];
     const uint16_t* bp[4];
@@ -309,17 +309,15 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
     for (int p = 0; p < 4; ++p) bp[p] = dbase + (size_t)(bval[p] ? r_lo + 32 * p : 0) * K + ch * 8;
     auto gload = [&](Stage& R, int k0) {
 #pragma unroll
-        for (int p = 0; p < AP; ++p) R.a[p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
+        for (int p = 0; p < AP; ++p) R.a[p] = ld16(ap[p] + k0);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) R.b[p] = *reinterpret_cast<const uint4*>(bp[p] + k0);
+        for (int p = 0; p < 4; ++p) R.b[p] = ld16(bp[p] + k0);
     };
     auto lstore = [&](const Stage& R, int s) {
 #pragma unroll
-        for (int p = 0; p < AP; ++p)
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(r_lo + 32 * p, ch)]) = keep_or_zero(R.a[p], aval[p]);
+        for (int p = 0; p < AP; ++p) st16(&lds[s][lds_off(r_lo + 32 * p, ch)], R.a[p]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            *reinterpret_cast<uint4*>(&lds[s][lds_off(BM + r_lo + 32 * p, ch)]) = keep_or_zero(R.b[p], bval[p]);
+        for (int p = 0; p < 4; ++p) st16(&lds[s][lds_off(BM + r_lo + 32 * p, ch)], R.b[p]);
     };
 
     const int mh = wave & 1, nh = wave >> 1;
@@ -329,23 +327,24 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
         acc0[i] = f32x16_t{};
         acc1[i] = f32x16_t{};
     }
-    auto compute = [&](int s) {
+    auto compute = [&](int s, int half) {
         const uint8_t* L = lds[s];
-        bf16x8_t f0[BK / 16], f1[BK / 16], fa[BK / 16][MT];
+        bf16x8_t f0[2], f1[2], fa[2][MT];
+        auto frags = [&](int j) {
+            const int c = 2 * (2 * half + j) + (lane >> 5);
+            f0[j] = lds_frag(L, BM + 64 * nh + (lane & 31), c);
+            f1[j] = lds_frag(L, BM + 64 * nh + 32 + (lane & 31), c);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = 2 * kk + (lane >> 5);
-            f0[kk] = lds_frag(L, BM + 64 * nh + (lane & 31), c);
-            f1[kk] = lds_frag(L, BM + 64 * nh + 32 + (lane & 31), c);
+            for (int i = 0; i < MT; ++i) fa[j][i] = lds_frag(L, (BM / 2) * mh + 32 * i + (lane & 31), c);
+        };
+        frags(0);
+        frags(1);
 #pragma unroll
-            for (int i = 0; i < MT; ++i) fa[kk][i] = lds_frag(L, (BM / 2) * mh + 32 * i + (lane & 31), c);
-        }
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
-                acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], f0[kk], acc0[i], 0, 0, 0);
-                acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], f1[kk], acc1[i], 0, 0, 0);
+                acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j][i], f0[j], acc0[i], 0, 0, 0);
+                acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j][i], f1[j], acc1[i], 0, 0, 0);
             }
     };
     Stage R0, R1;
@@ -355,12 +354,14 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
     __syncthreads();
     for (int k0 = 0; k0 < K; k0 += 2 * BK) {
         if (k0 + 2 * BK < K) gload(R0, k0 + 2 * BK);
-        compute(0);
+        compute(0, 0);
+        compute(0, 1);
         if (k0 + BK < K) lstore(R1, 1);
         __syncthreads();
         if (k0 + BK >= K) break;
         if (k0 + 3 * BK < K) gload(R1, k0 + 3 * BK);
-        compute(1);
+        compute(1, 0);
+        compute(1, 1);
         if (k0 + 2 * BK < K) lstore(R0, 0);
         __syncthreads();
     }
