@@ -236,9 +236,9 @@ def copy_probe(torch, hip, stream, mib):
 
 
 def cpu_baseline(cfg, L, x_all, target_s=12.0):
-    """The oracle, as it stands, on a bounded sample of the workload: a short
-    call on 4 tokens sizes the sample for about ``target_s`` seconds, then the
-    sample is timed in one call."""
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    sample grows (8 tokens, then as the last call's rate suggests) until one
+    call takes at least half of ``target_s`` seconds; that call is reported."""
     import numpy as np
     from oracle import Oracle
     orc = Oracle()
@@ -251,9 +251,11 @@ def cpu_baseline(cfg, L, x_all, target_s=12.0):
         orc.layer_forward(cfg, Ls, debug=False)
         return time.perf_counter() - t0
 
-    rate = 4 / run(4)
-    n = int(max(8, min(x_all.shape[0], rate * target_s)))
+    n, cap = 8, x_all.shape[0]
     dt = run(n)
+    while dt < target_s / 2 and n < cap:
+        n = int(min(cap, max(2 * n, n * target_s / max(dt, 1e-3))))
+        dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d tokens of the same workload in one call (token-major fp64 oracle, %d OpenMP threads),"
                       " %.1f s wall" % (n, threads, dt)}
