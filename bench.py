@@ -180,7 +180,7 @@ def _counter_rows(path):
     return out
 
 
-def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes):
+def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes, rec_path=None):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) into HBM bytes per launch of the dominant kernel.  Each counter is
     scaled by the factor that makes it read right on the plain device copy of
@@ -203,7 +203,7 @@ def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes):
         res[key + "_bytes_per_launch"] = kib * 1024.0 * factor
         res[key + "_launches"] = len(kern)
     res["hbm_bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
-    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec_path = rec_path or os.path.join(ROOT, "profiles", "traffic.json")
     recs = {}
     if os.path.exists(rec_path):
         with open(rec_path) as f:
