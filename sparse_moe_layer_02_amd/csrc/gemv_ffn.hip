@@ -44,8 +44,9 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(FfnArgs a) {
     }
     const int row0 = (blockIdx.x * 4 + wave_index()) * RG;
     if (row0 >= F) return;
-    gateup_wave<WF, AF, RG, MT, RG == 1 ? 4 : 2>(a, shared, e, F, r0, m, row0,
-                                                 shared ? nullptr : a.perm_rows + r0);
+    // two 16-byte loads per weight row in flight per lane (a 4096-wide int8
+    // row is read in two halves): measured slightly faster than the whole row
+    gateup_wave<WF, AF, RG, MT, 2>(a, shared, e, F, r0, m, row0, shared ? nullptr : a.perm_rows + r0);
 }
 
 // ---------------------------------------------------------------------------
