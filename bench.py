@@ -295,8 +295,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the MoE layer on a single MI355X "
-              "(see DESIGN.md for how it would shard); --gpus %d is not supported" % args.gpus,
+        print("bench.py measures one GPU: the MoE layer runs on a single MI355X "
+              "(expert-parallel sharding across GPUs is not built); --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

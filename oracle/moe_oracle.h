@@ -102,7 +102,7 @@ uint16_t moe_ref_bf16_from_f64(double v);
 float moe_ref_f16_to_f32(uint16_t h);
 float moe_ref_score(int32_t score, float logit);
 const char *moe_ref_status_str(int status);
-int moe_ref_mutant(void); /* which planted mistake this build carries (0 = none) */
+int moe_ref_mutant(void); /* which planted mistake this compiled copy carries (0 = none) */
 int moe_ref_threads(void); /* OpenMP threads the token loops use */
 
 #ifdef __cplusplus

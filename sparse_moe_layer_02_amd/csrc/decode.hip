@@ -214,7 +214,9 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(FfnArgs a) {
             for (int r = 0; r < DD_R; ++r)
 #pragma unroll
                 for (int i = 0; i < MT; ++i) acc[r][i] = 0.0f;
-            wave_dot<WF, AF, DD_R, MT>(wq, ws, hr, nt, F, acc);
+            // one chunk of each of the DD_R rows in flight per lane: with four rows
+            // per wavefront that already covers the latency (measured faster than two)
+            wave_dot<WF, AF, DD_R, MT, 1>(wq, ws, hr, nt, F, acc);
 #pragma unroll
             for (int r = 0; r < DD_R; ++r)
 #pragma unroll
