@@ -55,10 +55,13 @@ int ldh_of(const moe_config* c) {
     return c->n_shared ? (c->d_ff > c->d_ff_shared ? c->d_ff : c->d_ff_shared) : c->d_ff;
 }
 
-// Rows per grouped-GEMM tile: 128 once experts average 96 rows or more
-// (fewer re-reads of each weight tile, more MFMA work per LDS byte), else 64.
+// Rows per grouped-GEMM tile: 256 (the LDS-copy kernels of
+// grouped_gemm_dma.hip) once experts average 256 rows or more, 128 from 96
+// rows (fewer re-reads of each weight tile, more MFMA work per LDS byte), else
+// 64.
 int gemm_bm(const moe_config* c) {
     const long n = (long)c->n_tokens * c->top_k;
+    if (n >= 256L * c->n_expert) return 256;
     return n >= 96L * c->n_expert ? 128 : 64;
 }
 

@@ -27,6 +27,7 @@
 // wavefront's registers for the SiLU*mul epilogue.
 #include "common.h"
 #include "kernels.h"
+#include "gemm_dev.h"
 
 namespace moe {
 
@@ -38,56 +39,6 @@ __device__ __forceinline__ int lds_off(int row, int ch) { return row * ROWB + ((
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int row, int ch) {
     return *reinterpret_cast<const bf16x8_t*>(base + lds_off(row, ch));
-}
-
-// Rows of one tile: which source row to read and where the result goes.
-struct TileRows {
-    int g;        // group: expert, or E for the shared expert
-    int rbeg;     // first row in permutation (h) order
-    int nrows;    // valid rows (<= BM)
-};
-
-template <int BM>
-__device__ __forceinline__ bool tile_rows(const FfnArgs& a, int tile, TileRows& tr) {
-    if (tile >= a.meta[1]) return false;
-    const int2 t = a.tiles[tile];
-    tr.g = t.x;
-    if (t.x == a.E) {  // shared expert: rows are tokens
-        tr.rbeg = a.T * a.k + t.y;
-        tr.nrows = min(BM, a.T - t.y);
-    } else {
-        tr.rbeg = a.offsets[t.x] + t.y;
-        tr.nrows = min(BM, a.offsets[t.x + 1] - tr.rbeg);
-    }
-    return true;
-}
-// 16 bytes as a vector value (kept in registers; a struct copy of uint4 can
-// end up in scratch memory when staged across a loop).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ void st16(uint8_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-
-// The dispatcher deals consecutive workgroups to the 8 XCDs in turn, and each
-// XCD has its own L2.  Remap the linear workgroup index so that every XCD
-// receives one contiguous range of the logical work order.  That order walks
-// groups of NG N tiles; inside a group, M tile by M tile, all N tiles of the
-// group.  The workgroups an XCD runs side by side then cover a block of M
-// tiles x NG N tiles: each weight tile is read by the M tiles of its expert
-// and each A tile (rows of x or h) by the group's N tiles, mostly from that
-// XCD's L2.  NG = 4 pays off for 128-row tiles (experts with many rows); with
-// 64-row tiles (few rows per expert, bandwidth-bound) NG = 1 streams best.
-constexpr int N_XCD = 8;
-
-template <int NG>
-__device__ __forceinline__ void work_item(int& tile, int& ntile) {
-    const int gx = gridDim.x, gy = gridDim.y;
-    const int L = blockIdx.x + blockIdx.y * gx, N = gx * gy;
-    const int q = N / N_XCD, r = N % N_XCD, xcd = L % N_XCD, loc = L / N_XCD;
-    const int logical = xcd < r ? xcd * (q + 1) + loc : r * (q + 1) + (xcd - r) * q + loc;
-    const int group = logical / (gx * NG), rem = logical % (gx * NG);
-    const int gsize = min(NG, gy - group * NG);
-    tile = rem / gsize;
-    ntile = group * NG + rem % gsize;
 }
 
 // ---------------------------------------------------------------------------
@@ -104,7 +55,7 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + 2 * GU_BN) * ROWB];
     __shared__ int src_row[BM];
     int tile, ntile;
-    work_item<BM == 128 ? 4 : 1>(tile, ntile);
+    if (!work_item<BM == 128 ? 4 : 1>(a.meta[1], tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
@@ -259,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
     int tile, ntile;
-    work_item<BM == 128 ? 4 : 1>(tile, ntile);
+    if (!work_item<BM == 128 ? 4 : 1>(a.meta[1], tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
@@ -383,6 +334,7 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
 }
 
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
+    if (a.bm == 256) return launch_gateup_dma(a, st, kt);
     const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
     dim3 grid(a.max_tiles, (fmax + GU_BN - 1) / GU_BN);
     if (a.bm == 128) launch_kernel(gateup_mfma_kernel<128>, grid, 256, st, kt, a);
@@ -391,6 +343,7 @@ hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt)
 }
 
 hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
+    if (a.bm == 256) return launch_down_dma(a, st, kt);
     dim3 grid(a.max_tiles, (a.d + DN_BN - 1) / DN_BN);
     if (a.bm == 128) launch_kernel(down_mfma_kernel<128>, grid, 256, st, kt, a);
     else launch_kernel(down_mfma_kernel<64>, grid, 256, st, kt, a);

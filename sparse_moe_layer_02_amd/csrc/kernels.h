@@ -89,7 +89,7 @@ struct FfnArgs {
     float* shared_out;      // [T, d]
     float* y;               // [T, d] (fused combine)
     int max_tiles;          // grid bound of the grouped GEMMs (tiles of bm rows)
-    int bm;                 // rows per grouped-GEMM tile: 64 or 128
+    int bm;                 // rows per grouped-GEMM tile: 64, 128 or 256
     int shared_done;        // the shared expert's h rows were already produced (decode route kernel)
     int grid_has_shared;    // set by the launchers: the last grid slot is the shared expert
 };
@@ -100,6 +100,8 @@ hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st, const KTime&
 // grouped bf16 MFMA GEMMs (prefill)
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+hipError_t launch_gateup_dma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+hipError_t launch_down_dma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 // The decode path (T <= MOE_DECODE_MAX_TOKENS) in four launches: router;
 // selection + grouping beside the shared gate/up; routed gate/up; down +

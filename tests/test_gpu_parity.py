@@ -160,6 +160,15 @@ EDGE = {
     "bm128_odd_chunks": dict(T=300, d=192, E=4, k=2, F=320, Fs=448),
     "bm128_single_chunk": dict(T=200, d=64, E=2, k=1, F=64, Fs=64),
     "bm128_many_tiles": dict(T=700, d=256, E=6, k=3, F=128, Fs=128),
+    # 256-row tiles fed through LDS copies (experts average >= 256 rows):
+    # 32-wide K stages in groups of four with a tail (d = 320 -> 10 stages,
+    # Fs = 448 -> 14), a partial last N tile of gate/up (F = 320) and of down
+    # (d = 320), ragged last M tiles, fewer stages than the pipeline depth
+    # (d = F = 64 -> 2), exact multiples, three experts with two stage tails
+    "bm256_ragged": dict(T=700, d=320, E=2, k=2, F=320, Fs=448),
+    "bm256_short_k": dict(T=600, d=64, E=1, k=1, F=64, Fs=64),
+    "bm256_one_expert": dict(T=1000, d=256, E=1, k=1, F=256, n_shared=0),
+    "bm256_three_experts": dict(T=520, d=192, E=3, k=3, F=192, Fs=128),
 }
 
 
