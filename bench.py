@@ -145,16 +145,27 @@ def source_sha(paths):
 _CSRC = "sparse_moe_layer_02_amd/csrc/"
 DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it is built from
     ("decode", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
-    ("prefill", "bf16"): ("gateup_mfma_kernel", [_CSRC + f for f in ("grouped_gemm.hip", "common.h")]),
+    ("prefill", "bf16"): ("gateup_mfma_kernel", [_CSRC + f for f in ("grouped_gemm.hip", "gemm_dev.h", "common.h")]),
+    ("prefill", "bf16", "256"): ("gateup_dma_kernel",
+                                 [_CSRC + f for f in ("grouped_gemm_dma.hip", "gemm_dev.h", "common.h")]),
     ("prefill", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
 }
 
 
-def dominant(path_kind, w):
+def dominant(path_kind, w, rows_per_expert=None):
+    """The gate/up kernel a layer launches.  bf16 prefill layers whose experts
+    average 256 rows or more run the 256-row-tile kernels (the library's tile
+    rule: T * k >= 256 * E)."""
+    if path_kind == "prefill" and w == "bf16" and rows_per_expert is not None and rows_per_expert >= 256:
+        return DOMINANT[("prefill", "bf16", "256")]
     return DOMINANT.get((path_kind, w)) or DOMINANT[(path_kind, "any")]
 
 
-def traffic_record(path_kind, w, workload):
+def rows_per_expert(cfg):
+    return cfg["T"] * cfg["k"] / cfg["E"]
+
+
+def traffic_record(path_kind, w, workload, rpe=None):
     """HBM bytes per launch of the dominant kernel from profiles/traffic.json,
     if it was measured on the current kernel source."""
     rec_path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -162,7 +173,7 @@ def traffic_record(path_kind, w, workload):
         return None
     with open(rec_path) as f:
         recs = json.load(f)
-    kname, srcs = dominant(path_kind, w)
+    kname, srcs = dominant(path_kind, w, rpe)
     r = recs.get(workload)
     if not r or r.get("kernel") != kname or r.get("source_sha") != source_sha(srcs):
         return None
@@ -180,12 +191,12 @@ def _counter_rows(path):
     return out
 
 
-def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes, rec_path=None):
+def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes, rec_path=None, rpe=None):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) into HBM bytes per launch of the dominant kernel.  Each counter is
     scaled by the factor that makes it read right on the plain device copy of
     ``copy_bytes`` (read and written once) that the same command ran."""
-    kname, srcs = dominant(path_kind, w)
+    kname, srcs = dominant(path_kind, w, rpe)
     res = {"kernel": kname, "source_sha": source_sha(srcs), "copy_bytes": copy_bytes}
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r[2] == counter]
@@ -291,7 +302,7 @@ def main():
         cfg = _cf.get(spec["base"], T=spec["T"], **spec.get("over", {}))
         dec = args.path == "decode" or (args.path == "auto" and cfg["T"] <= DECODE_MAX_TOKENS)
         record_traffic(args.workload, "decode" if dec else "prefill", cfg["w"], args.record_traffic[0],
-                       args.record_traffic[1], (args.copy_probe_mib or 1024) * (1 << 20))
+                       args.record_traffic[1], (args.copy_probe_mib or 1024) * (1 << 20), rpe=rows_per_expert(cfg))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -422,17 +433,17 @@ def main():
     gu_us = stages_us["gate_up"]
     achieved = float(np.mean(gu_bytes)) / (gu_us * 1e-6) / 1e9
     path_kind = "decode" if decode else "prefill"
-    traffic = traffic_record(path_kind, cfg["w"], args.workload)
+    traffic = traffic_record(path_kind, cfg["w"], args.workload, rows_per_expert(cfg))
     if spec.get("bound") == "mfma":
         tfs = flops_gu / (gu_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
                     "frac": round(tfs / BF16_PEAK_TFS, 4), "traffic": traffic,
-                    "kernel": dominant(path_kind, cfg["w"])[0], "flops_per_launch": flops_gu,
+                    "kernel": dominant(path_kind, cfg["w"], rows_per_expert(cfg))[0], "flops_per_launch": flops_gu,
                     "bytes_per_launch": float(np.mean(gu_bytes)), "avg_launch_us": gu_us}
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": dominant(path_kind, cfg["w"])[0], "bytes_per_launch": float(np.mean(gu_bytes)),
+                    "kernel": dominant(path_kind, cfg["w"], rows_per_expert(cfg))[0], "bytes_per_launch": float(np.mean(gu_bytes)),
                     "avg_launch_us": gu_us}
 
     value = T * steps / (total_ms * 1e-3)

@@ -29,9 +29,10 @@
 // SIMD has no other wavefront to hide latency behind).
 //
 // LDS layout of a stage: rows of 64 bytes (32 bf16 of K), A rows first, then
-// 256 B rows.  The four 16-byte chunks of row r sit at slot c ^ ((r >> 1) & 3),
-// so the eight lanes an LDS cycle serves (eight consecutive rows, one chunk)
-// hit eight different 16-byte bank groups.
+// 256 B rows.  The four 16-byte chunks of row r sit at slot c ^ f(r),
+// f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1): the sixteen lanes that a 128-bit LDS
+// read serves per cycle (sixteen consecutive rows, one chunk) hit sixteen
+// different 16-byte bank groups (measured: no bank-conflict cycles).
 #include "common.h"
 #include "kernels.h"
 #include "gemm_dev.h"
@@ -190,10 +191,10 @@ __device__ __forceinline__ void k_loop(Gemm<GEO>& g, int nst, uint8_t* L0, uint8
 }
 
 // Copy lanes: lane l of copy q of wavefront w fills stage row
-// (q * WV + w) * 16 + l / 4, slot l & 3, which holds logical chunk
-// (l & 3) ^ ((l >> 3) & 3) (the row's (r >> 1) & 3 is (l >> 3) & 3).
+// r = (q * WV + w) * 16 + l / 4, slot l & 3, which holds logical chunk
+// (l & 3) ^ f(r); f(r) = ((l >> 3) & 3) ^ ((l >> 5) & 1) since r = l / 4 mod 16.
 __device__ __forceinline__ int copy_row(int q, int wv, int wave, int lane) { return (q * wv + wave) * 16 + (lane >> 2); }
-__device__ __forceinline__ int copy_col(int lane) { return ((lane & 3) ^ ((lane >> 3) & 3)) * 8; }
+__device__ __forceinline__ int copy_col(int lane) { return ((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1)) * 8; }
 
 // Per-lane fragment offsets: wavefront (mh, nh) reads A rows
 // mh * MI * 32 + 32 i + (lane & 31) and B rows brow[j] + (lane & 31).
@@ -201,7 +202,7 @@ template <class GEO>
 __device__ __forceinline__ void frag_offsets(Gemm<GEO>& g, int mh, const int (&brow)[GEO::NI], int lane) {
     using G = Gemm<GEO>;
     const int r = lane & 31;
-    const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3);
+    const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);  // chunk lane / 32 of row lane & 31
     const int base = r * SROW + slot0 * 16;
 #pragma unroll
     for (int i = 0; i < GEO::MI; ++i) g.fo[G::fa_idx(i)] = (mh * GEO::MI * 32 + 32 * i) * SROW + base;
