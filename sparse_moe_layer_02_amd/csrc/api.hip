@@ -73,6 +73,14 @@ int max_tiles_of(const moe_config* c, int bm) {
     return (int)t;
 }
 
+// Capacity of the decode slot table: the shared expert and at most
+// min(E, T*k) routed experts (decode token counts only).
+int n_dslots_of(const moe_config* c) {
+    if (c->n_tokens > MOE_DECODE_MAX_TOKENS) return 0;
+    const int n = c->n_tokens * c->top_k;
+    return c->n_shared + (n < c->n_expert ? n : c->n_expert);
+}
+
 Layout make_layout(const moe_config* c) {
     Layout L;
     const size_t T = (size_t)c->n_tokens, E = (size_t)c->n_expert, k = (size_t)c->top_k;
@@ -101,6 +109,7 @@ Layout make_layout(const moe_config* c) {
     L.slot_out = take(n * d * 4);
     L.shared_out = take(c->n_shared ? T * d * 4 : 0);
     L.scores = take(T * E * 4);
+    L.dslots = take((size_t)n_dslots_of(c) * sizeof(DecodeSlot));
     L.total = o;
     return L;
 }
@@ -190,6 +199,8 @@ FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, 
     f.max_tiles = max_tiles_of(c, f.bm);
     f.shared_done = 0;
     f.grid_has_shared = 0;
+    f.dslots = at<DecodeSlot>(ws, L.dslots);
+    f.n_dslots = n_dslots_of(c);
     return f;
 }
 

@@ -88,6 +88,18 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return __longlong_as_double(((uint64_t)hi << 32) | lo);
 }
 
+// Wave-wide maximum of an unsigned 32-bit value (0 is the neutral element);
+// every lane receives it.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<DPP_ROW_SHR1>(v));
+    v = max(v, dpp_u32<DPP_ROW_SHR2>(v));
+    v = max(v, dpp_u32<DPP_ROW_SHR4>(v));
+    v = max(v, dpp_u32<DPP_ROW_SHR8>(v));
+    v = max(v, dpp_u32<DPP_ROW_BCAST15, 0xA>(v));
+    v = max(v, dpp_u32<DPP_ROW_BCAST31, 0xC>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Wave-wide maximum of an unsigned 64-bit key (0 is the neutral element).
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 template <int CTRL, int ROW_MASK = 0xF>
@@ -125,7 +137,7 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // ---------------------------------------------------------------------------
 struct Layout {
     size_t logits, topk_idx, topk_w, offsets, perm_rows, inv_perm;
-    size_t blk_hist, blk_base, meta, active, tiles, h, slot_out, shared_out, scores, total;
+    size_t blk_hist, blk_base, meta, active, tiles, h, slot_out, shared_out, scores, dslots, total;
     int n_blk;       // permutation blocks of PERM_BLOCK assignments
     int max_tiles;   // capacity of the grouped-GEMM tile list
 };

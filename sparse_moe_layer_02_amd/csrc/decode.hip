@@ -45,25 +45,38 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeRouteArgs a) {
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_MAX_TOKENS; ++t) acc[t] = 0.0;
     const float* wrow = a.r.wr + (size_t)e * d;
-    for (int c = tid * 4; c < d; c += 1024) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wrow + c);
+    // Thread tid adds columns tid*4 .. tid*4+3 of every 1024-column stripe, in
+    // ascending order; the W_r loads of four stripes are issued before the
+    // first product (one memory round trip for d <= 4096).
+    for (int c0 = tid * 4; c0 < d; c0 += 4 * 1024) {
+        float4 w4[4];
 #pragma unroll
-        for (int t = 0; t < MOE_DECODE_MAX_TOKENS; ++t) {
-            if (t < T) {
-                float x0, x1, x2, x3;
-                if (AF == MOE_DT_BF16) {
-                    const uint2 xv = *reinterpret_cast<const uint2*>(
-                        static_cast<const uint16_t*>(a.r.x) + (size_t)t * d + c);
-                    x0 = bf16_lo(xv.x); x1 = bf16_hi(xv.x); x2 = bf16_lo(xv.y); x3 = bf16_hi(xv.y);
-                } else {
-                    const float4 xv = *reinterpret_cast<const float4*>(
-                        static_cast<const float*>(a.r.x) + (size_t)t * d + c);
-                    x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 + j * 1024;
+            w4[j] = c < d ? *reinterpret_cast<const float4*>(wrow + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 + j * 1024;
+            if (c >= d) break;
+#pragma unroll
+            for (int t = 0; t < MOE_DECODE_MAX_TOKENS; ++t) {
+                if (t < T) {
+                    float x0, x1, x2, x3;
+                    if (AF == MOE_DT_BF16) {
+                        const uint2 xv = *reinterpret_cast<const uint2*>(
+                            static_cast<const uint16_t*>(a.r.x) + (size_t)t * d + c);
+                        x0 = bf16_lo(xv.x); x1 = bf16_hi(xv.x); x2 = bf16_lo(xv.y); x3 = bf16_hi(xv.y);
+                    } else {
+                        const float4 xv = *reinterpret_cast<const float4*>(
+                            static_cast<const float*>(a.r.x) + (size_t)t * d + c);
+                        x0 = xv.x; x1 = xv.y; x2 = xv.z; x3 = xv.w;
+                    }
+                    acc[t] = __fma_rn((double)x0, (double)w4[j].x, acc[t]);
+                    acc[t] = __fma_rn((double)x1, (double)w4[j].y, acc[t]);
+                    acc[t] = __fma_rn((double)x2, (double)w4[j].z, acc[t]);
+                    acc[t] = __fma_rn((double)x3, (double)w4[j].w, acc[t]);
                 }
-                acc[t] = __fma_rn((double)x0, (double)w4.x, acc[t]);
-                acc[t] = __fma_rn((double)x1, (double)w4.y, acc[t]);
-                acc[t] = __fma_rn((double)x2, (double)w4.z, acc[t]);
-                acc[t] = __fma_rn((double)x3, (double)w4.w, acc[t]);
             }
         }
     }
@@ -86,8 +99,9 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeRouteArgs a) {
 // ---------------------------------------------------------------------------
 // 2. selection + grouping (workgroup 0), shared gate/up rows (the others)
 // ---------------------------------------------------------------------------
-constexpr int DS_THREADS = 1024;
+constexpr int DS_THREADS = 512;  // enough wavefronts for the top-k of MOE_DECODE_MAX_TOKENS tokens
 constexpr int DS_WAVES = DS_THREADS / WAVE;  // shared gate/up row pairs per workgroup
+constexpr int DS_MAX_N = MOE_DECODE_MAX_TOKENS * 32;  // assignments T*k at most
 
 // Exclusive prefix sum of arr[0..n) in place by one wavefront (n <= 1024);
 // returns the total.  Lane l owns the 16 consecutive entries from 16*l.
@@ -116,9 +130,76 @@ __device__ int wave_excl_scan_array(int* arr, int n) {
     return __builtin_amdgcn_readlane(inc, WAVE - 1);
 }
 
+// Grouping of n = T*k <= 64 assignments by one wavefront, in registers: lane
+// f holds assignment f = t*k + j (expert s_idx[f], weight s_w[f]).  Its row
+// in the stable order by (expert, token) is the number of assignments that
+// precede it, found by comparing against every other lane's key (n
+// v_readlane steps); the same pass counts the earlier assignments of its own
+// expert (its place in the expert's group) and the group size.  A group's
+// first assignment writes the slot header; slot numbers count the distinct
+// experts below.  Writes perm_rows, inv_perm, offsets, the active list, meta
+// and the decode slot table.
+__device__ void group_in_registers(const DecodeRouteArgs& a, const int32_t* s_idx, const float* s_w) {
+    const int lane = lane_id();
+    const int E = a.r.E, T = a.r.T, k = a.s.k, n = T * k;
+    const bool v = lane < n;
+    const int ef = v ? s_idx[lane] : 0x7FFFFFFF;
+    const float wf = v ? s_w[lane] : 0.0f;
+    const int tf = v ? lane / k : 0;
+    const int keyf = v ? ef * MOE_DECODE_MAX_TOKENS + tf : 0x7FFFFFFF;
+    int rank = 0, before = 0, same = 0;
+    for (int g = 0; g < n; ++g) {
+        const int kg = __builtin_amdgcn_readlane(keyf, g);
+        const int eg = __builtin_amdgcn_readlane(ef, g);
+        rank += kg < keyf;
+        before += (eg == ef) & (kg < keyf);
+        same += eg == ef;
+    }
+    const bool first = v && before == 0;
+    const uint64_t fb = __ballot(first);
+    const int na = __popcll(fb);
+    int slot = 0;  // distinct experts below ef
+    for (int g = 0; g < n; ++g) {
+        const int eg = __builtin_amdgcn_readlane(ef, g);
+        slot += (int)((fb >> g) & 1) & (eg < ef);
+    }
+    const int n_sh = a.f.n_shared ? 1 : 0;
+    DecodeSlot* ds = a.f.dslots;
+    if (v) {
+        a.p.perm_rows[rank] = lane;
+        a.p.inv_perm[lane] = rank;
+        DecodeSlot* D = ds + n_sh + slot;
+        D->tok[before] = tf;
+        D->w[before] = wf;
+        if (first) {
+            a.p.active[slot] = ef;
+            *reinterpret_cast<int4*>(D) = make_int4(ef, rank, same, 0);
+        }
+    }
+    for (int e = lane; e <= E; e += WAVE) {
+        int off = 0;
+        for (int g = 0; g < n; ++g) off += __builtin_amdgcn_readlane(ef, g) < e;
+        a.p.offsets[e] = off;
+    }
+    for (int j = n_sh + na + lane; j < a.f.n_dslots; j += WAVE)
+        *reinterpret_cast<int4*>(ds + j) = make_int4(-1, 0, 0, 0);
+    if (n_sh) {
+        if (lane == 0) *reinterpret_cast<int4*>(ds) = make_int4(0, n, T, 1);
+        if (lane < T) {
+            ds[0].tok[lane] = lane;
+            ds[0].w[lane] = 1.0f;
+        }
+    }
+    if (lane == 0) {
+        a.p.meta[0] = na;
+        a.p.meta[1] = 0;
+        a.p.meta[2] = n;
+    }
+}
+
 template <int KPL, int EFIX, int WF, int AF, int MT>
 __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteArgs a) {
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_index();
+    const int lane = lane_id(), wave = wave_index();
     if (blockIdx.x > 0) {
         const int row0 = ((int)blockIdx.x - 1) * DS_WAVES + wave;
         if (row0 < a.f.Fs)
@@ -126,18 +207,31 @@ __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteAr
                                                         nullptr);
         return;
     }
-    __shared__ int32_t s_idx[MOE_DECODE_MAX_TOKENS * 32];
-    __shared__ int cnt[1024];
+    __shared__ int32_t s_idx[DS_MAX_N];   // expert of assignment f = t*k + j
+    __shared__ float s_w[DS_MAX_N];       // its routing weight
+    __shared__ int32_t s_perm[DS_MAX_N];  // assignment of h row r
+    __shared__ int32_t s_act[DS_MAX_N];   // active experts, ascending
+    __shared__ int cnt[1024];             // counts, then scatter cursors (end offsets)
+    __shared__ int s_off[1024];           // first h row of each expert
+    __shared__ int s_slot[1024];          // routed slot of each active expert
     const int E = a.r.E, T = a.r.T, k = a.s.k, n = T * k;
     if (wave < T) {
+        float wl;
         const int my = topk_token<KPL, EFIX, true>(a.scores + (size_t)wave * E, a.s.bias, E, k, a.s.score,
                                                    a.s.route_scale, a.s.topk_idx + (size_t)wave * k,
-                                                   a.s.topk_w + (size_t)wave * k);
-        if (lane < k) s_idx[wave * k + lane] = my;
+                                                   a.s.topk_w + (size_t)wave * k, &wl);
+        if (lane < k) {
+            s_idx[wave * k + lane] = my;
+            s_w[wave * k + lane] = wl;
+        }
     }
     __syncthreads();
     if (wave != 0) return;
-    // one wavefront: counts, active list, offsets, stable scatter
+    if (n <= WAVE) {
+        group_in_registers(a, s_idx, s_w);
+        return;
+    }
+    // one wavefront: counts, active list, offsets, stable scatter, slot table
     for (int e = lane; e < E; e += WAVE) cnt[e] = 0;
     for (int f = lane; f < n; f += WAVE) atomicAdd(&cnt[s_idx[f]], 1);
     int na = 0;
@@ -145,11 +239,19 @@ __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteAr
         const int e = base + lane;
         const bool act = e < E && cnt[e] > 0;
         const uint64_t b = __ballot(act);
-        if (act) a.p.active[na + __popcll(b & lanemask_lt())] = e;
+        if (act) {
+            const int pos = na + __popcll(b & lanemask_lt());
+            a.p.active[pos] = e;
+            s_act[pos] = e;
+            s_slot[e] = pos;
+        }
         na += __popcll(b);
     }
     const int total = wave_excl_scan_array(cnt, E);
-    for (int e = lane; e < E; e += WAVE) a.p.offsets[e] = cnt[e];
+    for (int e = lane; e < E; e += WAVE) {
+        a.p.offsets[e] = cnt[e];
+        s_off[e] = cnt[e];
+    }
     if (lane == 0) {
         a.p.offsets[E] = total;
         a.p.meta[0] = na;
@@ -158,7 +260,32 @@ __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteAr
     }
     PermArgs p = a.p;
     p.topk_idx = s_idx;
+    p.perm_rows = s_perm;
     scatter_range(p, 0, n, cnt);
+    const int n_sh = a.f.n_shared ? 1 : 0;
+    DecodeSlot* ds = a.f.dslots;
+    for (int r = lane; r < n; r += WAVE) {
+        const int f = s_perm[r];
+        const int e = s_idx[f];
+        DecodeSlot* D = ds + n_sh + s_slot[e];
+        const int i = r - s_off[e];
+        a.p.perm_rows[r] = f;
+        D->tok[i] = f / k;
+        D->w[i] = s_w[f];
+    }
+    for (int j = lane; j < a.f.n_dslots; j += WAVE) {
+        int4 hd = make_int4(-1, 0, 0, 0);
+        if (j < n_sh) hd = make_int4(0, n, T, 1);
+        else if (j - n_sh < na) {
+            const int e = s_act[j - n_sh];
+            hd = make_int4(e, s_off[e], cnt[e] - s_off[e], 0);
+        }
+        *reinterpret_cast<int4*>(ds + j) = hd;
+    }
+    if (n_sh && lane < T) {
+        ds[0].tok[lane] = lane;
+        ds[0].w[lane] = 1.0f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -237,6 +364,186 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 4'. down projection + combine, one row of y per wavefront
+//
+// A wavefront owns one row of y and walks every slot of the decode slot table
+// in order (slot 0 the shared expert, then the active experts ascending),
+// adding weight * (W_down[e] row) . h into the lane of each token; y is
+// written once, in the same slot order as decode_down_kernel, so the two
+// give the same bits.
+//
+// Latency: the slot headers come in with one lane-parallel load (lane s holds
+// slot s) and are broadcast with v_readlane; the h rows of all slots are
+// copied into LDS through the global->LDS path (no VGPRs); then the weight
+// row pieces of a whole batch of slots are loaded at once, unconditionally
+// (slots past the last valid one repeat it), so the compiler's wait counts
+// are exact and each slot is reduced as soon as its own pieces have landed.
+// Used when F = F_s is 1-4 chunks of 64 lanes x 16 bytes, the table has at
+// most 64 slots and h fits the staging buffer; decode_down_kernel otherwise.
+// ---------------------------------------------------------------------------
+constexpr int DR_WAVES = 16;  // rows of y per workgroup
+constexpr int DR_THREADS = DR_WAVES * WAVE;
+constexpr int DR_H_BYTES = 64 * 1024;  // LDS staging buffer for h
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst
+// wave-uniform).
+__device__ __forceinline__ void copy16_lds(const uint8_t* src, uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(dst), 16, 0, 0);
+}
+
+// s_waitcnt for at most N vector-memory operations outstanding (vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt at their maxima do not wait).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Slot headers held across the wavefront: lane s has slot s.
+struct SlotLanes {
+    int e, r0, m, shared, tok0, tok1;
+    float w0, w1;
+    __device__ __forceinline__ int get(int v, int s) const { return __builtin_amdgcn_readlane(v, s); }
+};
+
+template <int WF, int NC>
+struct DownBatch {
+    static constexpr int NS = (WF == MOE_DT_Q8B32 ? 14 : 24) / NC;  // slots per batch
+    uint4 w[NS][NC];
+    uint16_t sc[NS][NC];
+    static constexpr int LOADS = NS * NC * (WF == MOE_DT_Q8B32 ? 2 : 1);  // vector-memory ops per batch
+};
+
+template <int WF, int NC>
+__device__ __forceinline__ void down_load_batch(DownBatch<WF, NC>& B, const FfnArgs& a, const SlotLanes& H,
+                                                int s0, int n_valid, int row) {
+    constexpr int EPL = WTraits<WF>::EPL, ESZ = WTraits<WF>::ESZ, NS = DownBatch<WF, NC>::NS;
+    const int lane = lane_id();
+#pragma unroll
+    for (int g = 0; g < NS; ++g) {
+        const int s = min(s0 + g, n_valid - 1);
+        const int e = H.get(H.e, s);
+        const bool sh = H.get(H.shared, s) != 0;
+        const uint8_t* q;
+        const uint16_t* sp;
+        row_ptrs<WF>(sh ? a.s_down : a.down, e, a.d, sh ? a.Fs : a.F, row, q, sp);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = (c * WAVE + lane) * EPL;
+            B.w[g][c] = *reinterpret_cast<const uint4*>(q + (size_t)col * ESZ);
+            if constexpr (WF == MOE_DT_Q8B32) B.sc[g][c] = sp[col >> 5];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // issue order = slot order (reductions wait in that order)
+    }
+}
+
+template <int WF, int AF, int NC>
+__device__ __forceinline__ void down_reduce_batch(const DownBatch<WF, NC>& B, const FfnArgs& a,
+                                                  const SlotLanes& H, int s0, int n_valid, const uint8_t* hs,
+                                                  float& my) {
+    constexpr int EPL = WTraits<WF>::EPL, NS = DownBatch<WF, NC>::NS;
+    const int lane = lane_id();
+    const size_t hrow_bytes = (size_t)a.ldh * (AF == MOE_DT_BF16 ? 2 : 4);
+#pragma unroll
+    for (int g = 0; g < NS; ++g) {
+        const int s = s0 + g;
+        if (s >= n_valid) break;
+        float sc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sc[c] = WF == MOE_DT_Q8B32 ? f16_to_f32(B.sc[g][c]) : 1.0f;
+        const int m = H.get(H.m, s), r0 = H.get(H.r0, s);
+        for (int i = 0; i < m; ++i) {
+            const uint8_t* hrow = hs + (size_t)(r0 + i) * hrow_bytes;
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                XChunk<AF, EPL> xc;
+                xc.load(hrow, (c * WAVE + lane) * EPL);
+                if constexpr (WF == MOE_DT_Q8B32)
+                    acc = fmaf(Dot<WF, AF>::run_u(B.w[g][c], xc, Dot<WF, AF>::corr(xc)), sc[c], acc);
+                else acc = Dot<WF, AF>::run(B.w[g][c], xc, acc);
+            }
+            const float v = wave_sum(acc);
+            const int t = i == 0 ? H.get(H.tok0, s) : i == 1 ? H.get(H.tok1, s) : a.dslots[s].tok[i];
+            const float w = i == 0   ? __int_as_float(H.get(__float_as_int(H.w0), s))
+                            : i == 1 ? __int_as_float(H.get(__float_as_int(H.w1), s))
+                                     : a.dslots[s].w[i];
+            if (lane == t) my += w * v;
+        }
+    }
+}
+
+template <int WF, int AF, int NC>
+__global__ __launch_bounds__(DR_THREADS) void decode_down_rows_kernel(FfnArgs a) {
+    using Batch = DownBatch<WF, NC>;
+    __shared__ uint4 s_h[DR_H_BYTES / 16];
+    const int lane = lane_id(), wave = wave_index();
+    const int row = blockIdx.x * DR_WAVES + wave;  // the grid covers d exactly
+    // h rows [0, T*k + T) -> LDS, 1 KB per wavefront copy, together with the
+    // slot headers; the workgroup barrier comes before any weight load:
+    // the CU accepts only so many outstanding loads, so a barrier behind the
+    // weight batch would release only once most weights had arrived, and the
+    // reductions would then run after the stream instead of beside it
+    const int hsz = AF == MOE_DT_BF16 ? 2 : 4;
+    const int n16 = (int)((size_t)(a.T * a.k + (a.n_shared ? a.T : 0)) * a.ldh * hsz / 16);
+    const uint4* hsrc = static_cast<const uint4*>(a.h);
+    static_assert(DR_H_BYTES == 4 * 16 * DR_THREADS, "four staged pieces per thread");
+    const int tq = threadIdx.x;
+    const uint4 h0 = hsrc[min(tq, n16 - 1)], h1 = hsrc[min(tq + DR_THREADS, n16 - 1)];
+    const uint4 h2 = hsrc[min(tq + 2 * DR_THREADS, n16 - 1)], h3 = hsrc[min(tq + 3 * DR_THREADS, n16 - 1)];
+    __builtin_amdgcn_sched_barrier(0);  // all staging loads in flight together
+    SlotLanes H{-1, 0, 0, 0, 0, 0, 0.0f, 0.0f};
+    if (lane < a.n_dslots) {
+        const DecodeSlot* D = a.dslots + lane;
+        const int4 hd = *reinterpret_cast<const int4*>(D);
+        const int2 tk = *reinterpret_cast<const int2*>(D->tok);
+        const float2 wv = *reinterpret_cast<const float2*>(D->w);
+        H.e = hd.x; H.r0 = hd.y; H.m = hd.z; H.shared = hd.w;
+        H.tok0 = tk.x; H.tok1 = tk.y;
+        H.w0 = wv.x; H.w1 = wv.y;
+    }
+    // valid slots form a prefix of the table (slot 0 is always valid)
+    const int n_valid = __popcll(__ballot(lane < a.n_dslots && H.e >= 0));
+    s_h[tq] = h0;  // (entries past n16 hold unread copies)
+    s_h[tq + DR_THREADS] = h1;
+    s_h[tq + 2 * DR_THREADS] = h2;
+    s_h[tq + 3 * DR_THREADS] = h3;
+    __syncthreads();
+    uint8_t* hdst = reinterpret_cast<uint8_t*>(s_h);
+    Batch B;
+    down_load_batch(B, a, H, 0, n_valid, row);
+    float my = 0.0f;  // lane t: y[t, row]
+    down_reduce_batch<WF, AF, NC>(B, a, H, 0, n_valid, hdst, my);
+    for (int s0 = Batch::NS; s0 < n_valid; s0 += Batch::NS) {
+        down_load_batch(B, a, H, s0, n_valid, row);
+        down_reduce_batch<WF, AF, NC>(B, a, H, s0, n_valid, hdst, my);
+    }
+    if (lane < a.T) a.y[(size_t)lane * a.d + row] = my;
+}
+
+// Chunks of 64 lanes x 16 bytes in a down row when decode_down_rows_kernel
+// applies, else 0.
+static int down_rows_nc(const FfnArgs& f) {
+    const int epl = f.wdt == MOE_DT_Q8B32 ? 16 : f.wdt == MOE_DT_BF16 ? 8 : 4;
+    if (f.F % (WAVE * epl) || (f.n_shared && f.Fs != f.F) || f.d % DR_WAVES || f.n_dslots > WAVE) return 0;
+    const int nc = f.F / (WAVE * epl);
+    if (nc < 1 || nc > (f.wdt == MOE_DT_Q8B32 ? 2 : f.wdt == MOE_DT_F32 ? 3 : 4)) return 0;  // (more would spill)
+    const size_t hb = (size_t)(f.T * f.k + (f.n_shared ? f.T : 0)) * f.ldh * (f.act == MOE_DT_BF16 ? 2 : 4);
+    return hb <= (size_t)DR_H_BYTES ? nc : 0;
+}
+
+template <int WF, int AF>
+static void down_rows_launch(const FfnArgs& a, int nc, hipStream_t st, const KTime& kt) {
+    const dim3 grid(a.d / DR_WAVES);
+    if (nc == 1) launch_kernel(decode_down_rows_kernel<WF, AF, 1>, grid, DR_THREADS, st, kt, a);
+    else if (nc == 2) launch_kernel(decode_down_rows_kernel<WF, AF, 2>, grid, DR_THREADS, st, kt, a);
+    else if (nc == 3) launch_kernel(decode_down_rows_kernel<WF, AF, 3>, grid, DR_THREADS, st, kt, a);
+    else launch_kernel(decode_down_rows_kernel<WF, AF, 4>, grid, DR_THREADS, st, kt, a);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static int mt_for(int T, int wdt) {
@@ -290,9 +597,15 @@ hipError_t launch_decode(const DecodeRouteArgs& a, const KTime* kt, hipStream_t 
     // 3. routed gate/up
     FfnArgs f = a.f;
     f.shared_done = 1;
-    if (e == hipSuccess) e = launch_gateup_gemv(f, st, kt[3]);
+    if (e == hipSuccess) e = launch_gateup_gemv_decode(f, st, kt[3]);
     // 4. down + combine
-    if (e == hipSuccess) {
+    const int nc = down_rows_nc(f);
+    if (e == hipSuccess && nc) {
+        if (f.wdt == MOE_DT_F32) down_rows_launch<MOE_DT_F32, MOE_DT_F32>(f, nc, st, kt[4]);
+        else if (f.wdt == MOE_DT_BF16) down_rows_launch<MOE_DT_BF16, MOE_DT_BF16>(f, nc, st, kt[4]);
+        else down_rows_launch<MOE_DT_Q8B32, MOE_DT_BF16>(f, nc, st, kt[4]);
+        e = hipGetLastError();
+    } else if (e == hipSuccess) {
         dim3 grid((f.d + DD_R - 1) / DD_R);
         if (f.wdt == MOE_DT_F32) down_launch<MOE_DT_F32, MOE_DT_F32>(f, mt, grid, st, kt[4]);
         else if (f.wdt == MOE_DT_BF16) down_launch<MOE_DT_BF16, MOE_DT_BF16>(f, mt, grid, st, kt[4]);

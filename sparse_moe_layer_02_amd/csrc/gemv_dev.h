@@ -63,18 +63,36 @@ template <> struct Dot<MOE_DT_BF16, MOE_DT_BF16> {
         return acc;
     }
 };
+// int8 blocks: u = q ^ 0x80 = q + 128 lies in [1, 255], so v_cvt_f32_ubyteN
+// turns it into an fp32 value whose low 16 bits are zero, i.e. an exact bf16;
+// pairs of them go through v_dot2_f32_bf16 against the packed activations
+// (about 2.25 VALU instructions per weight instead of sign-extract, convert
+// and FMA), and sum(q*x) = sum(u*x) - 128*sum(x), the last term computed
+// once per activation chunk (corr) and shared by every row that uses it.
 template <> struct Dot<MOE_DT_Q8B32, MOE_DT_BF16> {
-    __device__ __forceinline__ static float run(uint4 w, const XChunk<MOE_DT_BF16, 16>& x, float acc) {
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    __device__ __forceinline__ static float corr(const XChunk<MOE_DT_BF16, 16>& x) {
+        const bf16x2_t one = as_bf16x2(0x3F803F80u);  // (1.0, 1.0)
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(x.v[j]), one, s, false);
+        return 128.0f * s;
+    }
+    // upper halves of two fp32 values -> one bf16 pair (lo in bits 15:0); one v_perm_b32
+    __device__ __forceinline__ static uint32_t pack_hi(float lo, float hi) {
+        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    }
+    // sum over the chunk of q * x (before the block scale); c128 = corr(x)
+    __device__ __forceinline__ static float run_u(uint4 w, const XChunk<MOE_DT_BF16, 16>& x, float c128) {
+        const uint32_t ww[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u, w.w ^ 0x80808080u};
+        float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int32_t q = (int32_t)ww[j];
-            acc = fmaf((float)((q << 24) >> 24), bf16_lo(x.v[2 * j]), acc);
-            acc = fmaf((float)((q << 16) >> 24), bf16_hi(x.v[2 * j]), acc);
-            acc = fmaf((float)((q << 8) >> 24), bf16_lo(x.v[2 * j + 1]), acc);
-            acc = fmaf((float)(q >> 24), bf16_hi(x.v[2 * j + 1]), acc);
+            const float f0 = (float)(ww[j] & 0xFFu), f1 = (float)((ww[j] >> 8) & 0xFFu);
+            const float f2 = (float)((ww[j] >> 16) & 0xFFu), f3 = (float)(ww[j] >> 24);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pack_hi(f0, f1)), as_bf16x2(x.v[2 * j]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pack_hi(f2, f3)), as_bf16x2(x.v[2 * j + 1]), acc, false);
         }
-        return acc;
+        return acc - c128;
     }
 };
 
@@ -105,12 +123,13 @@ __device__ __forceinline__ void wave_dot(const uint8_t* const (&wq)[NR], const u
             if (i < nt) {
                 XChunk<AF, EPL> xc;
                 xc.load(xr[i], c);
+                if constexpr (WF == MOE_DT_Q8B32) {
+                    const float c128 = Dot<WF, AF>::corr(xc);
 #pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    if constexpr (WF == MOE_DT_Q8B32)
-                        acc[r][i] = fmaf(Dot<WF, AF>::run(w[r], xc, 0.0f), sc[r], acc[r][i]);
-                    else
-                        acc[r][i] = Dot<WF, AF>::run(w[r], xc, acc[r][i]);
+                    for (int r = 0; r < NR; ++r) acc[r][i] = fmaf(Dot<WF, AF>::run_u(w[r], xc, c128), sc[r], acc[r][i]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) acc[r][i] = Dot<WF, AF>::run(w[r], xc, acc[r][i]);
                 }
             }
         }
@@ -136,11 +155,11 @@ __device__ __forceinline__ void store_h(void* h, size_t idx, float v) {
 
 // Rows [row0, row0+RG) of gate and up for the m tokens of one expert group:
 // h rows r0 .. r0+m-1, where row r0+q serves token fr[q] / k (routed rows in
-// permutation order), or token q when fr is null (the shared expert, whose h
-// rows follow the routed ones).  h = silu(g) * u, rounded to the activation
-// format.  One wavefront; rows past F are computed on the last row and not
-// stored.
-template <int WF, int AF, int RG, int MT, int UNR>
+// permutation order), token fr[q] itself when TOKS (a decode slot's token
+// list), or token q when fr is null (the shared expert, whose h rows follow
+// the routed ones).  h = silu(g) * u, rounded to the activation format.  One
+// wavefront; rows past F are computed on the last row and not stored.
+template <int WF, int AF, int RG, int MT, int UNR, bool TOKS = false>
 __device__ __forceinline__ void gateup_wave(const FfnArgs& a, bool shared, int e, int F, int r0, int m,
                                             int row0, const int32_t* fr) {
     const int lane = lane_id();
@@ -163,7 +182,8 @@ __device__ __forceinline__ void gateup_wave(const FfnArgs& a, bool shared, int e
         for (int i = 0; i < MT; ++i) {
             const int ii = min(i, nt - 1);
             int t = tg + ii;
-            if (fr) {
+            if constexpr (TOKS) t = fr[tg + ii];
+            else if (fr) {
                 const int f = fr[tg + ii];
                 t = (f >= 0 && f < a.T * a.k) ? f / a.k : 0;  // a caller's bad row reads token 0
             }

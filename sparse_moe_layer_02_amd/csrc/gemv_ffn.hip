@@ -50,6 +50,20 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// gate/up of the decode path: grid (row tiles, routed slot); a workgroup
+// reads its slot's expert, h rows and tokens from the decode slot table in
+// one load, so the weight stream starts one memory round trip after launch.
+// ---------------------------------------------------------------------------
+template <int WF, int AF, int RG, int MT>
+__global__ __launch_bounds__(256) void gateup_gemv_decode_kernel(FfnArgs a) {
+    const DecodeSlot* D = a.dslots + (a.n_shared ? 1 : 0) + blockIdx.y;
+    const int4 hd = *reinterpret_cast<const int4*>(D);  // e, r0, m: one load, before any branch
+    const int row0 = (blockIdx.x * 4 + wave_index()) * RG;
+    if (hd.x < 0 || row0 >= a.F) return;
+    gateup_wave<WF, AF, RG, MT, 4, true>(a, false, hd.x, a.F, hd.y, hd.z, row0, D->tok);
+}
+
+// ---------------------------------------------------------------------------
 // down into slots: grid (row tiles, slot); writes slot_out[f] = w_f * down
 // rows and shared_out[t] (weight 1).
 // ---------------------------------------------------------------------------
@@ -121,6 +135,14 @@ hipError_t launch_gateup_gemv(const FfnArgs& a0, hipStream_t st, const KTime& kt
     dim3 grid((fmax + 4 * RG_ROWS - 1) / (4 * RG_ROWS), slots);
     const int mt = pick_mt(a.T);
     MOE_DISPATCH_FMT(gateup_gemv_kernel, RG_ROWS, mt, grid, a, st, kt);
+    return hipGetLastError();
+}
+
+hipError_t launch_gateup_gemv_decode(const FfnArgs& a, hipStream_t st, const KTime& kt) {
+    const int slots = a.E < a.T * a.k ? a.E : a.T * a.k;
+    dim3 grid((a.F + 4 * RG_ROWS - 1) / (4 * RG_ROWS), slots);
+    const int mt = pick_mt(a.T);
+    MOE_DISPATCH_FMT(gateup_gemv_decode_kernel, RG_ROWS, mt, grid, a, st, kt);
     return hipGetLastError();
 }
 

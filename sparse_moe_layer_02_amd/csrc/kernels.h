@@ -66,6 +66,20 @@ hipError_t launch_permute(const PermArgs& a, hipStream_t st, const KTime& kt = K
 // active / tile lists from existing offsets (offsets and perm_rows untouched)
 hipError_t launch_lists_from_offsets(const PermArgs& a, hipStream_t st, const KTime& kt = KTime());
 
+// One expert slot of the decode path, written by the selection kernel and read
+// by the decode expert kernels in a single dependent load.  Slot 0 is the
+// shared expert when there is one (e = 0, shared = 1, tokens 0..T-1, weight
+// 1); the routed slots follow in ascending expert index.  Slots past the last
+// active expert carry e = -1.
+struct DecodeSlot {
+    int32_t e;       // expert index, -1 for an unused slot
+    int32_t r0;      // first row of the slot in h
+    int32_t m;       // tokens routed to the slot (h rows r0 .. r0+m-1)
+    int32_t shared;  // 1 for the shared expert
+    int32_t tok[MOE_DECODE_MAX_TOKENS];  // token of h row r0+i
+    float w[MOE_DECODE_MAX_TOKENS];      // routing weight of that row (1 for the shared expert)
+};
+
 // One set of expert weights for the FFN kernels.
 struct MatRef {
     const void* q;
@@ -91,10 +105,14 @@ struct FfnArgs {
     int max_tiles;          // grid bound of the grouped GEMMs (tiles of bm rows)
     int bm;                 // rows per grouped-GEMM tile: 64, 128 or 256
     int shared_done;        // the shared expert's h rows were already produced (decode route kernel)
+    DecodeSlot* dslots;     // decode slot table (decode path only)
+    int n_dslots;           // its capacity: n_shared + min(E, T*k)
     int grid_has_shared;    // set by the launchers: the last grid slot is the shared expert
 };
 // gate/up GEMV over the active experts (and the shared one) -> h
 hipError_t launch_gateup_gemv(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+// gate/up GEMV of the decode path over the routed slots of the decode slot table
+hipError_t launch_gateup_gemv_decode(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 // down GEMV writing weighted slot rows and the shared rows
 hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 // grouped bf16 MFMA GEMMs (prefill)

@@ -34,13 +34,22 @@ __device__ __forceinline__ uint64_t pack_key(float key, int e) {
 }
 
 // Selection for one token by one wavefront: lane l holds experts l, l+64, ...
-// (KPL of them); writes topk_idx[0..k) and topk_w[0..k).  Returns with the
-// selected experts' indices in `my_idx` of lanes 0..k-1.
+// (KPL of them); writes topk_idx[0..k) and topk_w[0..k).  Returns the
+// expert of rank `lane` in lanes 0..k-1, and its weight in `w_lane`.
 // FROM_SCORES: `lrow` already holds the fp32 scores instead of the logits.
+//
+// Each lane first sorts its KPL packed keys in descending order, so its
+// candidate for the next rank is always its first key.  A round then takes
+// the wave maximum of the candidates' upper halves (the orderable score; a
+// 32-bit DPP maximum) and, only when several lanes hold that score, a second
+// maximum of their lower halves (the inverted index: the lowest expert wins).
+// The winning lane drops its first key.  Padding keys are 0 and real keys are
+// never 0, so k <= E rounds never select padding.
 template <int KPL, int EFIX, bool FROM_SCORES = false>
 __device__ __forceinline__ int topk_token(const float* __restrict__ lrow, const float* __restrict__ bias,
                                           int E_rt, int k, int score_kind, float route_scale,
-                                          int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+                                          int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                          float* w_lane = nullptr) {
     const int E = EFIX ? EFIX : E_rt;
     const int lane = lane_id();
     uint64_t key[KPL];
@@ -58,35 +67,57 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ lrow, const 
             key[j] = 0ull;
         }
     }
+    // insertion sort, descending
+#pragma unroll
+    for (int i = 1; i < KPL; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = key[j] > key[j - 1];
+            const uint64_t ka = key[j - 1], kb = key[j];
+            const float sa = sc[j - 1], sb = sc[j];
+            key[j - 1] = sw ? kb : ka;
+            key[j] = sw ? ka : kb;
+            sc[j - 1] = sw ? sb : sa;
+            sc[j] = sw ? sa : sb;
+        }
+    }
     int my_idx = 0;
     float my_s = 0.0f;
     double S = 0.0;
     for (int r = 0; r < k; ++r) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int j = 1; j < KPL; ++j) best = u64_max(best, key[j]);
-        best = wave_max_u64(best);
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-        const int owner = e % WAVE, slot = e / WAVE;
-        float s_owned = 0.0f;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-            if (lane == owner && j == slot) {
-                s_owned = sc[j];
-                key[j] = 0ull;
-            }
+        const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+        const uint32_t M = wave_max_u32(hi);
+        const uint64_t cand = __ballot(hi == M);
+        int win;
+        if (__popcll(cand) == 1) {
+            win = __ffsll((unsigned long long)cand) - 1;
+        } else {
+            const uint32_t L = wave_max_u32(hi == M ? lo : 0u);
+            win = __ffsll((unsigned long long)__ballot(hi == M && lo == L)) - 1;
         }
-        const float s_sel = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s_owned), owner));
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)__builtin_amdgcn_readlane(lo, win));
+        const float s_sel = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sc[0]), win));
+        if (lane == win) {
+#pragma unroll
+            for (int j = 0; j + 1 < KPL; ++j) {
+                key[j] = key[j + 1];
+                sc[j] = sc[j + 1];
+            }
+            key[KPL - 1] = 0ull;
+            sc[KPL - 1] = 0.0f;
+        }
         S += (double)s_sel;
         if (lane == r) {
             my_idx = e;
             my_s = s_sel;
         }
     }
+    const float w = S > 0.0 ? (float)(((double)my_s / S) * (double)route_scale) : 0.0f;
     if (lane < k) {
         idx_out[lane] = my_idx;
-        w_out[lane] = S > 0.0 ? (float)(((double)my_s / S) * (double)route_scale) : 0.0f;
+        w_out[lane] = w;
     }
+    if (w_lane) *w_lane = w;
     return my_idx;
 }
 
