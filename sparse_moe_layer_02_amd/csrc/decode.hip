@@ -33,12 +33,21 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// 1. router logits + scores, one workgroup per expert
+// 1. router logits + scores, one workgroup per expert; the workgroups after
+//    the first E compute the shared expert's gate/up rows (one row pair per
+//    wavefront), which do not depend on the routing
 // ---------------------------------------------------------------------------
-template <int AF>
+template <int WF, int AF, int MT>
 __global__ __launch_bounds__(256) void decode_router_kernel(DecodeRouteArgs a) {
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_index();
     const int E = a.r.E, T = a.r.T, d = a.r.d;
+    if ((int)blockIdx.x >= E) {
+        const int row0 = ((int)blockIdx.x - E) * 4 + wave;
+        if (row0 < a.f.Fs)
+            gateup_wave<WF, AF, 1, MT, MT == 1 ? 4 : 2>(a.f, true, 0, a.f.Fs, a.f.T * a.f.k, a.f.T, row0,
+                                                        nullptr);
+        return;
+    }
     __shared__ double part[4][MOE_DECODE_MAX_TOKENS];
     const int e = blockIdx.x;
     double acc[MOE_DECODE_MAX_TOKENS];
@@ -97,10 +106,12 @@ __global__ __launch_bounds__(256) void decode_router_kernel(DecodeRouteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. selection + grouping (workgroup 0), shared gate/up rows (the others)
+// 2. selection + grouping (workgroup 0), shared expert's down projection
+//    into shared_out (the others)
 // ---------------------------------------------------------------------------
 constexpr int DS_THREADS = 512;  // enough wavefronts for the top-k of MOE_DECODE_MAX_TOKENS tokens
-constexpr int DS_WAVES = DS_THREADS / WAVE;  // shared gate/up row pairs per workgroup
+constexpr int DS_WAVES = DS_THREADS / WAVE;
+constexpr int DS_ROWS = 2;  // shared down rows per wavefront
 constexpr int DS_MAX_N = MOE_DECODE_MAX_TOKENS * 32;  // assignments T*k at most
 
 // Exclusive prefix sum of arr[0..n) in place by one wavefront (n <= 1024);
@@ -201,10 +212,8 @@ template <int KPL, int EFIX, int WF, int AF, int MT>
 __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteArgs a) {
     const int lane = lane_id(), wave = wave_index();
     if (blockIdx.x > 0) {
-        const int row0 = ((int)blockIdx.x - 1) * DS_WAVES + wave;
-        if (row0 < a.f.Fs)
-            gateup_wave<WF, AF, 1, MT, MT == 1 ? 4 : 2>(a.f, true, 0, a.f.Fs, a.f.T * a.f.k, a.f.T, row0,
-                                                        nullptr);
+        const int row0 = (((int)blockIdx.x - 1) * DS_WAVES + wave) * DS_ROWS;
+        if (row0 < a.f.d) down_rows_wave<WF, AF, DS_ROWS, MT>(a.f, true, 0, a.f.Fs, a.f.T * a.f.k, a.f.T, row0);
         return;
     }
     __shared__ int32_t s_idx[DS_MAX_N];   // expert of assignment f = t*k + j
@@ -309,6 +318,11 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(FfnArgs a) {
     const int hsz = AF == MOE_DT_BF16 ? 2 : 4;
     for (int s = wave; s < n_slots; s += DD_WAVES) {
         const bool shared = s < n_sh;
+        if (shared) {  // computed by the selection launch
+            for (int q = lane; q < T * DD_R; q += WAVE)
+                if (row0 + q % DD_R < d) part[0][q / DD_R][q % DD_R] = a.shared_out[(size_t)(q / DD_R) * d + row0 + q % DD_R];
+            continue;
+        }
         const int e = shared ? 0 : a.active[s - n_sh];
         const int F = shared ? a.Fs : a.F;
         const int r0 = shared ? T * k : a.offsets[e];
@@ -504,8 +518,11 @@ __global__ __launch_bounds__(DR_THREADS) void decode_down_rows_kernel(FfnArgs a)
         H.tok0 = tk.x; H.tok1 = tk.y;
         H.w0 = wv.x; H.w1 = wv.y;
     }
-    // valid slots form a prefix of the table (slot 0 is always valid)
+    // valid slots form a prefix of the table (slot 0 is always valid); the
+    // shared expert's slot 0 comes from shared_out (selection launch)
     const int n_valid = __popcll(__ballot(lane < a.n_dslots && H.e >= 0));
+    const int first = a.n_shared ? 1 : 0;
+    float my = (first && lane < a.T) ? a.shared_out[(size_t)lane * a.d + row] : 0.0f;  // lane t: y[t, row]
     s_h[tq] = h0;  // (entries past n16 hold unread copies)
     s_h[tq + DR_THREADS] = h1;
     s_h[tq + 2 * DR_THREADS] = h2;
@@ -513,10 +530,9 @@ __global__ __launch_bounds__(DR_THREADS) void decode_down_rows_kernel(FfnArgs a)
     __syncthreads();
     uint8_t* hdst = reinterpret_cast<uint8_t*>(s_h);
     Batch B;
-    down_load_batch(B, a, H, 0, n_valid, row);
-    float my = 0.0f;  // lane t: y[t, row]
-    down_reduce_batch<WF, AF, NC>(B, a, H, 0, n_valid, hdst, my);
-    for (int s0 = Batch::NS; s0 < n_valid; s0 += Batch::NS) {
+    down_load_batch(B, a, H, first, n_valid, row);  // (k >= 1: there is a routed slot)
+    down_reduce_batch<WF, AF, NC>(B, a, H, first, n_valid, hdst, my);
+    for (int s0 = first + Batch::NS; s0 < n_valid; s0 += Batch::NS) {
         down_load_batch(B, a, H, s0, n_valid, row);
         down_reduce_batch<WF, AF, NC>(B, a, H, s0, n_valid, hdst, my);
     }
@@ -559,6 +575,14 @@ static void down_launch(const FfnArgs& a, int mt, dim3 grid, hipStream_t st, con
     else launch_kernel(decode_down_kernel<WF, AF, 8>, grid, DD_THREADS, st, kt, a);
 }
 
+template <int WF, int AF>
+static void router_launch_mt(const DecodeRouteArgs& a, int mt, dim3 grid, hipStream_t st, const KTime& kt) {
+    if (mt == 1) launch_kernel(decode_router_kernel<WF, AF, 1>, grid, 256, st, kt, a);
+    else if (mt == 2) launch_kernel(decode_router_kernel<WF, AF, 2>, grid, 256, st, kt, a);
+    else if (mt == 4) launch_kernel(decode_router_kernel<WF, AF, 4>, grid, 256, st, kt, a);
+    else launch_kernel(decode_router_kernel<WF, AF, 8>, grid, 256, st, kt, a);
+}
+
 template <int KPL, int EFIX, int WF, int AF>
 static void select_launch_mt(const DecodeRouteArgs& a, int mt, dim3 grid, hipStream_t st, const KTime& kt) {
     if (mt == 1) launch_kernel(decode_select_kernel<KPL, EFIX, WF, AF, 1>, grid, DS_THREADS, st, kt, a);
@@ -577,13 +601,15 @@ static void select_launch_fmt(const DecodeRouteArgs& a, int mt, dim3 grid, hipSt
 hipError_t launch_decode(const DecodeRouteArgs& a, const KTime* kt, hipStream_t st) {
     const int T = a.r.T, E = a.r.E;
     const int mt = mt_for(T, a.f.wdt);
-    // 1. router
-    if (a.r.act == MOE_DT_BF16) launch_kernel(decode_router_kernel<MOE_DT_BF16>, E, 256, st, kt[0], a);
-    else launch_kernel(decode_router_kernel<MOE_DT_F32>, E, 256, st, kt[0], a);
+    // 1. router, shared gate/up
+    const dim3 rgrid(E + (a.f.n_shared ? (a.f.Fs + 3) / 4 : 0));
+    if (a.f.wdt == MOE_DT_F32) router_launch_mt<MOE_DT_F32, MOE_DT_F32>(a, mt, rgrid, st, kt[0]);
+    else if (a.f.wdt == MOE_DT_BF16) router_launch_mt<MOE_DT_BF16, MOE_DT_BF16>(a, mt, rgrid, st, kt[0]);
+    else router_launch_mt<MOE_DT_Q8B32, MOE_DT_BF16>(a, mt, rgrid, st, kt[0]);
     hipError_t e = hipGetLastError();
-    // 2. selection + grouping, shared gate/up
+    // 2. selection + grouping, shared down
     if (e == hipSuccess) {
-        dim3 grid(1 + (a.f.n_shared ? (a.f.Fs + DS_WAVES - 1) / DS_WAVES : 0));
+        dim3 grid(1 + (a.f.n_shared ? (a.f.d + DS_WAVES * DS_ROWS - 1) / (DS_WAVES * DS_ROWS) : 0));
         const int kpl = (E + WAVE - 1) / WAVE;
         if (E == 256) select_launch_fmt<4, 256>(a, mt, grid, st, kt[1]);
         else if (kpl <= 1) select_launch_fmt<1, 0>(a, mt, grid, st, kt[1]);
