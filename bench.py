@@ -144,7 +144,8 @@ def source_sha(paths):
 
 _CSRC = "sparse_moe_layer_02_amd/csrc/"
 DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it is built from
-    ("decode", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
+    ("decode", "any"): ("gateup_gemv_decode_kernel",
+                        [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h", "kernels.h")]),
     ("prefill", "bf16"): ("gateup_mfma_kernel", [_CSRC + f for f in ("grouped_gemm.hip", "gemm_dev.h", "common.h")]),
     ("prefill", "bf16", "256"): ("gateup_dma_kernel",
                                  [_CSRC + f for f in ("grouped_gemm_dma.hip", "gemm_dev.h", "common.h")]),
