@@ -27,7 +27,7 @@ def _counter_csv(path, counter, rows):
             w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
 
 
-@pytest.mark.parametrize("kernel,path_kind,w", [("gateup_gemv_kernel", "decode", "q8b32"),
+@pytest.mark.parametrize("kernel,path_kind,w", [("gateup_gemv_decode_kernel", "decode", "q8b32"),
                                                  ("gateup_mfma_kernel", "prefill", "bf16")])
 def test_traffic_scaling(tmp_path, kernel, path_kind, w):
     """Each counter is scaled by the factor that makes it read the probe's
