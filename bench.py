@@ -280,6 +280,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated across steps")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="tokens per step instead of the workload's (small-batch sweeps)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"],
                     help="force the decode (GEMV) or prefill (grouped GEMM) path")
     ap.add_argument("--graph", action="store_true",
@@ -320,7 +322,7 @@ def main():
     spec = WORKLOADS[args.workload]
     steps = args.steps or spec["steps"]
     warmup = spec["warmup"] if args.warmup is None else args.warmup
-    cfg = configs.get(spec["base"], T=spec["T"], **spec.get("over", {}))
+    cfg = configs.get(spec["base"], T=args.tokens or spec["T"], **spec.get("over", {}))
     T = cfg["T"]
     decode = args.path == "decode" or (args.path == "auto" and T <= moe.DECODE_MAX_TOKENS)
     n_copies = args.copies or spec["copies"]

@@ -354,7 +354,8 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     int32_t* perm = dbg && dbg->perm_rows ? dbg->perm_rows : at<int32_t>(ws, L.perm_rows);
     int32_t* inv = dbg && dbg->inv_perm ? dbg->inv_perm : at<int32_t>(ws, L.inv_perm);
 
-    RouteArgs r{x, w->w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, logits, !decode};
+    // prefill: the token-grouped GEMV router up to 64 tokens, the tiled one beyond
+    RouteArgs r{x, w->w_router, cfg->n_tokens, cfg->d_model, cfg->n_expert, cfg->act_dtype, logits, false};
     KTime kt[MOE_STAGES];
     stage_timings(dbg, kt);
     if (decode) {

@@ -26,16 +26,22 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Decode router: one workgroup per expert, T <= MOE_DECODE_MAX_TOKENS.
-// Thread j sums columns 4*(j + 256*r) .. +3 in ascending order, then the
-// workgroup adds the 256 partials in a fixed tree order.
+// Router for few tokens: workgroup (e, g) computes expert e's logits for the
+// tokens 8g .. 8g+7.  Thread j sums columns 4*(j + 256*r) .. +3 in ascending
+// order, then the workgroup adds the 256 partials in a fixed tree order.
 // ---------------------------------------------------------------------------
+constexpr int ROUTER_GEMV_MAX_T = 64;  // more tokens: the tiled kernel below
+
 template <int AF>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict__ x,
                                                           const float* __restrict__ wr, int T, int d,
                                                           int E, float* __restrict__ logits) {
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
+    const int t0 = blockIdx.y * MOE_DECODE_MAX_TOKENS;
+    T = min(T - t0, MOE_DECODE_MAX_TOKENS);
+    x = static_cast<const uint8_t*>(x) + (size_t)t0 * d * (AF == MOE_DT_BF16 ? 2 : 4);
+    logits += (size_t)t0 * E;
     double acc[MOE_DECODE_MAX_TOKENS];
 #pragma unroll
     for (int t = 0; t < MOE_DECODE_MAX_TOKENS; ++t) acc[t] = 0.0;
@@ -241,8 +247,8 @@ static void router_gemm_launch(const RouteArgs& a, hipStream_t st, const KTime& 
 }
 
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t st, const KTime& kt) {
-    if (a.T <= MOE_DECODE_MAX_TOKENS && !a.force_gemm) {
-        dim3 grid(a.E);
+    if (a.T <= ROUTER_GEMV_MAX_T && !a.force_gemm) {
+        dim3 grid(a.E, (a.T + MOE_DECODE_MAX_TOKENS - 1) / MOE_DECODE_MAX_TOKENS);
         if (a.act == MOE_DT_BF16)
             launch_kernel(router_gemv_kernel<MOE_DT_BF16>, grid, 256, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
         else
