@@ -49,6 +49,9 @@ WORKLOADS = {
     "c3t2": dict(base="c3", T=2, copies=4, steps=200, warmup=20),
     "c4": dict(base="c4", T=512, copies=1, steps=20, warmup=5),
     "c5": dict(base="c5", T=4096, copies=1, steps=10, warmup=3),
+    # the c2 layer (int8 blocks of 32) with a 512-token prefill batch: the
+    # int8 grouped GEMMs
+    "c2p": dict(base="c2", T=512, copies=1, steps=10, warmup=3),
     # Compute-bound supplements for the matrix cores: s1 is c5's shared-expert
     # shape alone (one dense SwiGLU over 4096 tokens: one expert, top-1, no
     # shared expert); s2 is c4 with 16384 tokens (about 512 rows per expert).
@@ -149,6 +152,8 @@ DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it 
     ("prefill", "bf16"): ("gateup_mfma_kernel", [_CSRC + f for f in ("grouped_gemm.hip", "gemm_dev.h", "common.h")]),
     ("prefill", "bf16", "256"): ("gateup_dma_kernel",
                                  [_CSRC + f for f in ("grouped_gemm_dma.hip", "gemm_dev.h", "common.h")]),
+    ("prefill", "q8b32"): ("gateup_mfma_q8_kernel",
+                           [_CSRC + f for f in ("grouped_gemm_q8.hip", "gemm_dev.h", "common.h")]),
     ("prefill", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
 }
 
@@ -156,9 +161,12 @@ DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it 
 def dominant(path_kind, w, rows_per_expert=None):
     """The gate/up kernel a layer launches.  bf16 prefill layers whose experts
     average 256 rows or more run the 256-row-tile kernels (the library's tile
-    rule: T * k >= 256 * E)."""
+    rule: T * k >= 256 * E); int8 prefill layers run the int8 grouped GEMMs
+    from two rows per expert (T * k >= 2 * E), the GEMVs below."""
     if path_kind == "prefill" and w == "bf16" and rows_per_expert is not None and rows_per_expert >= 256:
         return DOMINANT[("prefill", "bf16", "256")]
+    if path_kind == "prefill" and w == "q8b32" and (rows_per_expert is None or rows_per_expert < 2):
+        return DOMINANT[("prefill", "any")]  # int8 layers with few rows per expert: the GEMVs
     return DOMINANT.get((path_kind, w)) or DOMINANT[(path_kind, "any")]
 
 

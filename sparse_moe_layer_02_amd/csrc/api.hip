@@ -58,8 +58,9 @@ int ldh_of(const moe_config* c) {
 // Rows per grouped-GEMM tile: 256 (the LDS-copy kernels of
 // grouped_gemm_dma.hip) once experts average 256 rows or more, 128 from 96
 // rows (fewer re-reads of each weight tile, more MFMA work per LDS byte), else
-// 64.
+// 64.  int8 weights always take 64-row tiles (grouped_gemm_q8.hip).
 int gemm_bm(const moe_config* c) {
+    if (c->w_dtype == MOE_DT_Q8B32) return 64;
     const long n = (long)c->n_tokens * c->top_k;
     if (n >= 256L * c->n_expert) return 256;
     return n >= 96L * c->n_expert ? 128 : 64;
@@ -204,12 +205,22 @@ FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, 
     return f;
 }
 
-// Experts of the prefill path: MFMA for bf16 weights, GEMVs otherwise.
+// int8 prefill layers go to the grouped MFMA GEMMs once experts average two
+// rows or more: below that the GEMVs over the grouped rows are faster (they
+// read each weight once per row, the GEMMs widen every weight tile to bf16).
+bool q8_mfma(const FfnArgs& f) { return f.wdt == MOE_DT_Q8B32 && (long)f.T * f.k >= 2L * f.E; }
+
+// Experts of the prefill path: MFMA for bf16 weights and for int8 weights with
+// enough rows per expert, GEMVs otherwise.
 hipError_t run_expert_kernels(const FfnArgs& f, hipStream_t st) {
     hipError_t e;
     if (f.wdt == MOE_DT_BF16) {
         if ((e = launch_gateup_mfma(f, st)) != hipSuccess) return e;
         return launch_down_mfma(f, st);
+    }
+    if (q8_mfma(f)) {
+        if ((e = launch_gateup_mfma_q8(f, st)) != hipSuccess) return e;
+        return launch_down_mfma_q8(f, st);
     }
     if ((e = launch_gateup_gemv(f, st)) != hipSuccess) return e;
     return launch_down_slots_gemv(f, st);
@@ -377,6 +388,9 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     if (f.wdt == MOE_DT_BF16) {
         e = launch_gateup_mfma(f, st, kt[3]);
         if (e == hipSuccess) e = launch_down_mfma(f, st, kt[4]);
+    } else if (q8_mfma(f)) {
+        e = launch_gateup_mfma_q8(f, st, kt[3]);
+        if (e == hipSuccess) e = launch_down_mfma_q8(f, st, kt[4]);
     } else {
         e = launch_gateup_gemv(f, st, kt[3]);
         if (e == hipSuccess) e = launch_down_slots_gemv(f, st, kt[4]);

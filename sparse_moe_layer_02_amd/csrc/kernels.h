@@ -119,6 +119,9 @@ hipError_t launch_down_slots_gemv(const FfnArgs& a, hipStream_t st, const KTime&
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 hipError_t launch_gateup_dma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+// grouped MFMA GEMMs for int8 (blocks of 32 + fp16 scale) weights, 64- or 128-row tiles
+hipError_t launch_gateup_mfma_q8(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+hipError_t launch_down_mfma_q8(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 hipError_t launch_down_dma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 // The decode path (T <= MOE_DECODE_MAX_TOKENS) in four launches: router;

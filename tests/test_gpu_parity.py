@@ -84,11 +84,13 @@ def test_decode_workloads(torch_cuda, orc, name, T):
 # Full-size prefill workloads c4 / c5
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c4", "c5"])
-def test_prefill_workloads(torch_cuda, orc, name):
-    cfg = configs.get(name)
+@pytest.mark.parametrize("name,T", [("c4", None), ("c5", None), ("c2", 512)])
+def test_prefill_workloads(torch_cuda, orc, name, T):
+    """c4 / c5, and the c2 layer (int8 weights) with a 512-token prefill batch
+    through the int8 grouped GEMMs."""
+    cfg = configs.get(name, T=T) if T else configs.get(name)
     T = cfg["T"]
-    say("case", name, "T", T, "(generating 19 GB of weights)")
+    say("case", name, "T", T, "(generating the layer's weights)")
     W = H.upload_weights_chunked(cfg)
     x_np = configs.gen_x(cfg)
     x = H.to_dev(x_np)
@@ -146,10 +148,16 @@ EDGE = {
                                bias="none"),
     "E384_T70_ragged_tiles": dict(T=70, d=576, E=384, k=8, F=192, Fs=128),
     "E16_T300_multiblock_perm": dict(T=300, d=128, E=16, k=8, F=64),
-    "q8_prefill_gemv": dict(T=37, d=256, E=16, k=4, F=128, w="q8b32", score="sqrt_softplus",
+    "q8_prefill_small": dict(T=37, d=256, E=16, k=4, F=128, w="q8b32", score="sqrt_softplus",
                             scale=1.5, bias="none"),
     "q8_decode_T8": dict(T=8, d=256, E=32, k=6, F=128, w="q8b32", score="sqrt_softplus", scale=1.5,
                          bias="none"),
+    # int8 grouped GEMMs: several 64-row tiles per expert, a partial last
+    # 128-column tile of down (d = 320), a shared expert wider than the routed
+    # ones, odd numbers of 64-wide K chunks (d = 320 -> 5, F = 192 -> 3)
+    "q8_prefill_tiles": dict(T=300, d=320, E=4, k=2, F=192, Fs=256, w="q8b32", score="sqrt_softplus",
+                             scale=1.5, bias="none"),
+    "q8_prefill_no_shared": dict(T=65, d=128, E=8, k=3, F=64, n_shared=0, w="q8b32"),
     "f32_prefill": dict(T=40, d=128, E=8, k=2, F=64, act="f32", w="f32", x_sigma=0.5, w_sigma=0.1),
     "f32_decode_T3": dict(T=3, d=512, E=32, k=4, F=256, act="f32", w="f32", x_sigma=0.5, w_sigma=0.1),
     "no_shared_prefill": dict(T=33, d=128, E=8, k=3, F=64, n_shared=0),
