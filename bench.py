@@ -209,7 +209,7 @@ def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes, rec
     res = {"kernel": kname, "source_sha": source_sha(srcs), "copy_bytes": copy_bytes}
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r[2] == counter]
-        kern = [v for _, n, _, v in rows if ("moe::" + kname + "<") in n or ("moe::" + kname + "(") in n]
+        kern = [v for _, n, _, v in rows if ("::" + kname + "<") in n or ("::" + kname + "(") in n]
         # the probe's three copies are the last copy dispatches of the run
         copy = [v for _, n, _, v in sorted(rows) if "copy" in n.lower()][-3:]
         if not kern or len(copy) < 3:
