@@ -100,24 +100,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Wave-wide maximum of an unsigned 64-bit key (0 is the neutral element).
-__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)v), hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = u64_max(v, dpp_u64<DPP_ROW_SHR1>(v));
-    v = u64_max(v, dpp_u64<DPP_ROW_SHR2>(v));
-    v = u64_max(v, dpp_u64<DPP_ROW_SHR4>(v));
-    v = u64_max(v, dpp_u64<DPP_ROW_SHR8>(v));
-    v = u64_max(v, dpp_u64<DPP_ROW_BCAST15, 0xA>(v));
-    v = u64_max(v, dpp_u64<DPP_ROW_BCAST31, 0xC>(v));
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Index of this wavefront in its workgroup, as a wave-uniform (scalar) value.

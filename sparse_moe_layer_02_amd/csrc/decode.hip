@@ -4,19 +4,19 @@
 // the fences serialise; a kernel boundary publishes results once):
 //
 //   1. decode_router_kernel: one workgroup per expert computes that expert's
-//      router logit and score for every token (fp64, rounded once).
+//      router logit and score for every token (fp64, rounded once); the
+//      workgroups after the first E compute the shared expert's gate/up rows.
 //   2. decode_select_kernel: workgroup 0 runs the top-k of every token (one
 //      wavefront each), then one wavefront builds the stable grouping and
-//      publishes indices, weights, offsets, permutation and the active-expert
-//      list; the other workgroups compute the shared expert's gate/up rows
-//      meanwhile (they do not depend on the routing).
-//   3. the routed experts' gate/up GEMV over the active list (gemv_ffn.hip).
-//   4. decode_down_kernel: a workgroup owns a tile of rows of y; its
-//      wavefronts take the expert slots (slot 0 the shared expert, then the
-//      active experts in ascending index), stream each slot's down-projection
-//      rows once and leave per-slot partial results in LDS, which are then
-//      added in slot order - y is written once, deterministically, without
-//      atomics and without a separate combine launch.
+//      publishes indices, weights, offsets, permutation, the active-expert
+//      list and the decode slot table; the other workgroups compute the
+//      shared expert's down projection into shared_out.
+//   3. the routed experts' gate/up GEMV over the slot table (gemv_ffn.hip).
+//   4. decode_down_rows_kernel: a wavefront owns one row of y, starts from
+//      shared_out and adds every routed slot's weighted down-projection row
+//      in slot order - y is written once, deterministically, without atomics
+//      and without a separate combine launch (decode_down_kernel, with
+//      per-slot partials in LDS, covers the shapes outside its limits).
 //
 // The pages: the router with a runtime n_expert and a parallel (not
 // single-thread) top-k ("256 experts, 512 lines", "The constant that always

@@ -3,10 +3,10 @@
 // wavefront top-k with renormalised weights.  Shared by the selection kernel
 // and the fused decode routing kernel.
 //
-// Packed key: (orderable fp32 key) << 32 | (0xFFFFFFFF - e), so one unsigned
-// maximum picks the larger key and, on equal keys, the lower expert index.
-// NaN keys map below every number; -0 is folded onto +0.  k rounds of a
-// wave-wide DPP maximum select the experts in rank order; the selected scores
+// Packed key: (orderable fp32 key) << 32 | (0xFFFFFFFF - e), so the unsigned
+// order is the larger key first and, on equal keys, the lower expert index.
+// NaN keys map below every number; -0 is folded onto +0.  k rounds of
+// wave-wide DPP maxima select the experts in rank order; the selected scores
 // are summed in fp64 in that order and the weights formed in fp64.
 #pragma once
 #include "common.h"
