@@ -69,6 +69,7 @@ def load(path: str | None = None):
     lib.moe_ref_expert_ffn.argtypes = [C, P, W, P, P, P, P, P]
     lib.moe_ref_combine.argtypes = [C, P, P, P]
     lib.moe_ref_layer_forward.argtypes = [C, P, W, P, ctypes.POINTER(RefDebug)]
+    lib.moe_ref_topk_rows.argtypes = [I, I, I, P, P, P]
     lib.moe_ref_dense_swiglu.argtypes = [I, I, I, I, I, P, RefMat, RefMat, RefMat, I, P]
     lib.moe_ref_bf16_from_f64.argtypes = [ctypes.c_double]
     lib.moe_ref_bf16_from_f64.restype = ctypes.c_uint16
@@ -143,6 +144,16 @@ class Oracle:
         self._check(self.lib.moe_ref_select(ctypes.byref(c), self._p(logits), self._p(bias),
                                             self._p(idx), self._p(w)))
         return idx, w
+
+    def topk_rows(self, scores, k):
+        """Per row of ``scores`` [rows, n] f32: the k chosen candidate indices in
+        ascending order [rows, k] i32, and their scores [rows, k] f32."""
+        rows, n = scores.shape
+        idx = np.empty((rows, k), np.int32)
+        vals = np.empty((rows, k), np.float32)
+        self._check(self.lib.moe_ref_topk_rows(rows, n, k, self._p(scores), self._p(idx),
+                                               self._p(vals)))
+        return idx, vals
 
     def permute(self, cfg, topk_idx):
         T = topk_idx.shape[0]

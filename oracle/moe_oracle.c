@@ -320,6 +320,61 @@ int moe_ref_route(const moe_ref_config *cfg, const void *x, const float *w_route
     return st;
 }
 
+/* Row top-k over long candidate rows (the sparse attention indexer's top-512 /
+ * top-1024 selection, "256 experts, 512 lines" blog post, section "The constant
+ * that always said 256").  Definition: under the selection order of precedes()
+ * the k chosen candidates of a row are its first k; they are listed by
+ * ascending candidate index. */
+typedef struct { float v; int32_t i; } ref_cand;
+
+static int cand_cmp(const void *pa, const void *pb) {
+    const ref_cand *a = pa, *b = pb;
+    if (precedes(a->v, a->i, b->v, b->i)) return -1;
+    if (precedes(b->v, b->i, a->v, a->i)) return 1;
+    return 0;
+}
+
+int moe_ref_topk_rows(int32_t rows, int32_t n, int32_t k, const float *scores, int32_t *idx,
+                      float *vals) {
+    if (rows < 0 || n < 1 || k < 1 || k > n) return MOE_REF_ERR_INVALID;
+    if (rows > 0 && (!scores || !idx)) return MOE_REF_ERR_INVALID;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int r = 0; r < rows; ++r) {
+        ref_cand *c = malloc(sizeof(ref_cand) * (size_t)n);
+        unsigned char *taken = calloc((size_t)n, 1);
+        if (!c || !taken) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            const float *row = scores + (size_t)r * n;
+            for (int i = 0; i < n; ++i) {
+                c[i].v = row[i];
+                c[i].i = i;
+            }
+            qsort(c, (size_t)n, sizeof(ref_cand), cand_cmp);
+            for (int j = 0; j < k; ++j) {
+#if ORACLE_MUTANT == 12 /* planted: the k-th and (k+1)-th candidates swapped */
+                const int jj = (j == k - 1 && k < n) ? k : j;
+                taken[c[jj].i] = 1;
+#else
+                taken[c[j].i] = 1;
+#endif
+            }
+            int o = 0;
+            for (int i = 0; i < n; ++i)
+                if (taken[i]) {
+                    idx[(size_t)r * k + o] = i;
+                    if (vals) vals[(size_t)r * k + o] = row[i];
+                    ++o;
+                }
+        }
+        free(c);
+        free(taken);
+    }
+    return failed ? MOE_REF_ERR_INVALID : MOE_REF_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Permutation: stable counting sort of assignments by expert.               */
 /* ------------------------------------------------------------------------ */

@@ -97,6 +97,13 @@ int moe_ref_dense_swiglu(int32_t n_tokens, int32_t d_model, int32_t d_ff, int32_
                          int32_t w_dtype, const void *x, moe_ref_mat gate, moe_ref_mat up,
                          moe_ref_mat down, int32_t expert, double *y64);
 
+/* Row top-k: for each of `rows` rows of n scores, the k candidates that come
+ * first under the selection order (larger value first, NaN after every number,
+ * -0 == +0, equal values by lower index), written to idx[rows, k] in ascending
+ * index order; vals[rows, k] (may be NULL) receives their scores.  1 <= k <= n. */
+int moe_ref_topk_rows(int32_t rows, int32_t n, int32_t k, const float *scores, int32_t *idx,
+                      float *vals);
+
 /* Format helpers, exported so the tests can pin them. */
 uint16_t moe_ref_bf16_from_f64(double v);
 float moe_ref_f16_to_f32(uint16_t h);

@@ -194,6 +194,101 @@ def pin_selection_invariants(orc):
 
 
 # ---------------------------------------------------------------------------
+# Row top-k over long candidate rows (indexer-style selection)
+# ---------------------------------------------------------------------------
+
+def _py_topk_rows(row, k):
+    """Python's own sort as the definition: NaN after every number, larger value
+    first (-0 equals +0), then lower index; the first k, listed by index."""
+    order = sorted(range(len(row)), key=lambda i: (1, 0.0, i) if math.isnan(row[i])
+                   else (0, -float(row[i]), i))
+    return sorted(order[:k])
+
+
+def pin_topk_rows_python_sort(orc):
+    """Against Python's sort on rows with heavy ties, NaN and signed zeros."""
+    rng = np.random.default_rng(21)
+    for n, k in ((1, 1), (7, 3), (64, 64), (300, 17), (1000, 512), (4099, 1024)):
+        rows = rng.standard_normal((6, n)).astype(np.float32)
+        rows[1] = np.round(rows[1] * 2) / 2                   # few distinct values
+        rows[2] = np.where(rng.random(n) < 0.3, np.nan, rows[2])
+        rows[3] = np.where(rng.random(n) < 0.5, -0.0, 0.0)    # only signed zeros
+        rows[4] = np.maximum(rows[4], 0)                      # ReLU-like: many exact zeros
+        rows[5] = np.float32(7.0)
+        rows = np.ascontiguousarray(rows, np.float32)
+        idx, vals = orc.topk_rows(rows, k)
+        for r in range(rows.shape[0]):
+            want = _py_topk_rows(rows[r].tolist(), k)
+            assert idx[r].tolist() == want, (n, k, r)
+            assert np.array_equal(vals[r].view(np.uint32), rows[r][want].view(np.uint32))
+
+
+def pin_topk_rows_bruteforce(orc):
+    """Every row over {-1, -0, +0, 1, NaN}^n for n <= 4, every k: the chosen set
+    is the unique k-subset whose members each precede every non-member."""
+    alphabet = [-1.0, -0.0, 0.0, 1.0, float("nan")]
+
+    def prec(r, a, b):
+        na, nb = math.isnan(r[a]), math.isnan(r[b])
+        if na != nb:
+            return nb
+        if not na and r[a] != r[b]:
+            return r[a] > r[b]
+        return a < b
+
+    for n in range(1, 5):
+        rows = np.array(list(itertools.product(alphabet, repeat=n)), np.float32)
+        for k in range(1, n + 1):
+            idx, _ = orc.topk_rows(rows, k)
+            for t, r in enumerate(rows.tolist()):
+                found = [sub for sub in itertools.combinations(range(n), k)
+                         if all(prec(r, a, b) for a in sub for b in range(n) if b not in sub)]
+                assert len(found) == 1
+                assert idx[t].tolist() == list(found[0]), (r, k, idx[t])
+
+
+def pin_topk_rows_special_cases(orc):
+    """Closed forms: all equal -> [0, k); rising -> [n-k, n); falling -> [0, k);
+    k == n -> everything; only m < k numbers -> those plus the first NaNs."""
+    for n in (1, 2, 33, 1000, 65536):
+        rise = np.arange(n, dtype=np.float32)
+        rows = np.stack([np.full(n, 3.0), rise, -rise]).astype(np.float32)
+        for k in sorted({1, min(n, 2), min(n, 512), min(n, 2048), n}):
+            idx, _ = orc.topk_rows(rows, k)
+            assert idx[0].tolist() == list(range(k))
+            assert idx[1].tolist() == list(range(n - k, n))
+            assert idx[2].tolist() == list(range(k))
+    n, k = 100, 10
+    row = np.full((1, n), np.nan, np.float32)
+    row[0, [90, 5, 50]] = [1.0, -2.0, 0.5]
+    idx, _ = orc.topk_rows(row, k)
+    assert idx[0].tolist() == sorted([5, 50, 90] + [i for i in range(n) if i not in (5, 50, 90)][:7])
+
+
+def pin_topk_rows_threshold_invariants(orc):
+    """At indexer scale (n = 65536, k = 2048): indices ascending and in range,
+    values copied exactly, every chosen value >= every unchosen one, and the
+    count strictly above the k-th largest value is < k."""
+    rng = np.random.default_rng(22)
+    n, k = 65536, 2048
+    rows = np.maximum(rng.standard_normal((2, n)), 0).astype(np.float32)
+    rows[1] = np.round(rows[1] * 8) / 8
+    idx, vals = orc.topk_rows(rows, k)
+    for r in range(2):
+        ix = idx[r]
+        assert (np.diff(ix) > 0).all() and ix[0] >= 0 and ix[-1] < n
+        assert np.array_equal(vals[r], rows[r][ix])
+        mask = np.zeros(n, bool)
+        mask[ix] = True
+        assert vals[r].min() >= rows[r][~mask].max()
+        kth = np.sort(rows[r])[::-1][k - 1]
+        assert (rows[r] > kth).sum() < k and vals[r].min() == kth
+        tied = np.flatnonzero(rows[r] == kth)          # the tie at the cut goes by index
+        taken = np.flatnonzero(mask & (rows[r] == kth))
+        assert np.array_equal(taken, tied[:len(taken)])
+
+
+# ---------------------------------------------------------------------------
 # Weights (renormalisation and scale)
 # ---------------------------------------------------------------------------
 

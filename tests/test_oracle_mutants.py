@@ -6,7 +6,7 @@ Each mutant is the oracle compiled with -DORACLE_MUTANT=n (see moe_oracle.c):
  3 bias leaks into the weights              9 router weights read transposed
  4 scale applied before renormalising      10 down projection indexed transposed
  5 SwiGLU intermediate left unrounded      11 NaN keys ranked first
- 6 shared expert dropped
+ 6 shared expert dropped                  12 row top-k: k-th and (k+1)-th swapped
 The pins are tried cheapest first and the search stops at the first one that
 fails, so a mutant costs only the pins it survives.
 """
@@ -20,7 +20,7 @@ CHEAP_FIRST = sorted(pins.ALL_PINS, key=lambda f: (f.__name__ in (
     "pin_f16_decode_all_patterns", "pin_logits_fp64_accuracy"), f.__name__))
 
 
-@pytest.mark.parametrize("n", range(1, 12))
+@pytest.mark.parametrize("n", range(1, 13))
 def test_mutant_is_caught(n, tmp_path):
     orc = Oracle(load(build.build_mutant(n, str(tmp_path))))
     assert orc.mutant() == n
