@@ -60,6 +60,13 @@ WORKLOADS = {
     "s2": dict(base="c4", T=16384, over=dict(label="s2"), copies=1, steps=5, warmup=2, bound="mfma"),
 }
 N_DECODE_TOKENS = 1024
+# Row top-k workloads (the indexer's selection; rows x candidates, top-k):
+# scores rotate over enough copies that no step finds its row in the 256 MB
+# Infinity Cache.
+TOPK_WORKLOADS = {
+    "i2": dict(copies=8, steps=200, warmup=20),
+    "i3": dict(copies=64, steps=400, warmup=40),
+}
 
 
 def describe(cfg):
@@ -281,12 +288,134 @@ def cpu_baseline(cfg, L, x_all, target_s=12.0):
                       " %.1f s wall" % (n, threads, dt)}
 
 
+def bench_topk_rows(args):
+    """Row top-k (moe_topk_rows): one step = one call over every row of the
+    workload.  value = rows per second; roofline: the kernel's algorithmic
+    bytes (scores read once, indices and values written once) over its average
+    dispatch time, taken in a second pass with dispatch events."""
+    import numpy as np
+    import torch
+    import sparse_moe_layer_02_amd as moe
+    from synth import configs
+
+    tw = TOPK_WORKLOADS[args.workload]
+    spec = configs.topk_rows_spec(args.workload)
+    steps = args.steps or tw["steps"]
+    warmup = tw["warmup"] if args.warmup is None else args.warmup
+    n_copies = args.copies or tw["copies"]
+    rows, n, k = spec["rows"], spec["n"], spec["k"]
+    torch.cuda.init()
+    moe.load()
+    hip = Hip()
+    t_gen = time.perf_counter()
+    host = configs.gen_indexer_scores(spec)
+    first = torch.from_numpy(host).cuda()
+    copies = [first] + [first.clone() for _ in range(n_copies - 1)]
+    idx = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    vals = torch.empty((rows, k), dtype=torch.float32, device="cuda")
+    t_gen = time.perf_counter() - t_gen
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i, events=None):
+        moe.moe_topk_rows(copies[i % n_copies], k, idx, vals, stream=stream, events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    w0 = time.perf_counter()
+    hip.record(e0, stream)
+    for i in range(steps):
+        step(warmup + i)
+    hip.record(e1, stream)
+    hip.sync(e1)
+    wall = time.perf_counter() - w0
+    total_ms = hip.ms(e0, e1)
+    # the same steps again with the dispatch's own timestamps
+    ev = [(hip.event(), hip.event()) for _ in range(steps)]
+    for i in range(steps):
+        step(warmup + i, events=(ctypes.c_void_p * 2)(ev[i][0].value, ev[i][1].value))
+    torch.cuda.synchronize()
+    kern_us = float(np.mean([hip.ms(a, b) for a, b in ev])) * 1e3
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    hip.destroy(e0)
+    hip.destroy(e1)
+    alg_bytes = rows * n * 4.0 + rows * k * 8.0
+    achieved = alg_bytes / (kern_us * 1e-6) / 1e9
+    threads = 1024 if n > 512 * 32 else 512  # workgroup size of the launch (one row per workgroup)
+    out = {
+        "metric": "row top-k rows/s (indexer selection); kernel HBM GB/s vs MI355X peak",
+        "value": round(rows * steps / (total_ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(total_ms / steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator; indexer-shaped scores: head-weighted ReLU sums)",
+        "config": {"workload": "%s: %d rows x %d candidates, top-%d, fp32 scores (%d copies rotated)"
+                               % (args.workload, rows, n, k, n_copies),
+                   "rows": rows, "n": n, "k": k, "workgroup_threads": threads},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": topk_traffic_record(args.workload),
+                     "kernel": "topk_rows_kernel", "bytes_per_launch": alg_bytes, "avg_launch_us": round(kern_us, 3)},
+        "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "setup_s": round(t_gen, 1),
+    }
+    if args.copy_probe_mib:
+        out["copy_probe_GBs"] = copy_probe(torch, hip, stream, args.copy_probe_mib)
+        out["copy_probe_bytes"] = args.copy_probe_mib * (1 << 20)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_topk(spec, host, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+TOPK_SOURCES = [_CSRC + f for f in ("topk_rows.hip", "permute_dev.h", "common.h", "kernels.h")]
+
+
+def topk_traffic_record(workload):
+    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(rec_path):
+        return None
+    with open(rec_path) as f:
+        r = json.load(f).get(workload)
+    if not r or r.get("kernel") != "topk_rows_kernel" or r.get("source_sha") != source_sha(TOPK_SOURCES):
+        return None
+    return r.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline_topk(spec, host, target_s=12.0):
+    """The oracle's row top-k on a bounded sample of the workload's rows."""
+    from oracle import Oracle
+    orc = Oracle()
+    n_rows, cap = 1, host.shape[0]
+
+    def run(m):
+        t0 = time.perf_counter()
+        orc.topk_rows(host[:m], spec["k"])
+        return time.perf_counter() - t0
+
+    dt = run(n_rows)
+    while dt < target_s / 2 and n_rows < cap:
+        n_rows = int(min(cap, max(2 * n_rows, n_rows * target_s / max(dt, 1e-3))))
+        dt = run(n_rows)
+    reps = 1
+    if dt < target_s / 2:  # the whole workload is quick: repeat it
+        reps = int(target_s / 2 / max(dt, 1e-3)) + 1
+        dt = sum(run(n_rows) for _ in range(reps))
+    threads = orc.threads()
+    return {"value": n_rows * reps / dt, "unit": "rows/s", "cores": min(threads, n_rows), "kind": "oracle",
+            "sample": "%d rows of the workload per call, %d call(s) (sort-based oracle, one row per OpenMP "
+                      "thread, %d threads), %.2f s wall" % (n_rows, reps, threads, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS) + sorted(TOPK_WORKLOADS))
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated across steps")
     ap.add_argument("--tokens", type=int, default=None,
                     help="tokens per step instead of the workload's (small-batch sweeps)")
@@ -321,6 +450,9 @@ def main():
               "(expert-parallel sharding across GPUs is not built); --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in TOPK_WORKLOADS:
+        return bench_topk_rows(args)
 
     import numpy as np
     import torch

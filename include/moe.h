@@ -176,6 +176,22 @@ int moe_combine(const moe_config *cfg, const float *slot_out, const float *share
 int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w, float *y,
                       moe_debug *dbg, void *ws, size_t ws_bytes, void *stream);
 
+/* Top-k over long candidate rows: the sparse attention indexer's selection of
+ * the best 512 or 1024 entries of a long score row ("256 experts, 512 lines"
+ * blog post, section "The constant that always said 256"), with the order of
+ * the expert selection above.  For each of `rows` rows of scores [rows, n]
+ * fp32, the k candidates that come first (larger score first, NaN after every
+ * number, -0 equal to +0, equal scores by lower candidate index) go to
+ * idx [rows, k] int32, listed by ascending candidate index, and their scores,
+ * bit for bit, to vals [rows, k] fp32 (vals may be NULL).
+ * 1 <= k <= n <= MOE_TOPK_ROWS_MAX_N and rows >= 0 (0 enqueues nothing), else
+ * MOE_ERR_INVALID; scores, idx and vals need 4-byte alignment.  No workspace.
+ * events: NULL, or 2 hipEvent_t created by the caller (entries may be NULL)
+ * that receive the start and end timestamps of the kernel dispatch. */
+#define MOE_TOPK_ROWS_MAX_N 65536
+int moe_topk_rows(const float *scores, int32_t rows, int32_t n, int32_t k, int32_t *idx, float *vals,
+                  void **events, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_str(int status);
 

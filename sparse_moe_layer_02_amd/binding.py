@@ -59,7 +59,8 @@ class moe_debug(ctypes.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_layer_forward", "moe_status_str")
+           "moe_combine", "moe_layer_forward", "moe_topk_rows", "moe_status_str")
+TOPK_ROWS_MAX_N = 65536  # MOE_TOPK_ROWS_MAX_N
 
 _lib = None
 
@@ -83,6 +84,8 @@ def load(path: str = LIB_PATH):
     lib.moe_expert_ffn.argtypes = [C, P, W, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_combine.argtypes = [C, P, P, P, P]
     lib.moe_layer_forward.argtypes = [C, P, W, P, ctypes.POINTER(moe_debug), P, ctypes.c_size_t, P]
+    I = ctypes.c_int32
+    lib.moe_topk_rows.argtypes = [P, I, I, I, P, P, ctypes.POINTER(ctypes.c_void_p), P]
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     for name in EXPORTS[1:-1]:
@@ -206,6 +209,17 @@ def moe_layer_forward(cfg, x, weights: moe_weights, y, ws, debug: dict | None = 
     return _check(lib.moe_layer_forward(ctypes.byref(cfg), ptr(x), ctypes.byref(weights), ptr(y),
                                         ctypes.byref(dbg) if dbg else None, ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)), lib)
+
+
+def moe_topk_rows(scores, k, idx, vals=None, stream=None, events=None):
+    """Row top-k of ``scores`` [rows, n] fp32 into ``idx`` [rows, k] int32 (ascending
+    candidate index) and ``vals`` [rows, k] fp32 (optional).  ``events``: optional
+    ctypes array of 2 hipEvent_t handles (dispatch start and end timestamps)."""
+    lib = load()
+    rows, n = scores.shape
+    ev = None if events is None else ctypes.cast(events, ctypes.POINTER(ctypes.c_void_p))
+    return _check(lib.moe_topk_rows(ptr(scores), rows, n, k, ptr(idx), ptr(vals), ev,
+                                    _stream(stream)), lib)
 
 
 def workspace(cfg: moe_config, device="cuda"):

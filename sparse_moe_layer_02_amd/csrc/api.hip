@@ -301,6 +301,21 @@ int moe_select(const moe_config* cfg, const float* logits, const float* bias, in
     return device_status(launch_topk(a, static_cast<hipStream_t>(stream)));
 }
 
+int moe_topk_rows(const float* scores, int32_t rows, int32_t n, int32_t k, int32_t* idx, float* vals,
+                  void** events, void* stream) {
+    static_assert(MOE_TOPK_ROWS_MAX_N == TOPK_ROWS_MAX_N, "row top-k limit");
+    if (rows < 0 || n < 1 || n > MOE_TOPK_ROWS_MAX_N || k < 1 || k > n) return MOE_ERR_INVALID;
+    if (rows == 0) return MOE_OK;
+    if (!elt_ok(scores) || !elt_ok(idx) || !opt_elt_ok(vals)) return MOE_ERR_INVALID;
+    KTime kt;
+    if (events) {
+        kt.start = static_cast<hipEvent_t>(events[0]);
+        kt.stop = static_cast<hipEvent_t>(events[1]);
+    }
+    TopkRowsArgs a{scores, rows, n, k, idx, vals};
+    return device_status(launch_topk_rows(a, static_cast<hipStream_t>(stream), kt));
+}
+
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* offsets, int32_t* perm_rows,
                 int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
     int s = validate_config(cfg);

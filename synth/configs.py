@@ -190,3 +190,55 @@ def algorithmic_bytes_per_expert(cfg) -> int:
     """HBM bytes of one routed expert's three matrices in the stored format."""
     n = 3 * cfg["F"] * cfg["d"]
     return {"f32": 4 * n, "bf16": 2 * n, "q8b32": n + n // 16}[cfg["w"]]
+
+
+# ---------------------------------------------------------------------------
+# Row top-k workloads: the sparse attention indexer's selection (its top-512
+# and top-1024 over a long row of scores: "256 experts, 512 lines" blog post,
+# section "The constant that always said 256").  A row is one query token's
+# scores against n candidate key rows.
+#   i1  small parity case: 8 rows x 5000 candidates, top-512
+#   i2  a 512-token prefill chunk against 32768 candidates, top-1024
+#   i3  one decode token against 65536 candidates, top-1024
+# Streams: normals 12, head weights 13.
+# ---------------------------------------------------------------------------
+S_IDX_Z, S_IDX_W = 12, 13
+
+TOPK_ROWS = {
+    "i1": dict(rows=8, n=5000, k=512, heads=4, fmt="f32"),
+    "i2": dict(rows=512, n=32768, k=1024, heads=4, fmt="f32"),
+    "i3": dict(rows=1, n=65536, k=1024, heads=4, fmt="f32"),
+}
+
+
+def topk_rows_spec(name: str, **over) -> dict:
+    spec = copy.deepcopy(TOPK_ROWS[name])
+    spec.update(over)
+    spec.setdefault("name", name)
+    spec.setdefault("seed", 0)
+    return spec
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 (ties to even), kept as fp32."""
+    b = a.astype(np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return (b & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+
+
+def gen_indexer_scores(spec, row0=0, rows=None):
+    """Scores [rows, n] fp32 shaped like an indexer's output: a weighted sum
+    over heads of ReLU'd dot products, score[r, s] = sum_h w[r, h] *
+    max(z[r, s, h], 0) with z ~ N(0, 1) and per-row head weights w ~ U(0, 1).
+    They are nonnegative with about one exact zero in 2^heads.  fmt "bf16"
+    rounds them to bf16 precision, which makes exact ties common."""
+    rows = spec["rows"] if rows is None else rows
+    n, H, seed = spec["n"], spec["heads"], spec["seed"]
+    z = normal_f32(seed, S_IDX_Z, rows * n * H, 1.0, start=row0 * n * H).reshape(rows, n, H)
+    w = uniform_f32(seed, S_IDX_W, rows * H, 0.0, 1.0, start=row0 * H).reshape(rows, H)
+    s = np.zeros((rows, n), np.float32)
+    for h in range(H):
+        s += w[:, h:h + 1] * np.maximum(z[:, :, h], np.float32(0))
+    if spec.get("fmt", "f32") == "bf16":
+        s = round_to_bf16(s)
+    return np.ascontiguousarray(s, np.float32)

@@ -93,6 +93,26 @@ def test_null_and_misaligned_pointers(moe):
     assert lib.moe_layer_forward(ctypes.byref(c), fake, ctypes.byref(w), fake, None, fake, 1 << 40, None) == 1
 
 
+@pytest.mark.parametrize("rows,n,k", [(-1, 8, 1), (4, 0, 1), (4, 8, 0), (4, 8, 9), (4, 65537, 8),
+                                      (4, 65537, 65537), (1, 1, 2)])
+def test_topk_rows_invalid_sizes(moe, rows, n, k):
+    lib = moe.load()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.moe_topk_rows(fake, rows, n, k, fake, fake, None, None) == 1
+
+
+def test_topk_rows_pointers(moe):
+    lib = moe.load()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.moe_topk_rows(None, 4, 100, 8, fake, fake, None, None) == 1
+    assert lib.moe_topk_rows(fake, 4, 100, 8, None, fake, None, None) == 1
+    assert lib.moe_topk_rows(odd, 4, 100, 8, fake, None, None, None) == 1
+    assert lib.moe_topk_rows(fake, 4, 100, 8, fake, odd, None, None) == 1
+    # no rows: nothing to do, nothing enqueued (valid even with NULL pointers)
+    assert lib.moe_topk_rows(None, 0, 100, 8, None, None, None, None) == 0
+
+
 def test_workspace_too_small(moe):
     lib = moe.load()
     c = _cfg(moe)
