@@ -212,7 +212,10 @@ def record_traffic(workload, path_kind, w, fetch_csv, write_csv, copy_bytes, rec
     dispatch) into HBM bytes per launch of the dominant kernel.  Each counter is
     scaled by the factor that makes it read right on the plain device copy of
     ``copy_bytes`` (read and written once) that the same command ran."""
-    kname, srcs = dominant(path_kind, w, rpe)
+    if workload in TOPK_WORKLOADS:
+        kname, srcs = "topk_rows_kernel", TOPK_SOURCES
+    else:
+        kname, srcs = dominant(path_kind, w, rpe)
     res = {"kernel": kname, "source_sha": source_sha(srcs), "copy_bytes": copy_bytes}
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(path) if r[2] == counter]
@@ -371,7 +374,7 @@ def bench_topk_rows(args):
     print(json.dumps(out), flush=True)
 
 
-TOPK_SOURCES = [_CSRC + f for f in ("topk_rows.hip", "permute_dev.h", "common.h", "kernels.h")]
+TOPK_SOURCES = [_CSRC + f for f in ("topk_rows.hip", "common.h", "kernels.h")]
 
 
 def topk_traffic_record(workload):
@@ -435,6 +438,10 @@ def main():
                     help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv "
                          "files of a run made with --copy-probe-mib")
     args = ap.parse_args()
+    if args.record_traffic and args.workload in TOPK_WORKLOADS:
+        record_traffic(args.workload, None, None, args.record_traffic[0], args.record_traffic[1],
+                       (args.copy_probe_mib or 1024) * (1 << 20))
+        return
     if args.record_traffic:
         from synth import configs as _cf
         from sparse_moe_layer_02_amd.binding import DECODE_MAX_TOKENS

@@ -5,119 +5,205 @@
 // sparse attention indexer (top-512 or top-1024 rows out of a long row; "256
 // experts, 512 lines" blog post, section "The constant that always said 256").
 //
-// One workgroup per row; the row stays in registers (NPT keys per thread,
-// element i = j * THREADS + tid, so every load instruction is coalesced).
-//   1. Keys: the float is mapped to an unsigned key whose integer order is the
-//      selection order (NaN -> 1, padding -> 0, -0 -> +0).
+// One workgroup per row; the row stays in registers.  Wavefront w owns the
+// contiguous candidates [w * NPT * 64, (w + 1) * NPT * 64): chunk j of it is
+// the 64 candidates from w * NPT * 64 + j * 64, one per lane, so every load
+// instruction reads 256 contiguous bytes and (chunk, lane) order is index order.
+//   1. Keys: the float's bits mapped to an unsigned key whose integer order is
+//      the selection order (padding -> 0).  NaN (-> 1) and -0 (-> the key of
+//      +0) need a fix-up that only wavefronts holding one of them run.
 //   2. Radix select, 8 bits per pass from the top: a 256-bin histogram of the
 //      keys that still match the resolved prefix, the bin where the running
 //      count from the top reaches the number still needed, and the prefix
 //      grows by that digit.  A pass ends the search early when the whole bin is
-//      needed.  The histogram keeps one column per lane (two 16-bit counters
-//      per word), so the LDS atomics of one instruction never share an
-//      address, whatever the score distribution (floats in a narrow range put
-//      nearly every key in one or two top-byte bins).
-//   3. Compaction in index order: per (chunk, wavefront) group the counts of
-//      keys above the threshold and equal to it, a block-wide exclusive scan
-//      of both, then each chosen key's output position = keys above it with a
-//      lower index + min(equal keys with a lower index, equal keys needed).
-//      The tie at the threshold is thereby cut by index.
+//      needed.  The histogram keeps 32 columns per bin and lane l adds to
+//      column l % 32, so the LDS atomics of one instruction never collide more
+//      than two to an address, whatever the score distribution (floats in a
+//      narrow range put nearly every key in one or two top-byte bins).
+//   3. Output in index order: each wavefront counts its keys above the
+//      threshold and equal to it; the wavefront totals give every wavefront the
+//      number of chosen candidates before it.  Equal keys are chosen while their
+//      rank among equal keys is below the number still needed, which cuts the
+//      tie at the threshold by index; only the wavefront holding the cut tests
+//      that rank.  A chosen candidate's position is the running count of its
+//      wavefront plus its rank in the chunk's ballot; chosen candidates wait in
+//      a ring in LDS private to the wavefront and leave 64 at a time, in one
+//      coalesced store per output array.
 #include "kernels.h"
-#include "permute_dev.h"
 
 namespace moe {
 namespace {
 
-// Selection order as an unsigned integer order; 0 is reserved for padding.
-// Integer operations only (subnormal scores keep their order), and every step
-// works on the key itself, so the loaded value dies at once.
-__device__ __forceinline__ uint32_t order_key(float x) {
-    const uint32_t u = __float_as_uint(x);
-    uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // negative: ~u; else u | sign bit
-    k = k == 0x7FFFFFFFu ? 0x80000000u : k;                          // -0 ranks with +0
-    // NaN: +NaN maps above +inf's key 0xFF800000, -NaN below -inf's 0x007FFFFF
+// Key of a float whose bits are u: negative -> ~u, else u with the sign bit
+// set.  Integer order of keys is numeric order (integer operations only, so
+// subnormal scores keep their order), except for NaN and -0 (fixed below).
+__device__ __forceinline__ uint32_t raw_key(uint32_t u) {
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+// The fix-up: -0 (key 0x7FFFFFFF) ranks with +0, every NaN (+NaN above +inf's
+// key 0xFF800000, -NaN below -inf's 0x007FFFFF) becomes 1, below every number.
+__device__ __forceinline__ uint32_t fix_key(uint32_t k) {
+    k = k == 0x7FFFFFFFu ? 0x80000000u : k;
     return k - 0x007FFFFFu <= 0xFF800000u - 0x007FFFFFu ? k : 1u;
+}
+
+// The score a key came from, branch-free: a key with the top bit set came from
+// a non-negative float (clear the bit), any other from a negative one (invert).
+// Exact except for the two keys that merge several bit patterns (0x80000000:
+// +0 or -0; 1: any NaN), which the caller reloads.
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float(k ^ (~(uint32_t)((int32_t)k >> 31) | 0x80000000u));
 }
 
 struct TkState {
     uint32_t prefix, mask, need, done;
 };
 
+// Writes the chosen candidates of one wavefront.  CUT: this wavefront holds the
+// cut of the tie at the threshold (equal keys are chosen while their rank among
+// equal keys, erun + ballot rank, is below need); otherwise a key is chosen when
+// key & mask >= pc.  SPECIAL: the row holds NaN or -0, whose values are reloaded.
+// The wavefront's outputs are the contiguous positions [run, run + its count):
+// chosen candidates go to a 128-entry ring in LDS (private to the wavefront, so
+// no workgroup barrier), and every 64 of them leave in one coalesced store per
+// output array.  The stores go through buffer descriptors of k entries.
+constexpr int TK_RING = 128;
+
+template <int NPT, bool CUT, bool SPECIAL>
+__device__ __forceinline__ void emit_wave(const uint32_t* key, uint32_t mask, uint32_t pc, uint32_t prefix,
+                                          uint32_t need, uint32_t run, uint32_t erun, int base0, bool with_vals,
+                                          uint32_t* ring_i, uint32_t* ring_v, __amdgpu_buffer_rsrc_t out_idx,
+                                          __amdgpu_buffer_rsrc_t out_vals, __amdgpu_buffer_rsrc_t rsrc) {
+    const int lane = lane_id();
+    const uint32_t start = run;  // outputs [start, flushed) are stored, [flushed, run) wait in the ring
+    uint32_t flushed = start;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const uint32_t km = key[j] & mask;
+        bool chosen;
+        if (CUT) {
+            const uint64_t em = __ballot(km == prefix);
+            const uint32_t erank = (uint32_t)__builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(em >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)em, erun));
+            chosen = km > prefix || (km == prefix && erank < need);
+            erun += (uint32_t)__popcll(em);
+        } else {
+            chosen = km >= pc;
+        }
+        const uint64_t cm = __ballot(chosen);
+        if (cm == 0ull) continue;
+        const uint32_t pos =
+            (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cm, run));
+        run += (uint32_t)__popcll(cm);
+        if (chosen) {
+            const int i = base0 + j * WAVE + lane;
+            const uint32_t kk = key[j];
+            float v = key_value(kk);  // rebuilt from the key: no memory round trip per chosen score
+            if (SPECIAL && with_vals && (kk == 0x80000000u || kk == 1u))
+                v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, i * 4, 0, 0));
+            const uint32_t slot = (pos - start) % TK_RING;
+            ring_i[slot] = (uint32_t)i;
+            ring_v[slot] = __float_as_uint(v);
+        }
+        if (run - flushed >= (uint32_t)WAVE) {  // fewer than 64 wait before a chunk, so the ring never overruns
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const uint32_t e = flushed + (uint32_t)lane, slot = (e - start) % TK_RING;
+            __builtin_amdgcn_raw_buffer_store_b32(ring_i[slot], out_idx, (int)(e * 4u), 0, 0);
+            if (with_vals) __builtin_amdgcn_raw_buffer_store_b32(ring_v[slot], out_vals, (int)(e * 4u), 0, 0);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            flushed += WAVE;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const uint32_t e = flushed + (uint32_t)lane;
+    if (e < run) {
+        const uint32_t slot = (e - start) % TK_RING;
+        __builtin_amdgcn_raw_buffer_store_b32(ring_i[slot], out_idx, (int)(e * 4u), 0, 0);
+        if (with_vals) __builtin_amdgcn_raw_buffer_store_b32(ring_v[slot], out_vals, (int)(e * 4u), 0, 0);
+    }
+}
+
 template <int THREADS, int NPT>
 __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
     constexpr int WAVES = THREADS / WAVE;
-    constexpr int GROUPS = NPT * WAVES;  // (chunk, wavefront) groups in index order
-    constexpr int S = THREADS / 128;     // merge threads per histogram word
-    constexpr int R = WAVE / S;          // lane columns each of them sums
-    static_assert(GROUPS <= THREADS && S >= 1 && R * S == WAVE, "launch shape");
+    constexpr int SPAN = NPT * WAVE;  // candidates per wavefront
+    constexpr int COLS = 32;          // histogram columns: lane l adds to column l % 32
+    constexpr int S = THREADS / 256;  // merge threads per bin
+    constexpr int R = COLS / S;       // columns each of them sums
+    static_assert(S >= 1 && R * S == COLS && WAVES <= WAVE, "launch shape");
 
-    __shared__ uint32_t hist[128][WAVE];  // word w: bins 2w (low half), 2w+1 (high half); column = lane
+    __shared__ uint32_t hist[256 * COLS];  // [bin][column]
     __shared__ uint32_t tot[256];         // tot[r] = count of bin 255 - r
-    __shared__ uint32_t cgt[GROUPS], ceq[GROUPS];
-    __shared__ uint32_t wsum[2][WAVES];
+    __shared__ uint32_t wtot[3][WAVES];   // per wavefront: keys above, equal, any NaN / -0
+    __shared__ uint32_t ring[WAVES][2][TK_RING];  // per wavefront: chosen indices and values on their way out
     __shared__ TkState st;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_index();
     const int n = a.n, k = a.k;
+    const int base0 = wave * SPAN;
     const float* row = a.scores + (size_t)blockIdx.x * n;
 
-    for (int w = tid; w < 128 * WAVE; w += THREADS) (&hist[0][0])[w] = 0;
+    for (int w = tid; w < 256 * COLS; w += THREADS) hist[w] = 0;
 
     // Every load is issued before the first key is formed.  Buffer loads: one
-    // offset register for all chunks (the chunk goes in the scalar offset),
-    // and the range check of the descriptor (n floats) returns 0 past the row.
+    // offset register (the chunk goes in the instruction's offset), and the
+    // range check of the descriptor (n floats) returns 0 past the row.
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, n * 4, 0x00020000);
-    float v[NPT];
-#pragma unroll
-    for (int j = 0; j < NPT; ++j)
-        v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 4, j * THREADS * 4, 0));
     uint32_t key[NPT];
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) key[j] = tid < n - j * THREADS ? order_key(v[j]) : 0u;  // scalar bound per chunk
+    for (int j = 0; j < NPT; ++j) key[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (base0 + lane) * 4, j * WAVE * 4, 0);
+    uint64_t special = 0;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        uint32_t u = key[j];
+        asm volatile("" : "+v"(u));  // keeps every load ahead of all key arithmetic
+        special |= __ballot(__builtin_amdgcn_classf(__uint_as_float(u), 0x23));  // NaN or -0
+        key[j] = raw_key(u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (special != 0ull) {
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) key[j] = fix_key(key[j]);
+    }
+    if (base0 + SPAN > n) {  // the wavefront reaches past the row: padding keys are 0
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) key[j] = lane < n - (base0 + j * WAVE) ? key[j] : 0u;
+    }
+    if (lane == 0) wtot[2][wave] = special != 0ull ? 1u : 0u;
     __syncthreads();
 
     // ---- radix select ----------------------------------------------------
     uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
+    uint32_t* my_col = &hist[lane % COLS];
     for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
         for (int j = 0; j < NPT; ++j) {
             const uint32_t kk = key[j];
-            if ((kk & mask) == prefix) {
-                const uint32_t b = (kk >> shift) & 255u;
-                atomicAdd(&hist[b >> 1][lane], 1u << ((b & 1u) * 16u));
-            }
+            if ((kk & mask) == prefix) atomicAdd(my_col + ((kk >> shift) & 255u) * COLS, 1u);
         }
         __syncthreads();
         {
-            const int w = tid / S, s = tid % S;
-            uint32_t lo = 0, hi = 0;
+            const int b = tid / S, s = tid % S;
+            uint32_t c = 0;
             // not unrolled fully: the R column addresses would stay live in
             // registers for the whole kernel
 #pragma unroll 4
             for (int i = 0; i < R; ++i) {
-                const int l = s * R + ((i + w) % R);  // distinct columns across a wavefront: no bank conflicts
-                const uint32_t c = hist[w][l];
-                hist[w][l] = 0;
-                lo += c & 0xFFFFu;
-                hi += c >> 16;
+                const int l = s * R + ((i + b) % R);  // distinct columns across a wavefront: no bank conflicts
+                c += hist[b * COLS + l];
+                hist[b * COLS + l] = 0;
             }
 #pragma unroll
-            for (int o = 1; o < S; o <<= 1) {
-                lo += __shfl_xor(lo, o);
-                hi += __shfl_xor(hi, o);
-            }
-            if (s == 0) {
-                tot[255 - 2 * w] = lo;
-                tot[254 - 2 * w] = hi;
-            }
+            for (int o = 1; o < S; o <<= 1) c += __shfl_xor(c, o);
+            if (s == 0) tot[255 - b] = c;
         }
         __syncthreads();
         if (wave == 0) {
             const uint32_t c0 = tot[4 * lane], c1 = tot[4 * lane + 1], c2 = tot[4 * lane + 2],
                            c3 = tot[4 * lane + 3];
             const uint32_t sum = c0 + c1 + c2 + c3;
-            const uint32_t incl = (uint32_t)wave_incl_scan((int)sum);
+            const uint32_t incl = wave_incl_scan_u32(sum);
             const uint64_t hit = __ballot(incl >= need);
             if (hit != 0ull && lane == __ffsll((unsigned long long)hit) - 1) {
                 uint32_t above = incl - sum, c = c0;
@@ -150,61 +236,56 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
         if (__builtin_amdgcn_readfirstlane(st.done)) break;
     }
 
-    // ---- compaction in index order ----------------------------------------
+    // ---- output in index order --------------------------------------------
     // Chosen: key & mask > prefix (all of them), and the first `need` keys with
     // key & mask == prefix by index.  Padding (key 0) never passes either test.
+    uint32_t g_w = 0, e_w = 0;  // this wavefront's keys above / at the threshold
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
         const uint32_t km = key[j] & mask;
-        const uint64_t bg = __ballot(km > prefix), be = __ballot(km == prefix);
-        if (lane == 0) {
-            cgt[j * WAVES + wave] = (uint32_t)__popcll(bg);
-            ceq[j * WAVES + wave] = (uint32_t)__popcll(be);
-        }
+        g_w += (uint32_t)__popcll(__ballot(km > prefix));
+        e_w += (uint32_t)__popcll(__ballot(km == prefix));
+        __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: no scalar masks held across chunks
+    }
+    asm volatile("" : "+s"(g_w), "+s"(e_w));  // counted here, not inside the store's branch
+    if (lane == 0) {
+        wtot[0][wave] = g_w;
+        wtot[1][wave] = e_w;
     }
     __syncthreads();
-    {
-        const uint32_t g = tid < GROUPS ? cgt[tid] : 0u, e = tid < GROUPS ? ceq[tid] : 0u;
-        const uint32_t gi = (uint32_t)wave_incl_scan((int)g), ei = (uint32_t)wave_incl_scan((int)e);
-        if (lane == WAVE - 1) {
-            wsum[0][wave] = gi;
-            wsum[1][wave] = ei;
-        }
-        __syncthreads();
-        uint32_t gb = 0, eb = 0;
-        for (int w = 0; w < wave; ++w) {
-            gb += wsum[0][w];
-            eb += wsum[1][w];
-        }
-        if (tid < GROUPS) {
-            cgt[tid] = gb + gi - g;
-            ceq[tid] = eb + ei - e;
-        }
-    }
-    __syncthreads();
-    // The threshold is read again after the barrier, so the tests below are
-    // recomputed instead of being held in registers since the count loop.
-    const uint32_t M = __builtin_amdgcn_readfirstlane(st.mask), P = __builtin_amdgcn_readfirstlane(st.prefix),
-                   NEED = __builtin_amdgcn_readfirstlane(st.need);
-    const uint64_t below = lanemask_lt();
-    int32_t* idx = a.idx + (size_t)blockIdx.x * k;
-    float* vals = a.vals ? a.vals + (size_t)blockIdx.x * k : nullptr;
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-        const uint32_t km = key[j] & M;
-        const bool gt = km > P, eq = km == P;
-        const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        if (bg == 0ull && be == 0ull) continue;
-        const uint32_t g_before = cgt[j * WAVES + wave] + (uint32_t)__popcll(bg & below);
-        const uint32_t e_before = ceq[j * WAVES + wave] + (uint32_t)__popcll(be & below);
-        uint32_t pos = 0xFFFFFFFFu;
-        if (gt) pos = g_before + min(e_before, NEED);
-        else if (eq && e_before < NEED) pos = g_before + e_before;
-        if (pos < (uint32_t)k && tid < n - j * THREADS) {  // both hold by construction
-            const int i = j * THREADS + tid;
-            idx[pos] = i;
-            if (vals) vals[pos] = row[i];
-        }
+    // lane w < WAVES holds wavefront w's totals; DPP sums give the totals of the
+    // wavefronts before this one
+    const uint32_t wg = lane < WAVES ? wtot[0][lane] : 0u, we = lane < WAVES ? wtot[1][lane] : 0u;
+    const bool row_special = __ballot(lane < WAVES && wtot[2][lane] != 0u) != 0ull;
+    const uint32_t g_base = wave_sum_u32(lane < wave ? wg : 0u), e_base = wave_sum_u32(lane < wave ? we : 0u);
+    // The threshold passes through an empty asm statement, so the tests below
+    // are recomputed instead of being held in scalar registers since the counts.
+    uint32_t M = mask, P = prefix, NEED = need;
+    asm volatile("" : "+s"(M), "+s"(P), "+s"(NEED));
+    const uint32_t run = g_base + min(e_base, NEED);  // chosen candidates before this wavefront
+    const bool with_vals = a.vals != nullptr;
+    const __amdgpu_buffer_rsrc_t out_idx =
+        __builtin_amdgcn_make_buffer_rsrc(a.idx + (size_t)blockIdx.x * k, (short)0, k * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t out_vals = __builtin_amdgcn_make_buffer_rsrc(
+        with_vals ? (void*)(a.vals + (size_t)blockIdx.x * k) : (void*)(a.idx + (size_t)blockIdx.x * k), (short)0,
+        k * 4, 0x00020000);
+    const bool all_eq = e_base + e_w <= NEED, no_eq = e_base >= NEED;
+    if (all_eq || no_eq) {
+        if (no_eq && P == 0xFFFFFFFFu) return;  // nothing above the largest key: no output here
+        const uint32_t pc = all_eq ? P : P + 1u;
+        if (row_special)
+            emit_wave<NPT, false, true>(key, M, pc, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+                                         out_idx, out_vals, rsrc);
+        else
+            emit_wave<NPT, false, false>(key, M, pc, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+                                         out_idx, out_vals, rsrc);
+    } else {
+        if (row_special)
+            emit_wave<NPT, true, true>(key, M, P, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+                                        out_idx, out_vals, rsrc);
+        else
+            emit_wave<NPT, true, false>(key, M, P, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+                                        out_idx, out_vals, rsrc);
     }
 }
 
