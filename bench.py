@@ -374,7 +374,7 @@ def bench_topk_rows(args):
     print(json.dumps(out), flush=True)
 
 
-TOPK_SOURCES = [_CSRC + f for f in ("topk_rows.hip", "common.h", "kernels.h")]
+TOPK_SOURCES = [_CSRC + f for f in ("topk_rows.hip", "topk_rows.h", "common.h", "kernels.h")]
 
 
 def topk_traffic_record(workload):

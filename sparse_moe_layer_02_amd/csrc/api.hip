@@ -8,6 +8,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk_rows.h"
 
 using namespace moe;
 

@@ -100,23 +100,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Inclusive scan of an unsigned 32-bit value over the 64 lanes (the same DPP
-// steps: after them lane l holds the sum of lanes 0..l).
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
-    v += dpp_u32<DPP_ROW_SHR1>(v);
-    v += dpp_u32<DPP_ROW_SHR2>(v);
-    v += dpp_u32<DPP_ROW_SHR4>(v);
-    v += dpp_u32<DPP_ROW_SHR8>(v);
-    v += dpp_u32<DPP_ROW_BCAST15, 0xA>(v);
-    v += dpp_u32<DPP_ROW_BCAST31, 0xC>(v);
-    return v;
-}
-
-// Wave-wide sum of an unsigned 32-bit value; every lane receives it.
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-    return __builtin_amdgcn_readlane(wave_incl_scan_u32(v), 63);
-}
-
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Index of this wavefront in its workgroup, as a wave-uniform (scalar) value.

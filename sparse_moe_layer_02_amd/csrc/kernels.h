@@ -47,18 +47,6 @@ struct SelectArgs {
 };
 hipError_t launch_topk(const SelectArgs& a, hipStream_t st, const KTime& kt = KTime());
 
-// Top-k over long candidate rows (one workgroup per row); n <= TOPK_ROWS_MAX_N.
-constexpr int TOPK_ROWS_MAX_N = 65536;
-struct TopkRowsArgs {
-    const float* scores;  // [rows, n]
-    int rows, n, k;
-    int32_t* idx;  // [rows, k], ascending candidate index
-    float* vals;   // [rows, k] or null
-};
-hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t st, const KTime& kt = KTime());
-int topk_rows_threads(int n);  // workgroup size of the launch that takes n candidates
-int topk_rows_npt(int n);      // keys per thread of that launch (0: n out of range)
-
 struct PermArgs {
     const int32_t* topk_idx;
     int T, k, E;

@@ -29,7 +29,7 @@
 //      wavefront plus its rank in the chunk's ballot; chosen candidates wait in
 //      a ring in LDS private to the wavefront and leave 64 at a time, in one
 //      coalesced store per output array.
-#include "kernels.h"
+#include "topk_rows.h"
 
 namespace moe {
 namespace {
