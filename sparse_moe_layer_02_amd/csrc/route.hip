@@ -210,6 +210,122 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Prefill router on the fp64 matrix cores, for many tokens: a workgroup of eight
+// wavefronts computes a 64-token x 64-expert tile of logits, each wavefront a
+// 16 x 32 piece as 1 x 2 blocks of v_mfma_f64_16x16x4_f64 (A = x rows, B =
+// Wr rows, widened to fp64 as they are read from LDS; every product is exact
+// in fp64 and the unit accumulates in fp64, so only the order of the fp64
+// additions differs from the definition's, far below the fp32 rounding of the
+// result).  K is staged raw through two LDS stages of 64 columns: the next
+// chunk's global loads are in flight while the current one is consumed, and
+// one barrier per chunk separates the stages.
+//
+// Operand layout of the 16x16x4 f64 instruction (checked on the device): lane l
+// supplies A[l % 16][l / 16] and B[l / 16][l % 16]; its four results are
+// D[l / 16 + 4 j][l % 16], j = 0..3.
+// ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+template <int AF>
+__global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict__ x,
+                                                          const float* __restrict__ wr, int T, int d,
+                                                          int E, float* __restrict__ logits) {
+    constexpr int TM = 64, TE = 64, KC = 64, NT = 512;
+    constexpr int XW = AF == MOE_DT_BF16 ? KC / 2 : KC;  // 32-bit words of one staged x row
+    constexpr int XP = XW + 1, WP = KC + 1;              // row pitches in words (odd: rows on distinct banks)
+    __shared__ uint32_t xs[2][TM * XP];                  // raw x (bf16 pairs or fp32), two stages
+    __shared__ float ws[2][TE * WP];                     // raw Wr, two stages
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
+    // staging items of 16 bytes: x rows hold XW / 4 of them, Wr rows KC / 4
+    constexpr int XQ = TM * XW / 4, WQ = TE * KC / 4;
+    constexpr int XI = (XQ + NT - 1) / NT, WI = WQ / NT;
+    static_assert(WQ % NT == 0 && XI <= 2, "staging shape");
+    uint4 rx[XI];
+    float4 rw[WI];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int it = 0; it < XI; ++it) {
+            const int q = tid + NT * it, r = q / (XW / 4), c = (q % (XW / 4)) * 4;  // c in words
+            rx[it] = make_uint4(0, 0, 0, 0);
+            if (q < XQ && t0 + r < T) {
+                const uint32_t* row = AF == MOE_DT_BF16
+                    ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + (size_t)(t0 + r) * d + k0)
+                    : reinterpret_cast<const uint32_t*>(static_cast<const float*>(x) + (size_t)(t0 + r) * d + k0);
+                rx[it] = *reinterpret_cast<const uint4*>(row + c);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < WI; ++it) {
+            const int q = tid + NT * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
+            rw[it] = e0 + r < E ? *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * d + k0 + c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto lstore = [&](int stg) {
+#pragma unroll
+        for (int it = 0; it < XI; ++it) {
+            const int q = tid + NT * it, r = q / (XW / 4), c = (q % (XW / 4)) * 4;
+            if (q < XQ) {
+                uint32_t* dst = &xs[stg][r * XP + c];
+                dst[0] = rx[it].x; dst[1] = rx[it].y; dst[2] = rx[it].z; dst[3] = rx[it].w;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < WI; ++it) {
+            const int q = tid + NT * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
+            float* dst = &ws[stg][r * WP + c];
+            dst[0] = rw[it].x; dst[1] = rw[it].y; dst[2] = rw[it].z; dst[3] = rw[it].w;
+        }
+    };
+    // x[m][k] of a stage, widened to fp64 (exact)
+    auto xval = [&](int stg, int m, int kk) -> double {
+        if (AF == MOE_DT_BF16) {
+            const uint32_t pair = xs[stg][m * XP + (kk >> 1)];
+            return (double)((kk & 1) ? bf16_hi(pair) : bf16_lo(pair));
+        }
+        return (double)__uint_as_float(xs[stg][m * XP + kk]);
+    };
+
+    // wavefront w: tokens (w / 2) * 16 .. +15, experts (w % 2) * 32 .. +31 of the tile
+    const int wm = (wave / 2) * 16, wn = (wave % 2) * 32;
+    const int lr = lane % 16, lk = lane / 16;
+    f64x4 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+    const int nch = d / KC;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        const int stg = ch & 1;
+        if (ch + 1 < nch) gload((ch + 1) * KC);  // in flight during this chunk's products
+#pragma unroll
+        for (int ks = 0; ks < KC; ks += 4) {
+            const double a = xval(stg, wm + lr, ks + lk);
+            double b[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = (double)ws[stg][(wn + 16 * j + lr) * WP + ks + lk];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[j], acc[j], 0, 0, 0);
+        }
+        // the other stage was last read in the previous chunk, before the barrier below it
+        if (ch + 1 < nch) lstore(stg ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = e0 + wn + 16 * j + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + wm + lk + 4 * r;
+            if (t < T && e < E) logits[(size_t)t * E + e] = (float)acc[j][r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Top-k: one wavefront per token (topk_token in route_dev.h).
 // ---------------------------------------------------------------------------
 template <int KPL, int EFIX>
@@ -235,12 +351,18 @@ static void router_gemm_tile(const RouteArgs& a, hipStream_t st, const KTime& kt
                   a.logits);
 }
 
-// The largest tile that still gives every compute unit two workgroups; the
-// smallest when none does (few tokens).
+// The matrix-core kernel from 128 tiles of 64 x 64 on (it runs one
+// workgroup per compute unit and cannot split K); below that the largest VALU
+// tile that still gives every compute unit two workgroups, the smallest when
+// none does (few tokens).
+constexpr long ROUTER_MFMA_MIN_TILES = 128;
 template <int AF>
 static void router_gemm_launch(const RouteArgs& a, hipStream_t st, const KTime& kt) {
     auto blocks = [&](int tm, int te) { return (long)((a.T + tm - 1) / tm) * ((a.E + te - 1) / te); };
-    if (a.d % 64 == 0 && blocks(64, 64) >= 512) router_gemm_tile<AF, 64, 64, 4, 4, 32>(a, st, kt);
+    if (a.d % 64 == 0 && blocks(64, 64) >= ROUTER_MFMA_MIN_TILES) {
+        dim3 grid((a.T + 63) / 64, (a.E + 63) / 64);
+        launch_kernel(router_mfma_kernel<AF>, grid, 512, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
+    } else if (a.d % 64 == 0 && blocks(64, 64) >= 512) router_gemm_tile<AF, 64, 64, 4, 4, 32>(a, st, kt);
     else if (a.d % 64 == 0 && blocks(32, 64) >= 512) router_gemm_tile<AF, 32, 64, 2, 4, 64>(a, st, kt);
     else if (a.d % 128 == 0) router_gemm_tile<AF, 16, 32, 1, 2, 128>(a, st, kt);
     else router_gemm_tile<AF, 16, 32, 1, 2, 64>(a, st, kt);

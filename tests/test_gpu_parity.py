@@ -291,6 +291,36 @@ def test_split_entry_points(torch_cuda, orc):
         assert H.rownorm_err(y2.cpu().numpy(), orc.combine(cfg, r_slot, r_shared)) < 1e-6
 
 
+@pytest.mark.parametrize("spec", [dict(T=4100, d=128, E=192, k=8, F=64, act="bf16", w="bf16"),
+                                  dict(T=2100, d=192, E=250, k=6, F=64, act="f32", w="f32",
+                                       score="sqrt_softplus", scale=1.5, bias="none")],
+                         ids=["bf16_T4100_E192", "f32_T2100_E250"])
+def test_router_matrix_cores(torch_cuda, orc, spec):
+    """Router shapes with at least 128 tiles of 64 x 64 (the fp64 matrix-core
+    kernel), with ragged token and expert tails: logits within one ulp, indices
+    and weights as the oracle's."""
+    import torch
+    import sparse_moe_layer_02_amd as moe
+    cfg = _custom(**spec)
+    T, E, k, d = cfg["T"], cfg["E"], cfg["k"], cfg["d"]
+    assert ((T + 63) // 64) * ((E + 63) // 64) >= 128 and (T % 64, E % 64) != (0, 0)
+    say("router", spec)
+    x = configs.gen_x(cfg)
+    wr = configs.gen_router(cfg)
+    bias = configs.gen_bias(cfg)
+    c = moe.config_from(cfg, path="prefill")
+    ws = moe.workspace(c)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(c, H.to_dev(x), H.to_dev(wr), H.to_dev(bias), logits, idx, w, ws)
+    torch.cuda.synchronize()
+    r_lg, r_idx, r_w = orc.route(cfg, x, wr, bias)
+    hist = H.check_routing(dict(logits=logits.cpu().numpy(), topk_idx=idx.cpu().numpy(),
+                                topk_w=w.cpu().numpy()), dict(logits=r_lg, topk_idx=r_idx, topk_w=r_w))
+    say("  ulp histograms", hist)
+
+
 def test_select_special_values(torch_cuda, orc):
     """NaN logits rank last, integer logits tie, and the compile-time
     256-expert top-k gives the same bits as the runtime-E kernel."""
