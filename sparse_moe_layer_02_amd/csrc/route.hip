@@ -326,6 +326,113 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// The same on a 16-token x 32-expert tile, for token counts whose 64 x 64 tiles
+// cannot fill the chip (c4: 32 of them): the eight wavefronts form four K
+// groups of two, group g taking the 64-column chunks g, g + 4, ...; each
+// wavefront owns one 16 x 16 block and alternates two accumulators, and the
+// groups' partial sums are added in a fixed order at the end (deterministic;
+// only the order of fp64 additions differs from the definition's).
+// ---------------------------------------------------------------------------
+template <int AF>
+__global__ __launch_bounds__(512) void router_mfma_split_kernel(const void* __restrict__ x,
+                                                                const float* __restrict__ wr, int T, int d,
+                                                                int E, float* __restrict__ logits) {
+    constexpr int TM = 16, TE = 32, KC = 64, KG = 4, GT = 128;  // GT threads per K group
+    constexpr int XW = AF == MOE_DT_BF16 ? KC / 2 : KC;
+    constexpr int XP = XW + 1, WP = KC + 1;
+    constexpr int XQ = TM * XW / 4, WQ = TE * KC / 4;  // 16-byte staging items per chunk
+    constexpr int XI = (XQ + GT - 1) / GT, WI = WQ / GT;
+    static_assert(WQ % GT == 0 && XQ % GT == 0, "staging shape");
+    __shared__ uint32_t xs[KG][2][TM * XP];
+    __shared__ float ws[KG][2][TE * WP];
+    __shared__ f64x4 red[KG - 1][2][WAVE];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    const int kg = wave / 2, blk = wave % 2, gtid = tid % GT;
+    const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
+    uint4 rx[XI];
+    float4 rw[WI];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int it = 0; it < XI; ++it) {
+            const int q = gtid + GT * it, r = q / (XW / 4), c = (q % (XW / 4)) * 4;
+            rx[it] = make_uint4(0, 0, 0, 0);
+            if (t0 + r < T) {
+                const uint32_t* row = AF == MOE_DT_BF16
+                    ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + (size_t)(t0 + r) * d + k0)
+                    : reinterpret_cast<const uint32_t*>(static_cast<const float*>(x) + (size_t)(t0 + r) * d + k0);
+                rx[it] = *reinterpret_cast<const uint4*>(row + c);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < WI; ++it) {
+            const int q = gtid + GT * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
+            rw[it] = e0 + r < E ? *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * d + k0 + c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto lstore = [&](int stg) {
+#pragma unroll
+        for (int it = 0; it < XI; ++it) {
+            const int q = gtid + GT * it, r = q / (XW / 4), c = (q % (XW / 4)) * 4;
+            uint32_t* dst = &xs[kg][stg][r * XP + c];
+            dst[0] = rx[it].x; dst[1] = rx[it].y; dst[2] = rx[it].z; dst[3] = rx[it].w;
+        }
+#pragma unroll
+        for (int it = 0; it < WI; ++it) {
+            const int q = gtid + GT * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
+            float* dst = &ws[kg][stg][r * WP + c];
+            dst[0] = rw[it].x; dst[1] = rw[it].y; dst[2] = rw[it].z; dst[3] = rw[it].w;
+        }
+    };
+    const int lr = lane % 16, lk = lane / 16;
+    auto xval = [&](int stg, int kk) -> double {
+        if (AF == MOE_DT_BF16) {
+            const uint32_t pair = xs[kg][stg][lr * XP + (kk >> 1)];
+            return (double)((kk & 1) ? bf16_hi(pair) : bf16_lo(pair));
+        }
+        return (double)__uint_as_float(xs[kg][stg][lr * XP + kk]);
+    };
+
+    f64x4 acc0 = f64x4{0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
+    const int nch = d / KC, rounds = (nch + KG - 1) / KG;
+    if (kg < nch) {
+        gload(kg * KC);
+        lstore(0);
+    }
+    __syncthreads();
+    for (int rd = 0; rd < rounds; ++rd) {
+        const int ch = rd * KG + kg, stg = rd & 1;
+        const bool have = ch < nch, have_next = ch + KG < nch;
+        if (have_next) gload((ch + KG) * KC);
+        if (have) {
+#pragma unroll
+            for (int ks = 0; ks < KC; ks += 8) {
+                const double a0 = xval(stg, ks + lk), a1 = xval(stg, ks + 4 + lk);
+                const double b0 = (double)ws[kg][stg][(16 * blk + lr) * WP + ks + lk];
+                const double b1 = (double)ws[kg][stg][(16 * blk + lr) * WP + ks + 4 + lk];
+                acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc1, 0, 0, 0);
+            }
+        }
+        if (have_next) lstore(stg ^ 1);
+        __syncthreads();
+    }
+    f64x4 acc = acc0 + acc1;
+    if (kg > 0) red[kg - 1][blk][lane] = acc;
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+        for (int g = 0; g < KG - 1; ++g) acc += red[g][blk][lane];
+        const int e = e0 + 16 * blk + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + lk + 4 * r;
+            if (t < T && e < E) logits[(size_t)t * E + e] = (float)acc[r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Top-k: one wavefront per token (topk_token in route_dev.h).
 // ---------------------------------------------------------------------------
 template <int KPL, int EFIX>
@@ -351,10 +458,10 @@ static void router_gemm_tile(const RouteArgs& a, hipStream_t st, const KTime& kt
                   a.logits);
 }
 
-// The matrix-core kernel from 128 tiles of 64 x 64 on (it runs one
-// workgroup per compute unit and cannot split K); below that the largest VALU
-// tile that still gives every compute unit two workgroups, the smallest when
-// none does (few tokens).
+// The matrix-core kernels from 128 tiles on: 64 x 64 tiles with the whole K
+// per workgroup, else 16 x 32 tiles with K split over four groups of
+// wavefronts; below that the largest VALU tile that still gives every compute
+// unit two workgroups, the smallest when none does.
 constexpr long ROUTER_MFMA_MIN_TILES = 128;
 template <int AF>
 static void router_gemm_launch(const RouteArgs& a, hipStream_t st, const KTime& kt) {
@@ -362,6 +469,9 @@ static void router_gemm_launch(const RouteArgs& a, hipStream_t st, const KTime& 
     if (a.d % 64 == 0 && blocks(64, 64) >= ROUTER_MFMA_MIN_TILES) {
         dim3 grid((a.T + 63) / 64, (a.E + 63) / 64);
         launch_kernel(router_mfma_kernel<AF>, grid, 512, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
+    } else if (a.d % 64 == 0 && blocks(16, 32) >= ROUTER_MFMA_MIN_TILES) {
+        dim3 grid((a.T + 15) / 16, (a.E + 31) / 32);
+        launch_kernel(router_mfma_split_kernel<AF>, grid, 512, st, kt, a.x, a.wr, a.T, a.d, a.E, a.logits);
     } else if (a.d % 64 == 0 && blocks(64, 64) >= 512) router_gemm_tile<AF, 64, 64, 4, 4, 32>(a, st, kt);
     else if (a.d % 64 == 0 && blocks(32, 64) >= 512) router_gemm_tile<AF, 32, 64, 2, 4, 64>(a, st, kt);
     else if (a.d % 128 == 0) router_gemm_tile<AF, 16, 32, 1, 2, 128>(a, st, kt);

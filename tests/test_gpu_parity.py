@@ -293,17 +293,22 @@ def test_split_entry_points(torch_cuda, orc):
 
 @pytest.mark.parametrize("spec", [dict(T=4100, d=128, E=192, k=8, F=64, act="bf16", w="bf16"),
                                   dict(T=2100, d=192, E=250, k=6, F=64, act="f32", w="f32",
-                                       score="sqrt_softplus", scale=1.5, bias="none")],
-                         ids=["bf16_T4100_E192", "f32_T2100_E250"])
+                                       score="sqrt_softplus", scale=1.5, bias="none"),
+                                  dict(T=1000, d=320, E=72, k=4, F=64, act="bf16", w="bf16"),
+                                  dict(T=1100, d=128, E=64, k=8, F=64, act="f32", w="f32")],
+                         ids=["bf16_T4100_E192", "f32_T2100_E250", "split_bf16_T1000_E72_d320",
+                              "split_f32_T1100_E64_d128"])
 def test_router_matrix_cores(torch_cuda, orc, spec):
-    """Router shapes with at least 128 tiles of 64 x 64 (the fp64 matrix-core
-    kernel), with ragged token and expert tails: logits within one ulp, indices
-    and weights as the oracle's."""
+    """Router shapes on the fp64 matrix-core kernels (at least 128 tiles of
+    64 x 64, or of 16 x 32 with K split over four groups of wavefronts, five
+    and two 64-column chunks for the split cases), with ragged token and expert
+    tails: logits within one ulp, indices and weights as the oracle's."""
     import torch
     import sparse_moe_layer_02_amd as moe
     cfg = _custom(**spec)
     T, E, k, d = cfg["T"], cfg["E"], cfg["k"], cfg["d"]
-    assert ((T + 63) // 64) * ((E + 63) // 64) >= 128 and (T % 64, E % 64) != (0, 0)
+    assert (((T + 63) // 64) * ((E + 63) // 64) >= 128 or ((T + 15) // 16) * ((E + 31) // 32) >= 128) \
+        and (T % 64, E % 64) != (0, 0)
     say("router", spec)
     x = configs.gen_x(cfg)
     wr = configs.gen_router(cfg)
