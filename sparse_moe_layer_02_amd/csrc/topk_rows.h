@@ -10,8 +10,9 @@ constexpr int TOPK_ROWS_MAX_N = 65536;
 struct TopkRowsArgs {
     const float* scores;  // [rows, n]
     int rows, n, k;
-    int32_t* idx;  // [rows, k], ascending candidate index
-    float* vals;   // [rows, k] or null
+    int32_t* idx;     // [rows, k], ascending candidate index
+    float* vals;      // [rows, k] or null
+    int sample_rank;  // rank of the sampled threshold (0: no sampled pass); set by launch_topk_rows
 };
 hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t st, const KTime& kt = KTime());
 int topk_rows_threads(int n);  // workgroup size of the launch that takes n candidates

@@ -29,6 +29,9 @@
 //      wavefront plus its rank in the chunk's ballot; chosen candidates wait in
 //      a ring in LDS private to the wavefront and leave 64 at a time, in one
 //      coalesced store per output array.
+#include <cmath>
+#include <type_traits>
+
 #include "topk_rows.h"
 
 namespace moe {
@@ -68,6 +71,8 @@ struct TkState {
 // no workgroup barrier), and every 64 of them leave in one coalesced store per
 // output array.  The stores go through buffer descriptors of k entries.
 constexpr int TK_RING = 128;
+constexpr int TK_SAMPLES = 256;          // keys sampled per row for the threshold
+constexpr int TK_CAND_PER_THREAD = 8;    // LDS room for candidates per thread
 
 template <int NPT, bool CUT, bool SPECIAL>
 __device__ __forceinline__ void emit_wave(const uint32_t* key, uint32_t mask, uint32_t pc, uint32_t prefix,
@@ -137,6 +142,12 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
     __shared__ uint32_t wtot[3][WAVES];   // per wavefront: keys above, equal, any NaN / -0
     __shared__ uint32_t ring[WAVES][2][TK_RING];  // per wavefront: chosen indices and values on their way out
     __shared__ TkState st;
+    // the sampled pass runs on rows of 64 keys per thread only (see topk_rows_sample_rank)
+    constexpr bool SAMPLED = NPT == 64;
+    constexpr int CAP = SAMPLED ? TK_CAND_PER_THREAD * THREADS : 1;  // candidates the sampled pass can hold
+    __shared__ uint32_t cand_key[CAP], cand_idx[CAP];
+    __shared__ uint32_t samp[TK_SAMPLES];
+    __shared__ uint32_t wmax[WAVES], wcnt[WAVES], fst[2];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_index();
     const int n = a.n, k = a.k;
@@ -171,70 +182,227 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
         for (int j = 0; j < NPT; ++j) key[j] = lane < n - (base0 + j * WAVE) ? key[j] : 0u;
     }
     if (lane == 0) wtot[2][wave] = special != 0ull ? 1u : 0u;
+    // Samples for the threshold: the middle chunk of every wavefront, every
+    // LSTEP-th lane (TK_SAMPLES in all, spread over the row); and the row's
+    // largest key.
+    constexpr int SPW = TK_SAMPLES / WAVES, LSTEP = WAVE / SPW;
+    static_assert(SPW * WAVES == TK_SAMPLES && LSTEP * SPW == WAVE, "sample layout");
+    const bool sampled = SAMPLED && a.sample_rank > 0;
+    if (sampled) {
+        if (lane % LSTEP == 0) samp[wave * SPW + lane / LSTEP] = key[NPT / 2];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) mx = max(mx, key[j]);
+        mx = wave_max_u32(mx);
+        if (lane == 0) wmax[wave] = mx;
+    }
     __syncthreads();
 
     // ---- radix select ----------------------------------------------------
-    uint32_t prefix = 0, mask = 0, need = (uint32_t)k;
+    // Passes of 8 bits from bit position shift down (the last one aligned at
+    // bit 0; a pass may re-read bits already resolved, which are constant among
+    // the matching keys).  count(mask, prefix, shift) adds every key with
+    // key & mask == prefix to the histogram.  On return st holds the threshold
+    // (prefix under mask) and the number of keys at it that are still needed.
     uint32_t* my_col = &hist[lane % COLS];
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    // cols: the counts are spread over COLS columns per bin (keys of the whole
+    // row, whose top bytes collide); otherwise one counter per bin in the first
+    // 256 words (the few candidates of the sampled pass, spread over the bins).
+    auto radix = [&](auto&& count, uint32_t prefix, uint32_t mask, int shift, uint32_t need, auto cols_tag) {
+        constexpr bool cols = decltype(cols_tag)::value;
+        for (;;) {
+            count(mask, prefix, shift);
+            __syncthreads();
+            if constexpr (!cols) {
+                if (tid < 256) {
+                    tot[255 - tid] = hist[tid];
+                    hist[tid] = 0;
+                }
+            } else {
+                const int b = tid / S, s = tid % S;
+                uint32_t c = 0;
+                // not unrolled fully: the R column addresses would stay live in
+                // registers for the whole kernel
+#pragma unroll 4
+                for (int i = 0; i < R; ++i) {
+                    const int l = s * R + ((i + b) % R);  // distinct columns across a wavefront: no bank conflicts
+                    c += hist[b * COLS + l];
+                    hist[b * COLS + l] = 0;
+                }
+#pragma unroll
+                for (int o = 1; o < S; o <<= 1) c += __shfl_xor(c, o);
+                if (s == 0) tot[255 - b] = c;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                const uint32_t c0 = tot[4 * lane], c1 = tot[4 * lane + 1], c2 = tot[4 * lane + 2],
+                               c3 = tot[4 * lane + 3];
+                const uint32_t sum = c0 + c1 + c2 + c3;
+                const uint32_t incl = wave_incl_scan_u32(sum);
+                const uint64_t hit = __ballot(incl >= need);
+                if (hit != 0ull && lane == __ffsll((unsigned long long)hit) - 1) {
+                    uint32_t above = incl - sum, c = c0;
+                    int r = 0;
+                    if (above + c0 < need) {
+                        above += c0, c = c1, r = 1;
+                        if (above + c1 < need) {
+                            above += c1, c = c2, r = 2;
+                            if (above + c2 < need) above += c2, c = c3, r = 3;
+                        }
+                    }
+                    const uint32_t b = 255u - (uint32_t)(4 * lane + r);
+                    const uint32_t rem = need - above;
+                    st.prefix = prefix | (b << shift);
+                    st.mask = mask | (255u << shift);
+                    st.need = rem;
+                    // Padding keys (0) are counted only while the prefix is 0, i.e. in
+                    // the lowest bin; the search never stops on a zero prefix, so the
+                    // final threshold is never matched by padding.
+                    st.done = ((rem == c && st.prefix != 0u) || shift == 0) ? 1u : 0u;
+                } else if (hit == 0ull && lane == 0) {
+                    // unreachable while k <= valid keys; keeps the exit uniform
+                    st.prefix = prefix, st.mask = mask, st.need = need, st.done = 1u;
+                }
+            }
+            __syncthreads();
+            prefix = __builtin_amdgcn_readfirstlane(st.prefix);
+            mask = __builtin_amdgcn_readfirstlane(st.mask);
+            need = __builtin_amdgcn_readfirstlane(st.need);
+            if (__builtin_amdgcn_readfirstlane(st.done)) break;
+            shift = max(shift - 8, 0);
+        }
+    };
+    const bool with_vals = a.vals != nullptr;
+    const __amdgpu_buffer_rsrc_t out_idx =
+        __builtin_amdgcn_make_buffer_rsrc(a.idx + (size_t)blockIdx.x * k, (short)0, k * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t out_vals = __builtin_amdgcn_make_buffer_rsrc(
+        with_vals ? (void*)(a.vals + (size_t)blockIdx.x * k) : (void*)(a.idx + (size_t)blockIdx.x * k), (short)0,
+        k * 4, 0x00020000);
+
+    // ---- sampled pass ------------------------------------------------------
+    // T = the sample_rank-th largest sample.  If between k and CAP keys are
+    // >= T, the chosen candidates are all among them (every key below T has at
+    // least k keys above it): they are compacted in index order into LDS and
+    // the exact selection and the output run on them alone.  Otherwise (an
+    // unlucky sample, heavy ties) the row takes the full radix path below.
+    if constexpr (SAMPLED) if (sampled) {
+        if (wave == 0) {
+            uint32_t s0 = samp[4 * lane], s1 = samp[4 * lane + 1], s2 = samp[4 * lane + 2], s3 = samp[4 * lane + 3];
+            auto cs = [](uint32_t& x, uint32_t& y) { const uint32_t h = max(x, y), l = min(x, y); x = h; y = l; };
+            cs(s0, s1); cs(s2, s3); cs(s0, s2); cs(s1, s3); cs(s1, s2);  // each lane's four, descending
+            uint32_t tv = 0;
+            for (int it = 0; it < a.sample_rank; ++it) {  // take the largest head sample_rank times
+                const uint32_t m = wave_max_u32(s0);
+                const uint64_t who = __ballot(s0 == m);
+                if (lane == __ffsll((unsigned long long)who) - 1) s0 = s1, s1 = s2, s2 = s3, s3 = 0u;
+                tv = m;
+            }
+            const uint32_t km = wave_max_u32(lane < WAVES ? wmax[lane] : 0u);
+            if (lane == 0) fst[0] = tv, fst[1] = km;
+        }
+        __syncthreads();
+        const uint32_t T = __builtin_amdgcn_readfirstlane(fst[0]), KMAX = __builtin_amdgcn_readfirstlane(fst[1]);
+        uint32_t c_w = 0;
 #pragma unroll
         for (int j = 0; j < NPT; ++j) {
-            const uint32_t kk = key[j];
-            if ((kk & mask) == prefix) atomicAdd(my_col + ((kk >> shift) & 255u) * COLS, 1u);
+            c_w += (uint32_t)__popcll(__ballot(key[j] >= T));
+            __builtin_amdgcn_sched_barrier(0);
         }
+        asm volatile("" : "+s"(c_w));
+        if (lane == 0) wcnt[wave] = c_w;
         __syncthreads();
-        {
-            const int b = tid / S, s = tid % S;
-            uint32_t c = 0;
-            // not unrolled fully: the R column addresses would stay live in
-            // registers for the whole kernel
-#pragma unroll 4
-            for (int i = 0; i < R; ++i) {
-                const int l = s * R + ((i + b) % R);  // distinct columns across a wavefront: no bank conflicts
-                c += hist[b * COLS + l];
-                hist[b * COLS + l] = 0;
-            }
+        const uint32_t wc = lane < WAVES ? wcnt[lane] : 0u;
+        const uint32_t C = wave_sum_u32(wc);
+        if (T != 0u && C >= (uint32_t)k && C <= (uint32_t)CAP) {
+            uint32_t run = wave_sum_u32(lane < wave ? wc : 0u);
+            uint32_t TC = T;
+            asm volatile("" : "+s"(TC));  // the tests are made again, not held in scalar registers since the count
 #pragma unroll
-            for (int o = 1; o < S; o <<= 1) c += __shfl_xor(c, o);
-            if (s == 0) tot[255 - b] = c;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const uint32_t c0 = tot[4 * lane], c1 = tot[4 * lane + 1], c2 = tot[4 * lane + 2],
-                           c3 = tot[4 * lane + 3];
-            const uint32_t sum = c0 + c1 + c2 + c3;
-            const uint32_t incl = wave_incl_scan_u32(sum);
-            const uint64_t hit = __ballot(incl >= need);
-            if (hit != 0ull && lane == __ffsll((unsigned long long)hit) - 1) {
-                uint32_t above = incl - sum, c = c0;
-                int r = 0;
-                if (above + c0 < need) {
-                    above += c0, c = c1, r = 1;
-                    if (above + c1 < need) {
-                        above += c1, c = c2, r = 2;
-                        if (above + c2 < need) above += c2, c = c3, r = 3;
+            for (int j = 0; j < NPT; ++j) {
+                const bool c = key[j] >= TC;
+                const uint64_t m = __ballot(c);
+                const uint32_t pos = (uint32_t)__builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, run));
+                if (c) {
+                    cand_key[pos] = key[j];
+                    cand_idx[pos] = (uint32_t)(base0 + j * WAVE + lane);
+                }
+                run += (uint32_t)__popcll(m);
+            }
+            __syncthreads();
+            // Exact selection among the candidates, which lie in [T, KMAX]: the
+            // bits above the highest one where T and KMAX differ are resolved.
+            uint32_t M = 0xFFFFFFFFu, P = T, NEED = (uint32_t)k;
+            const uint32_t diff = T ^ KMAX;
+            if (diff != 0u) {
+                const int hb = 31 - __builtin_clz(diff);
+                const uint32_t m0 = ~((2u << hb) - 1u);  // 0 when hb = 31
+                radix(
+                    [&](uint32_t mask, uint32_t prefix, int shift) {
+                        for (int i = tid; i < (int)C; i += THREADS) {
+                            const uint32_t kk = cand_key[i];
+                            if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+                        }
+                    },
+                    T & m0, m0, max(hb - 7, 0), (uint32_t)k, std::false_type());
+                M = __builtin_amdgcn_readfirstlane(st.mask);
+                P = __builtin_amdgcn_readfirstlane(st.prefix);
+                NEED = __builtin_amdgcn_readfirstlane(st.need);
+            }
+            // Output: thread t takes the candidates [t * per, (t + 1) * per);
+            // block scans of its counts above and at the threshold give its
+            // first output position.
+            const int per = ((int)C + THREADS - 1) / THREADS;
+            const int i0 = min(tid * per, (int)C), i1 = min(i0 + per, (int)C);
+            uint32_t g = 0, e = 0;
+            for (int i = i0; i < i1; ++i) {
+                const uint32_t km = cand_key[i] & M;
+                g += km > P ? 1u : 0u;
+                e += km == P ? 1u : 0u;
+            }
+            const uint32_t gi = wave_incl_scan_u32(g), ei = wave_incl_scan_u32(e);
+            if (lane == WAVE - 1) wtot[0][wave] = gi, wtot[1][wave] = ei;
+            __syncthreads();
+            const bool row_special = __ballot(lane < WAVES && wtot[2][lane] != 0u) != 0ull;
+            uint32_t g_before = wave_sum_u32(lane < wave && lane < WAVES ? wtot[0][lane] : 0u) + gi - g;
+            uint32_t e_before = wave_sum_u32(lane < wave && lane < WAVES ? wtot[1][lane] : 0u) + ei - e;
+            for (int i = i0; i < i1; ++i) {
+                const uint32_t kk = cand_key[i], km = kk & M;
+                int off = -1;
+                if (km > P) {
+                    off = (int)((g_before + min(e_before, NEED)) * 4u);
+                    ++g_before;
+                } else if (km == P) {
+                    if (e_before < NEED) off = (int)((g_before + e_before) * 4u);
+                    ++e_before;
+                }
+                if (off >= 0) {
+                    const uint32_t ci = cand_idx[i];
+                    __builtin_amdgcn_raw_buffer_store_b32(ci, out_idx, off, 0, 0);
+                    if (with_vals) {
+                        float v = key_value(kk);
+                        if (row_special && (kk == 0x80000000u || kk == 1u))
+                            v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(ci * 4u), 0, 0));
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_vals, off, 0, 0);
                     }
                 }
-                const uint32_t b = 255u - (uint32_t)(4 * lane + r);
-                const uint32_t rem = need - above;
-                st.prefix = prefix | (b << shift);
-                st.mask = mask | (255u << shift);
-                st.need = rem;
-                // Padding keys (0) are counted only while the prefix is 0, i.e. in
-                // the lowest bin; the search never stops on a zero prefix, so the
-                // final threshold is never matched by padding.
-                st.done = ((rem == c && st.prefix != 0u) || shift == 0) ? 1u : 0u;
-            } else if (hit == 0ull && lane == 0) {
-                // unreachable while k <= valid keys; keeps the exit uniform
-                st.prefix = prefix, st.mask = mask, st.need = need, st.done = 1u;
             }
+            return;
         }
-        __syncthreads();
-        prefix = __builtin_amdgcn_readfirstlane(st.prefix);
-        mask = __builtin_amdgcn_readfirstlane(st.mask);
-        need = __builtin_amdgcn_readfirstlane(st.need);
-        if (__builtin_amdgcn_readfirstlane(st.done)) break;
     }
+
+    // ---- full radix path over the keys in registers ------------------------
+    radix(
+        [&](uint32_t mask, uint32_t prefix, int shift) {
+#pragma unroll
+            for (int j = 0; j < NPT; ++j) {
+                const uint32_t kk = key[j];
+                if ((kk & mask) == prefix) atomicAdd(my_col + ((kk >> shift) & 255u) * COLS, 1u);
+            }
+        },
+        0u, 0u, 24, (uint32_t)k, std::true_type());
+    const uint32_t prefix = __builtin_amdgcn_readfirstlane(st.prefix), mask = __builtin_amdgcn_readfirstlane(st.mask),
+                   need = __builtin_amdgcn_readfirstlane(st.need);
 
     // ---- output in index order --------------------------------------------
     // Chosen: key & mask > prefix (all of them), and the first `need` keys with
@@ -263,12 +431,6 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
     uint32_t M = mask, P = prefix, NEED = need;
     asm volatile("" : "+s"(M), "+s"(P), "+s"(NEED));
     const uint32_t run = g_base + min(e_base, NEED);  // chosen candidates before this wavefront
-    const bool with_vals = a.vals != nullptr;
-    const __amdgpu_buffer_rsrc_t out_idx =
-        __builtin_amdgcn_make_buffer_rsrc(a.idx + (size_t)blockIdx.x * k, (short)0, k * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t out_vals = __builtin_amdgcn_make_buffer_rsrc(
-        with_vals ? (void*)(a.vals + (size_t)blockIdx.x * k) : (void*)(a.idx + (size_t)blockIdx.x * k), (short)0,
-        k * 4, 0x00020000);
     const bool all_eq = e_base + e_w <= NEED, no_eq = e_base >= NEED;
     if (all_eq || no_eq) {
         if (no_eq && P == 0xFFFFFFFFu) return;  // nothing above the largest key: no output here
@@ -309,9 +471,30 @@ int topk_rows_npt(int n) {
     return npt;
 }
 
-hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t st, const KTime& kt) {
+// Rank of the sampled threshold among the TK_SAMPLES samples: the expected
+// number of samples above the k-th largest key plus six standard deviations
+// and four, so that fewer than k keys reach it only for very unusual rows; 0
+// (no sampled pass) when the expected number of candidates would not fit
+// comfortably in the LDS room for them, and for rows of up to 32768 keys: with
+// 32 keys per thread the radix passes over all keys cost about what the
+// sampled pass's threshold, compaction and selection cost (measured on the
+// 512 x 32768 indexer workload), while with 64 keys per thread each full pass
+// costs twice as much and the sampled pass wins (one 65536-key row: 25.7 ->
+// 19 us).
+int topk_rows_sample_rank(int n, int k) {
+    if (topk_rows_npt(n) < 64) return 0;
+    const double kf = (double)k * TK_SAMPLES / n;
+    const int r = (int)std::ceil(kf + 6.0 * std::sqrt(kf) + 4.0);
+    const double expect = (double)r * n / TK_SAMPLES;
+    if (r > TK_SAMPLES / 2 || expect > 0.7 * TK_CAND_PER_THREAD * topk_rows_threads(n)) return 0;
+    return r;
+}
+
+hipError_t launch_topk_rows(const TopkRowsArgs& a_in, hipStream_t st, const KTime& kt) {
+    TopkRowsArgs a = a_in;
     if (a.rows == 0) return hipSuccess;
     if (a.rows < 0 || a.n < 1 || a.n > TOPK_ROWS_MAX_N || a.k < 1 || a.k > a.n) return hipErrorInvalidValue;
+    a.sample_rank = topk_rows_sample_rank(a.n, a.k);
     const int npt = topk_rows_npt(a.n);
     if (topk_rows_threads(a.n) == 1024) {
         if (npt == 32) return launch_shape<1024, 32>(a, st, kt);

@@ -66,10 +66,14 @@ def check(dev, orc, scores, k, label, with_vals=True):
         assert np.array_equal(gv.view(np.uint32), want_vals.view(np.uint32)), label
 
 
-# (n, k): every launch shape, tails, k at both ends
+# (n, k): every launch shape, tails, k at both ends; the long rows with small k
+# take the sampled pass when their sample is good (random and ramp rows) and
+# the full radix path otherwise (constant, signed-zero and few-valued rows)
 SHAPES = [(1, 1), (7, 7), (64, 5), (300, 17), (512, 512), (513, 100), (1000, 999), (2048, 64),
           (3000, 300), (4097, 1024), (8192, 8192), (16384, 2048), (16385, 1024), (20000, 512), (32768, 1),
-          (32769, 4096), (50000, 2048), (65536, 65536)]
+          (32769, 4096), (50000, 2048), (65536, 65536),
+          # rows of more than 32768 keys with k small enough for the sampled pass
+          (40000, 512), (65536, 700), (65536, 1200)]
 
 
 @pytest.mark.parametrize("n,k", SHAPES, ids=["n%d_k%d" % s for s in SHAPES])
