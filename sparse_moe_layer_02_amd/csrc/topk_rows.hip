@@ -483,9 +483,11 @@ int topk_rows_npt(int n) {
 // 19 us).
 int topk_rows_sample_rank(int n, int k) {
     if (topk_rows_npt(n) < 64) return 0;
-    const double kf = (double)k * TK_SAMPLES / n;
+    // the samples are spread over the workgroup's key slots, those past n being padding
+    const double slots = (double)topk_rows_threads(n) * topk_rows_npt(n);
+    const double kf = (double)k * TK_SAMPLES / slots;
     const int r = (int)std::ceil(kf + 6.0 * std::sqrt(kf) + 4.0);
-    const double expect = (double)r * n / TK_SAMPLES;
+    const double expect = (double)r * slots / TK_SAMPLES;
     if (r > TK_SAMPLES / 2 || expect > 0.7 * TK_CAND_PER_THREAD * topk_rows_threads(n)) return 0;
     return r;
 }
