@@ -42,8 +42,10 @@ __device__ __forceinline__ void st16(uint8_t* p, u32x4 v) { *reinterpret_cast<u3
 // a block of M tiles x NG N tiles: each weight tile is read by the M tiles of
 // its expert and each A tile (rows of x or h) by the group's N tiles, mostly
 // from that XCD's L2.  NG = 4 pays off for tiles of 128 rows or more (experts
-// with many rows); with 64-row tiles (few rows per expert, bandwidth-bound)
-// NG = 1 streams best.
+// with many rows).  With 64-row tiles (few rows per expert, bandwidth-bound)
+// every weight tile is read by one M tile anyway, and NG = 16 lets the N
+// tiles that share an activation tile run side by side (about 2-3% faster
+// than NG = 1 at 512 tokens, bf16 and int8 weights).
 constexpr int N_XCD = 8;
 
 template <int NG>
