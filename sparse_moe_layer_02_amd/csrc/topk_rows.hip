@@ -73,6 +73,7 @@ struct TkState {
 constexpr int TK_RING = 128;
 constexpr int TK_SAMPLES = 256;          // keys sampled per row for the threshold
 constexpr int TK_CAND_PER_THREAD = 8;    // LDS room for candidates per thread
+constexpr int TK_BIN_BITS = 12, TK_BINS = 1 << TK_BIN_BITS;  // bins of the candidates' counting pass
 
 template <int NPT, bool CUT, bool SPECIAL>
 __device__ __forceinline__ void emit_wave(const uint32_t* key, uint32_t mask, uint32_t pc, uint32_t prefix,
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
     // the sampled pass runs on rows of 64 keys per thread only (see topk_rows_sample_rank)
     constexpr bool SAMPLED = NPT == 64;
     constexpr int CAP = SAMPLED ? TK_CAND_PER_THREAD * THREADS : 1;  // candidates the sampled pass can hold
+    static_assert(TK_BINS % THREADS == 0 && TK_BINS <= 256 * COLS && TK_SAMPLES >= WAVE, "candidate bins");
     __shared__ uint32_t cand_key[CAP], cand_idx[CAP];
     __shared__ uint32_t samp[TK_SAMPLES];
     __shared__ uint32_t wmax[WAVES], wcnt[WAVES], fst[2];
@@ -287,18 +289,44 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
     // unlucky sample, heavy ties) the row takes the full radix path below.
     if constexpr (SAMPLED) if (sampled) {
         if (wave == 0) {
-            uint32_t s0 = samp[4 * lane], s1 = samp[4 * lane + 1], s2 = samp[4 * lane + 2], s3 = samp[4 * lane + 3];
-            auto cs = [](uint32_t& x, uint32_t& y) { const uint32_t h = max(x, y), l = min(x, y); x = h; y = l; };
-            cs(s0, s1); cs(s2, s3); cs(s0, s2); cs(s1, s3); cs(s1, s2);  // each lane's four, descending
-            uint32_t tv = 0;
-            for (int it = 0; it < a.sample_rank; ++it) {  // take the largest head sample_rank times
-                const uint32_t m = wave_max_u32(s0);
-                const uint64_t who = __ballot(s0 == m);
-                if (lane == __ffsll((unsigned long long)who) - 1) s0 = s1, s1 = s2, s2 = s3, s3 = 0u;
-                tv = m;
+            // T: two 8-bit radix steps over the samples (one wavefront, four
+            // samples per lane, the histogram in tot), which find the 16-bit
+            // prefix of the sample_rank-th largest sample; T is the smallest key
+            // with that prefix, so at least sample_rank samples are >= T.
+            uint32_t sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = samp[4 * lane + i];
+            uint32_t prefix = 0, mask = 0, need = (uint32_t)a.sample_rank;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                const int shift = 24 - 8 * pass;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[4 * lane + i] = 0u;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((sv[i] & mask) == prefix) atomicAdd(&tot[(sv[i] >> shift) & 255u], 1u);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                const uint32_t c0 = tot[255 - 4 * lane], c1 = tot[254 - 4 * lane], c2 = tot[253 - 4 * lane],
+                               c3 = tot[252 - 4 * lane];  // lane l: bins 255 - 4l down to 252 - 4l
+                const uint32_t sum = c0 + c1 + c2 + c3, incl = wave_incl_scan_u32(sum);
+                uint32_t above = incl - sum;
+                int r = 0;
+                if (above + c0 < need) {
+                    above += c0, r = 1;
+                    if (above + c1 < need) {
+                        above += c1, r = 2;
+                        if (above + c2 < need) above += c2, r = 3;
+                    }
+                }
+                const int L = __ffsll((unsigned long long)__ballot(incl >= need)) - 1;  // exists: need <= matching samples
+                const uint32_t b = 255u - (uint32_t)(4 * L + __builtin_amdgcn_readlane(r, L));
+                need -= (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+                prefix |= b << shift;
+                mask |= 255u << shift;
             }
             const uint32_t km = wave_max_u32(lane < WAVES ? wmax[lane] : 0u);
-            if (lane == 0) fst[0] = tv, fst[1] = km;
+            if (lane == 0) fst[0] = prefix, fst[1] = km;
         }
         __syncthreads();
         const uint32_t T = __builtin_amdgcn_readfirstlane(fst[0]), KMAX = __builtin_amdgcn_readfirstlane(fst[1]);
@@ -330,24 +358,85 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
                 run += (uint32_t)__popcll(m);
             }
             __syncthreads();
-            // Exact selection among the candidates, which lie in [T, KMAX]: the
-            // bits above the highest one where T and KMAX differ are resolved.
-            uint32_t M = 0xFFFFFFFFu, P = T, NEED = (uint32_t)k;
-            const uint32_t diff = T ^ KMAX;
-            if (diff != 0u) {
-                const int hb = 31 - __builtin_clz(diff);
-                const uint32_t m0 = ~((2u << hb) - 1u);  // 0 when hb = 31
-                radix(
-                    [&](uint32_t mask, uint32_t prefix, int shift) {
-                        for (int i = tid; i < (int)C; i += THREADS) {
-                            const uint32_t kk = cand_key[i];
-                            if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+            // Exact selection among the candidates, which lie in [T, KMAX].  One
+            // pass counts them in TK_BINS bins of 2^sh consecutive keys from T;
+            // the bin where the count from the top reaches k holds the k-th key.
+            // If it is needed whole, every key from its lower end is chosen;
+            // else its keys (usually a handful) are gathered and one wavefront
+            // takes the remaining rank among them.  A crossing bin of more than
+            // 64 keys (dense ties) runs 8-bit radix passes on the candidates.
+            uint32_t M = 0xFFFFFFFFu, P = T, NEED = (uint32_t)k;  // all candidates equal: the first k
+            if (T != KMAX) {
+                const uint32_t span = KMAX - T;
+                const int sh = max(0, 32 - __builtin_clz(span) - TK_BIN_BITS);  // (span >> sh) < TK_BINS
+                for (int i = tid; i < (int)C; i += THREADS) atomicAdd(&hist[(cand_key[i] - T) >> sh], 1u);
+                __syncthreads();
+                constexpr int BPT = TK_BINS / THREADS;  // bins per thread, highest first
+                uint32_t cb[BPT], csum = 0;
+#pragma unroll
+                for (int q = 0; q < BPT; ++q) {
+                    const int bin = TK_BINS - 1 - BPT * tid - q;
+                    cb[q] = hist[bin];
+                    hist[bin] = 0u;  // (zero again for the radix fallback)
+                    csum += cb[q];
+                }
+                const uint32_t ci = wave_incl_scan_u32(csum);
+                if (lane == WAVE - 1) wcnt[wave] = ci;
+                __syncthreads();
+                const uint32_t cincl = wave_sum_u32(lane < wave && lane < WAVES ? wcnt[lane] : 0u) + ci;
+                if (cincl - csum < (uint32_t)k && cincl >= (uint32_t)k) {  // exactly one thread
+                    uint32_t above = cincl - csum;
+                    int q = 0;
+                    while (q < BPT - 1 && above + cb[q] < (uint32_t)k) above += cb[q++];
+                    st.prefix = (uint32_t)(TK_BINS - 1 - BPT * tid - q);  // the crossing bin
+                    st.need = (uint32_t)k - above;                       // keys still needed from it
+                    st.mask = cb[q];                                      // keys in it
+                    st.done = 0u;                                         // gathered so far
+                }
+                __syncthreads();
+                const uint32_t bstar = __builtin_amdgcn_readfirstlane(st.prefix), rem = __builtin_amdgcn_readfirstlane(st.need),
+                               cbin = __builtin_amdgcn_readfirstlane(st.mask);
+                const uint32_t lo = T + (bstar << sh);  // smallest key of the crossing bin
+                if (rem == cbin) {
+                    M = 0xFFFFFFFFu, P = lo - 1u, NEED = 0u;  // chosen: key >= lo (lo >= T >= 1)
+                } else if (cbin <= (uint32_t)WAVE) {
+                    for (int i = tid; i < (int)C; i += THREADS) {
+                        const uint32_t kk = cand_key[i];
+                        if (((kk - T) >> sh) == bstar) samp[atomicAdd(&st.done, 1u)] = kk;
+                    }
+                    __syncthreads();
+                    if (wave == 0) {
+                        // the rem-th largest of the bin's keys, taken one by one
+                        uint32_t v = lane < (int)cbin ? samp[lane] : 0u, kth = 0u;
+                        const uint32_t mine = v;
+                        for (uint32_t it = 0; it < rem; ++it) {
+                            kth = wave_max_u32(v);
+                            const uint64_t who = __ballot(v == kth);
+                            if (lane == __ffsll((unsigned long long)who) - 1) v = 0u;
                         }
-                    },
-                    T & m0, m0, max(hb - 7, 0), (uint32_t)k, std::false_type());
-                M = __builtin_amdgcn_readfirstlane(st.mask);
-                P = __builtin_amdgcn_readfirstlane(st.prefix);
-                NEED = __builtin_amdgcn_readfirstlane(st.need);
+                        const uint32_t greater = (uint32_t)__popcll(__ballot(lane < (int)cbin && mine > kth));
+                        if (lane == 0) st.prefix = kth, st.need = rem - greater;
+                    }
+                    __syncthreads();
+                    M = 0xFFFFFFFFu;
+                    P = __builtin_amdgcn_readfirstlane(st.prefix);
+                    NEED = __builtin_amdgcn_readfirstlane(st.need);
+                } else {
+                    const uint32_t diff = T ^ KMAX;
+                    const int hb = 31 - __builtin_clz(diff);
+                    const uint32_t m0 = ~((2u << hb) - 1u);  // 0 when hb = 31
+                    radix(
+                        [&](uint32_t mask, uint32_t prefix, int shift) {
+                            for (int i = tid; i < (int)C; i += THREADS) {
+                                const uint32_t kk = cand_key[i];
+                                if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+                            }
+                        },
+                        T & m0, m0, max(hb - 7, 0), (uint32_t)k, std::false_type());
+                    M = __builtin_amdgcn_readfirstlane(st.mask);
+                    P = __builtin_amdgcn_readfirstlane(st.prefix);
+                    NEED = __builtin_amdgcn_readfirstlane(st.need);
+                }
             }
             // Output: thread t takes the candidates [t * per, (t + 1) * per);
             // block scans of its counts above and at the threshold give its
