@@ -138,16 +138,25 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
     constexpr int R = COLS / S;       // columns each of them sums
     static_assert(S >= 1 && R * S == COLS && WAVES <= WAVE, "launch shape");
 
-    __shared__ uint32_t hist[256 * COLS];  // [bin][column]
+    // One LDS region serves the two paths, which never run in the same
+    // workgroup at once (the sampled pass writes nothing here before it is
+    // sure to finish the row): the full path's histogram and output rings, or
+    // the sampled pass's TK_BINS counters (the histogram's first words, zero
+    // as the full path needs them), candidate keys and 16-bit candidate
+    // indices (n <= 65536).  Small enough for two 1024-thread workgroups of
+    // 32 keys per thread on one CU.
+    constexpr bool SAMPLED = THREADS == 1024 && NPT >= 32;  // rows of 32 or 64 keys per thread (see topk_rows_sample_rank)
+    constexpr int CAP = SAMPLED ? TK_CAND_PER_THREAD * THREADS : 0;  // candidates the sampled pass can hold
+    static_assert(TK_BINS % THREADS == 0 && TK_BINS <= 256 * COLS && TK_SAMPLES >= WAVE, "candidate bins");
+    constexpr int FULL_WORDS = 256 * COLS + WAVES * 2 * TK_RING, SAMPLED_WORDS = TK_BINS + CAP + CAP / 2;
+    __shared__ uint32_t lds[FULL_WORDS > SAMPLED_WORDS ? FULL_WORDS : SAMPLED_WORDS];
+    uint32_t* const hist = lds;                      // [bin][column]
+    uint32_t* const ring = lds + 256 * COLS;         // per wavefront: chosen indices, then values, on their way out
+    uint32_t* const cand_key = lds + TK_BINS;        // sampled pass
+    uint16_t* const cand_idx = (uint16_t*)(lds + TK_BINS + CAP);
     __shared__ uint32_t tot[256];         // tot[r] = count of bin 255 - r
     __shared__ uint32_t wtot[3][WAVES];   // per wavefront: keys above, equal, any NaN / -0
-    __shared__ uint32_t ring[WAVES][2][TK_RING];  // per wavefront: chosen indices and values on their way out
     __shared__ TkState st;
-    // the sampled pass runs on rows of 64 keys per thread only (see topk_rows_sample_rank)
-    constexpr bool SAMPLED = NPT == 64;
-    constexpr int CAP = SAMPLED ? TK_CAND_PER_THREAD * THREADS : 1;  // candidates the sampled pass can hold
-    static_assert(TK_BINS % THREADS == 0 && TK_BINS <= 256 * COLS && TK_SAMPLES >= WAVE, "candidate bins");
-    __shared__ uint32_t cand_key[CAP], cand_idx[CAP];
     __shared__ uint32_t samp[TK_SAMPLES];
     __shared__ uint32_t wmax[WAVES], wcnt[WAVES], fst[2];
 
@@ -353,7 +362,7 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, run));
                 if (c) {
                     cand_key[pos] = key[j];
-                    cand_idx[pos] = (uint32_t)(base0 + j * WAVE + lane);
+                    cand_idx[pos] = (uint16_t)(base0 + j * WAVE + lane);
                 }
                 run += (uint32_t)__popcll(m);
             }
@@ -525,17 +534,17 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
         if (no_eq && P == 0xFFFFFFFFu) return;  // nothing above the largest key: no output here
         const uint32_t pc = all_eq ? P : P + 1u;
         if (row_special)
-            emit_wave<NPT, false, true>(key, M, pc, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+            emit_wave<NPT, false, true>(key, M, pc, P, NEED, run, e_base, base0, with_vals, ring + wave * 2 * TK_RING, ring + (wave * 2 + 1) * TK_RING,
                                          out_idx, out_vals, rsrc);
         else
-            emit_wave<NPT, false, false>(key, M, pc, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+            emit_wave<NPT, false, false>(key, M, pc, P, NEED, run, e_base, base0, with_vals, ring + wave * 2 * TK_RING, ring + (wave * 2 + 1) * TK_RING,
                                          out_idx, out_vals, rsrc);
     } else {
         if (row_special)
-            emit_wave<NPT, true, true>(key, M, P, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+            emit_wave<NPT, true, true>(key, M, P, P, NEED, run, e_base, base0, with_vals, ring + wave * 2 * TK_RING, ring + (wave * 2 + 1) * TK_RING,
                                         out_idx, out_vals, rsrc);
         else
-            emit_wave<NPT, true, false>(key, M, P, P, NEED, run, e_base, base0, with_vals, ring[wave][0], ring[wave][1],
+            emit_wave<NPT, true, false>(key, M, P, P, NEED, run, e_base, base0, with_vals, ring + wave * 2 * TK_RING, ring + (wave * 2 + 1) * TK_RING,
                                         out_idx, out_vals, rsrc);
     }
 }
@@ -571,7 +580,7 @@ int topk_rows_npt(int n) {
 // costs twice as much and the sampled pass wins (one 65536-key row: 25.7 ->
 // 19 us).
 int topk_rows_sample_rank(int n, int k) {
-    if (topk_rows_npt(n) < 64) return 0;
+    if (topk_rows_threads(n) != 1024) return 0;
     // the samples are spread over the workgroup's key slots, those past n being padding
     const double slots = (double)topk_rows_threads(n) * topk_rows_npt(n);
     const double kf = (double)k * TK_SAMPLES / slots;
