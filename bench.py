@@ -45,6 +45,12 @@ BF16_PEAK_TFS = 2500.0
 
 WORKLOADS = {
     "c2": dict(base="c2", T=1, copies=4, steps=200, warmup=20),
+    # c2 with the router look-ahead: consecutive tokens correlated like a
+    # layer's input and the next layer's; each step also routes its token with
+    # the next step's router and reads the predicted experts' gate/up weights
+    # on a second stream, from the end of the step on (same steps also timed
+    # without it)
+    "c2la": dict(base="c2", T=1, copies=4, steps=200, warmup=20, lookahead=True),
     "c3": dict(base="c3", T=1, copies=4, steps=200, warmup=20),
     "c3t2": dict(base="c3", T=2, copies=4, steps=200, warmup=20),
     "c4": dict(base="c4", T=512, copies=1, steps=20, warmup=5),
@@ -85,15 +91,25 @@ class Hip:
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so.7")
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
 
     def event(self):
         e = ctypes.c_void_p()
         assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def sync_event(self):
+        """An event that only orders streams (the work after it reads no data
+        that the work before it writes): no timing and no system-scope fence,
+        so recording it writes back and invalidates no cache."""
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0x2 | 0x20000000) == 0
         return e
 
     def record(self, e, stream):
@@ -103,6 +119,9 @@ class Hip:
         out = ctypes.c_float()
         assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
         return out.value
+
+    def wait(self, stream, e):
+        assert self.lib.hipStreamWaitEvent(ctypes.c_void_p(stream), e, 0) == 0
 
     def sync(self, e):
         assert self.lib.hipEventSynchronize(e) == 0
@@ -427,6 +446,11 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the steps in a HIP graph (64 steps per graph) and replay it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefetch-wg", type=int, default=256, help="look-ahead: workgroups of the prefetch launch")
+    ap.add_argument("--prefetch-rows", type=int, default=512,
+                    help="look-ahead: leading rows of each matrix the prefetch reads (0: all)")
+    ap.add_argument("--prefetch-which", type=int, default=3,
+                    help="look-ahead: matrices the prefetch reads (bit 0 gate, 1 up, 2 down)")
     ap.add_argument("--stage-times", default="auto", choices=["auto", "live", "pass"],
                     help="take the per-stage kernel times in the timed steps (live) or in a second eager pass "
                          "(pass); auto: live for prefill, pass for decode, whose 50 us steps the per-dispatch "
@@ -480,7 +504,12 @@ def main():
     t_gen = time.perf_counter()
     L = gen_weights_host(cfg)
     copies = upload_copies(L, n_copies, torch)
-    if T <= moe.DECODE_MAX_TOKENS:
+    la = bool(spec.get("lookahead"))
+    if la and (T != 1 or args.graph or not decode):
+        raise SystemExit("the look-ahead workload runs one token per step on the decode path, eagerly")
+    if la:
+        x_all = configs.gen_x_walk(cfg, N_DECODE_TOKENS, configs.LOOKAHEAD_RHO)
+    elif T <= moe.DECODE_MAX_TOKENS:
         x_all = configs.gen_x(cfg, N_DECODE_TOKENS, stream=configs.S_DECODE)
     else:
         x_all = configs.gen_x(cfg)
@@ -494,10 +523,61 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     n_tok_rows = x_dev.shape[0]
 
+    # router look-ahead (on while la_on[0]): the side stream routes this step's
+    # token with the next step's router (inputs only: no wait), and reads the
+    # predicted experts of the next step's weights once the step has ended
+    # (one event per step, recorded without a system-scope fence)
+    side = torch.cuda.Stream() if la else None
+    side_ws = moe.workspace(c) if la else None
+    pred = torch.empty((T, cfg["k"]), dtype=torch.int32, device="cuda") if la else None
+    pred_w = torch.empty((T, cfg["k"]), dtype=torch.float32, device="cuda") if la else None
+    la_ev = [hip.sync_event() for _ in range(warmup + steps)] if la else None
+    la_on = [False]
+
+    def hold(ms):
+        """Queue a bounded spin kernel of about ms milliseconds on the stream, so
+        that the host enqueues the steps behind it and its launch time (the
+        look-ahead adds six runtime calls per step) stays out of the timed region."""
+        if not la:
+            return
+        a0, a1 = hip.event(), hip.event()
+        hip.record(a0, stream)
+        torch.cuda._sleep(1 << 20)
+        hip.record(a1, stream)
+        hip.sync(a1)
+        per = hip.ms(a0, a1) / float(1 << 20)
+        torch.cuda._sleep(int(min(ms / max(per, 1e-9), 1 << 40)))
+
     def step(i, events=None, dbg=None, strm=None):
         r = (i * T) % n_tok_rows if n_tok_rows > T else 0
+        st = stream if strm is None else strm
         moe.moe_layer_forward(c, x_dev[r:r + T], Wc[i % n_copies], y, ws, debug=dbg,
-                              stream=stream if strm is None else strm, stage_events=events)
+                              stream=st, stage_events=events)
+        if la_on[0]:
+            ev_e = la_ev[i % len(la_ev)]
+            hip.record(ev_e, st)
+            nxt = copies[(i + 1) % n_copies]
+            moe.moe_route(c, x_dev[r:r + T], nxt["w_router"], nxt["bias"], None, pred, pred_w, side_ws,
+                          stream=side.cuda_stream)
+            hip.wait(side.cuda_stream, ev_e)
+            moe.moe_prefetch_experts(c, Wc[(i + 1) % n_copies], pred, which=args.prefetch_which,
+                                     rows=args.prefetch_rows, workgroups=args.prefetch_wg,
+                                     stream=side.cuda_stream)
+
+    la_off = None
+    if la:  # the same steps without the look-ahead first
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        a0, a1 = hip.event(), hip.event()
+        hold(0.2 * steps)
+        hip.record(a0, stream)
+        for i in range(steps):
+            step(warmup + i)
+        hip.record(a1, stream)
+        hip.sync(a1)
+        la_off = hip.ms(a0, a1) / steps
+        la_on[0] = True
 
     for i in range(warmup):
         step(i)
@@ -536,6 +616,7 @@ def main():
     e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    hold(0.2 * steps)
     hip.record(e0, stream)
     if graph is not None:
         for _ in range(steps // 64):
@@ -607,7 +688,7 @@ def main():
                    "top_k": cfg["k"], "d_ff": cfg["F"], "weights": cfg["w"], "activations": cfg["act"],
                    "path": path_kind, "weight_copies": n_copies, "hip_graph": bool(args.graph),
                    "stage_times": "live" if live else "second eager pass",
-                   "distinct_tokens": n_tok_rows if decode else T},
+                   "distinct_tokens": n_tok_rows if decode else T, "router_lookahead": la},
         "roofline": roofline,
         "layer_hbm_GBs": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
         "layer_hbm_frac": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -620,6 +701,17 @@ def main():
     }
     if not decode:
         out["mfma_frac_gate_up"] = round(out["gate_up_tflops"] / BF16_PEAK_TFS, 4)
+    if la:
+        # copies share the router weights, so the next step's prediction (its
+        # router on this step's token) is this step's own selection
+        hits = [len(set(idx_np[i].ravel()) & set(idx_np[i + 1].ravel())) / cfg["k"] for i in range(steps - 1)]
+        out["lookahead"] = {
+            "rho": configs.LOOKAHEAD_RHO, "hit_rate": round(float(np.mean(hits)), 4),
+            "off_value": round(T / (la_off * 1e-3), 2), "off_ms_per_step": round(la_off, 5),
+            "gain": round(ms_per_step and la_off / ms_per_step, 4),
+            "prefetch_workgroups": args.prefetch_wg, "prefetch_which": args.prefetch_which,
+            "prefetch_rows": args.prefetch_rows,
+            "enqueue": "both passes queued behind a bounded spin kernel (host launch time outside the timed region)"}
 
     if args.copy_probe_mib:
         out["copy_probe_GBs"] = copy_probe(torch, hip, stream, args.copy_probe_mib)

@@ -192,6 +192,32 @@ int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w
 int moe_topk_rows(const float *scores, int32_t rows, int32_t n, int32_t k, int32_t *idx, float *vals,
                   void **events, void *stream);
 
+/* Router look-ahead, its read half (NeutronStar fork page, "Cross-layer
+ * expert prefetch": the next layer's router runs on this layer's hidden
+ * state and the experts it predicts are read while the GPU still computes).
+ * The predictions come from moe_route called with the next layer's router
+ * weights on this layer's input x; this call then reads the weights of the
+ * experts ids [n_ids] int32 (device memory, e.g. that topk_idx; entries
+ * outside [0, n_expert) are skipped on the device) of the layer w: bit 0 of
+ * `which` selects gate, bit 1 up, bit 2 down (for MOE_DT_Q8B32 the codes
+ * and their scales), and `rows` > 0 limits the read to the leading rows of
+ * each selected matrix (gate and up have d_ff rows, down d_model; 0: all).
+ * It writes no memory, so no result of any call changes; the reads leave
+ * those weights in the device's memory-side cache (the Infinity Cache),
+ * where that layer's expert kernels find them if they run before other
+ * traffic evicts them.  Meant for a second stream, beside the work of the
+ * current layer: `workgroups` (1 .. MOE_PREFETCH_MAX_WORKGROUPS) fixes the
+ * launch's size, so that it takes only part of the chip.
+ * 0 <= n_ids <= MOE_PREFETCH_MAX_IDS (0 enqueues nothing), 1 <= which <= 7,
+ * rows >= 0, the selected matrices as in moe_weights, else MOE_ERR_INVALID;
+ * an expert matrix of more than 2^31 - 1 bytes is MOE_ERR_UNSUPPORTED.  No
+ * workspace.  events: NULL, or 2 hipEvent_t created by the caller (entries
+ * may be NULL) that receive the start and end timestamps of the dispatch. */
+#define MOE_PREFETCH_MAX_IDS 65536
+#define MOE_PREFETCH_MAX_WORKGROUPS 4096
+int moe_prefetch_experts(const moe_config *cfg, const moe_weights *w, const int32_t *ids, int32_t n_ids,
+                         int32_t which, int32_t rows, int32_t workgroups, void **events, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_str(int status);
 

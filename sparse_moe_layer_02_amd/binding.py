@@ -59,8 +59,11 @@ class moe_debug(ctypes.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_layer_forward", "moe_topk_rows", "moe_status_str")
+           "moe_combine", "moe_layer_forward", "moe_topk_rows", "moe_prefetch_experts", "moe_status_str")
 TOPK_ROWS_MAX_N = 65536  # MOE_TOPK_ROWS_MAX_N
+PREFETCH_MAX_IDS = 65536  # MOE_PREFETCH_MAX_IDS
+PREFETCH_MAX_WORKGROUPS = 4096  # MOE_PREFETCH_MAX_WORKGROUPS
+PREFETCH_GATE, PREFETCH_UP, PREFETCH_DOWN = 1, 2, 4  # bits of moe_prefetch_experts' `which`
 
 _lib = None
 
@@ -86,6 +89,7 @@ def load(path: str = LIB_PATH):
     lib.moe_layer_forward.argtypes = [C, P, W, P, ctypes.POINTER(moe_debug), P, ctypes.c_size_t, P]
     I = ctypes.c_int32
     lib.moe_topk_rows.argtypes = [P, I, I, I, P, P, ctypes.POINTER(ctypes.c_void_p), P]
+    lib.moe_prefetch_experts.argtypes = [C, W, P, I, I, I, I, ctypes.POINTER(ctypes.c_void_p), P]
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     for name in EXPORTS[1:-1]:
@@ -220,6 +224,19 @@ def moe_topk_rows(scores, k, idx, vals=None, stream=None, events=None):
     ev = None if events is None else ctypes.cast(events, ctypes.POINTER(ctypes.c_void_p))
     return _check(lib.moe_topk_rows(ptr(scores), rows, n, k, ptr(idx), ptr(vals), ev,
                                     _stream(stream)), lib)
+
+
+def moe_prefetch_experts(cfg, weights: moe_weights, ids, which=3, rows=0, workgroups=256, stream=None,
+                         events=None):
+    """Read the weights of the experts in ``ids`` (int32 device tensor, any shape;
+    e.g. moe_route's topk_idx for the next layer's router on this layer's input)
+    of the layer ``weights``: ``which`` bit 0 gate, 1 up, 2 down; ``rows`` > 0: only
+    the leading rows of each matrix.  Writes nothing.  ``events``: optional ctypes
+    array of 2 hipEvent_t handles."""
+    lib = load()
+    ev = None if events is None else ctypes.cast(events, ctypes.POINTER(ctypes.c_void_p))
+    return _check(lib.moe_prefetch_experts(ctypes.byref(cfg), ctypes.byref(weights), ptr(ids), ids.numel(),
+                                           which, rows, workgroups, ev, _stream(stream)), lib)
 
 
 def workspace(cfg: moe_config, device="cuda"):

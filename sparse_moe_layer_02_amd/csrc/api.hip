@@ -317,6 +317,48 @@ int moe_topk_rows(const float* scores, int32_t rows, int32_t n, int32_t k, int32
     return device_status(launch_topk_rows(a, static_cast<hipStream_t>(stream), kt));
 }
 
+int moe_prefetch_experts(const moe_config* cfg, const moe_weights* w, const int32_t* ids, int32_t n_ids,
+                         int32_t which, int32_t rows, int32_t workgroups, void** events, void* stream) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if (!w || n_ids < 0 || n_ids > MOE_PREFETCH_MAX_IDS || which < 1 || which > 7 || rows < 0 || workgroups < 1 ||
+        workgroups > MOE_PREFETCH_MAX_WORKGROUPS)
+        return MOE_ERR_INVALID;
+    if ((which & 1 && !mat_ok(cfg, w->gate)) || (which & 2 && !mat_ok(cfg, w->up)) ||
+        (which & 4 && !mat_ok(cfg, w->down)))
+        return MOE_ERR_INVALID;
+    if (n_ids == 0) return MOE_OK;
+    if (!elt_ok(ids)) return MOE_ERR_INVALID;
+    // every matrix of an expert holds F * d elements: gate and up F rows of d,
+    // down d rows of F
+    const int64_t elems = (int64_t)cfg->d_ff * cfg->d_model;
+    const int64_t esize = cfg->w_dtype == MOE_DT_F32 ? 4 : cfg->w_dtype == MOE_DT_BF16 ? 2 : 1;
+    if (elems * esize > 0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;  // one buffer descriptor per expert matrix
+    const bool q8 = cfg->w_dtype == MOE_DT_Q8B32;
+    const moe_mat* mats[3] = {&w->gate, &w->up, &w->down};
+    PrefetchArgs a{};
+    const int order[PF_SEGMENTS][2] = {{0, 0}, {1, 0}, {0, 1}, {1, 1}, {2, 0}, {2, 1}};  // (matrix, scales?)
+    for (int g = 0; g < PF_SEGMENTS; ++g) {
+        const int m = order[g][0];
+        const bool sc = order[g][1] != 0;
+        if (!(which >> m & 1) || (sc && !q8)) continue;
+        const int64_t n_rows = m == 2 ? cfg->d_model : cfg->d_ff, row_elems = elems / n_rows;
+        const int64_t r = rows == 0 || rows > n_rows ? n_rows : rows;  // leading rows read
+        a.base[g] = sc ? reinterpret_cast<const uint8_t*>(mats[m]->scale) : static_cast<const uint8_t*>(mats[m]->q);
+        a.stride[g] = sc ? elems / 32 * 2 : elems * esize;
+        a.bytes[g] = sc ? r * (row_elems / 32) * 2 : r * row_elems * esize;
+    }
+    a.ids = ids;
+    a.n_ids = n_ids;
+    a.E = cfg->n_expert;
+    KTime kt;
+    if (events) {
+        kt.start = static_cast<hipEvent_t>(events[0]);
+        kt.stop = static_cast<hipEvent_t>(events[1]);
+    }
+    return device_status(launch_prefetch_experts(a, workgroups, static_cast<hipStream_t>(stream), kt));
+}
+
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t* offsets, int32_t* perm_rows,
                 int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
     int s = validate_config(cfg);

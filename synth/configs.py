@@ -89,6 +89,31 @@ def gen_x(cfg, T=None, stream=S_X, token0=0):
     return _normal(cfg, stream, T * d, cfg["x_sigma"], start=token0 * d).reshape(T, d)
 
 
+# Correlation of consecutive tokens in the look-ahead workload: with 256
+# experts and top-6 selection, logits of correlation 0.97 share about 74% of
+# their top-6 sets, the prediction rate the NeutronStar fork page reports for
+# its router look-ahead.
+LOOKAHEAD_RHO = 0.97
+
+
+def gen_x_walk(cfg, T, rho, stream=S_DECODE):
+    """T tokens [T, d] whose consecutive rows have correlation ``rho``: x_0 = z_0,
+    x_t = rho x_{t-1} + sqrt(1 - rho^2) z_t with z ~ N(0, x_sigma^2) (fp32 walk;
+    bf16 workloads get each row rounded to bf16, as uint16 bits).  A stand-in
+    for a layer's input and the next layer's, which share the residual stream."""
+    d = cfg["d"]
+    z = normal_f32(cfg["seed"], stream, T * d, cfg["x_sigma"]).reshape(T, d).astype(np.float64)
+    x = np.empty_like(z)
+    x[0] = z[0]
+    c = math.sqrt(1.0 - rho * rho)
+    for t in range(1, T):
+        x[t] = rho * x[t - 1] + c * z[t]
+    x = x.astype(np.float32)
+    if cfg["act"] == "f32":
+        return x
+    return (round_to_bf16(x).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def gen_router(cfg):
     E, d = cfg["E"], cfg["d"]
     return normal_f32(cfg["seed"], S_WR, E * d, cfg["wr_sigma"]).reshape(E, d)

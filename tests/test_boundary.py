@@ -143,3 +143,31 @@ def test_workspace_monotone(moe):
     c5 = _cfg(moe, T=4096, d=6144, E=256, k=8, F=2048, Fs=2048)
     n = lib.moe_workspace_bytes(ctypes.byref(c5))
     assert 0.9e9 < n < 1.2e9
+
+
+def test_prefetch_experts_arguments(moe):
+    lib = moe.load()
+    c = _cfg(moe)
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    m = moe.binding.moe_mat(fake.value, None)
+    w = moe.binding.moe_weights(fake.value, None, m, m, m, m, m, m)
+    W = ctypes.byref(w)
+    # which outside 1..7, rows < 0, workgroups outside 1..4096, n_ids outside 0..65536
+    for which, rows, wg, n in [(0, 0, 64, 4), (8, 0, 64, 4), (3, -1, 64, 4), (3, 0, 0, 4), (3, 0, 4097, 4),
+                               (3, 0, 64, -1), (3, 0, 64, 65537)]:
+        assert lib.moe_prefetch_experts(ctypes.byref(c), W, fake, n, which, rows, wg, None, None) == 1
+    assert lib.moe_prefetch_experts(None, W, fake, 4, 3, 0, 64, None, None) == 1
+    assert lib.moe_prefetch_experts(ctypes.byref(c), None, fake, 4, 3, 0, 64, None, None) == 1
+    assert lib.moe_prefetch_experts(ctypes.byref(c), W, None, 4, 3, 0, 64, None, None) == 1
+    assert lib.moe_prefetch_experts(ctypes.byref(c), W, odd, 4, 3, 0, 64, None, None) == 1
+    # a selected matrix that is NULL, or int8 codes without scales
+    w_nodown = moe.binding.moe_weights(fake.value, None, m, m, moe.binding.moe_mat(None, None), m, m, m)
+    assert lib.moe_prefetch_experts(ctypes.byref(c), ctypes.byref(w_nodown), fake, 4, 4, 0, 64, None, None) == 1
+    cq = _cfg(moe, w="q8b32")
+    assert lib.moe_prefetch_experts(ctypes.byref(cq), W, fake, 4, 1, 0, 64, None, None) == 1
+    # the down matrix is not read when not selected; no ids: nothing enqueued
+    assert lib.moe_prefetch_experts(ctypes.byref(c), ctypes.byref(w_nodown), None, 0, 3, 0, 64, None, None) == 0
+    # an expert matrix beyond one buffer descriptor
+    big = _cfg(moe, d=65536, F=65536, w="f32", act="f32")
+    assert lib.moe_prefetch_experts(ctypes.byref(big), W, fake, 4, 1, 0, 64, None, None) == 2
