@@ -8,6 +8,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "prefetch.h"
 #include "topk_rows.h"
 
 using namespace moe;

@@ -16,7 +16,7 @@
 // A fixed number of workgroups walks the list, so the launch leaves most of
 // the chip to the kernels that run beside it.  The loaded data feeds an empty
 // asm statement only: nothing is written.  Ids outside [0, E) are skipped.
-#include "kernels.h"
+#include "prefetch.h"
 
 namespace moe {
 namespace {
