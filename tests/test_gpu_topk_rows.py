@@ -124,3 +124,17 @@ def test_topk_rows_events_and_empty(dev):
         hip.hipEventDestroy(e)
     stream = torch.cuda.current_stream().cuda_stream
     assert lib.moe_topk_rows(None, 0, 4096, 8, None, None, None, ctypes.c_void_p(stream)) == 0
+
+
+@pytest.mark.parametrize("n,k", [(32768, 1024), (65536, 1024), (20000, 512)])
+def test_topk_rows_clustered(dev, orc, n, k):
+    """High scores gathered in a few wavefronts' ranges (recent positions of an
+    attention row, a block of equal scores at the cut): the sampled pass's
+    compaction takes candidates from anywhere in the row."""
+    rng = np.random.default_rng(n + 3 * k)
+    rows = rng.standard_normal((4, n)).astype(np.float32)
+    rows[0, -2000:] += 6.0                                 # the last 2000 positions score high
+    rows[1, 100:1100] += 6.0                               # one block early in the row
+    rows[2, -3 * k:] = np.float32(5.0)                     # 3k equal scores at the end: ties at the cut
+    rows[3, ::97] += 8.0                                   # spread thinly over every wavefront
+    check(dev, orc, rows, k, "clustered_n%d_k%d" % (n, k))
