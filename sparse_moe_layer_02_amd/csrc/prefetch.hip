@@ -12,8 +12,7 @@
 // down matrices (int8 codes and their fp16 scales, or the bf16 / fp32
 // elements), or their leading rows only.  The work is a flat list of 64 KiB
 // chunks ordered (segment, chunk, expert): the GEMVs of the next layer read
-// all experts side by side.
-// A fixed number of workgroups walks the list, so the launch leaves most of
+// all experts side by side.  A fixed number of workgroups walks the list, so the launch leaves most of
 // the chip to the kernels that run beside it.  The loaded data feeds an empty
 // asm statement only: nothing is written.  Ids outside [0, E) are skipped.
 #include "prefetch.h"
@@ -47,11 +46,12 @@ __global__ __launch_bounds__(PF_THREADS) void prefetch_experts_kernel(PrefetchAr
         // the expert's segment as a buffer: loads past its end return 0
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(a.base[s] + (int64_t)e * a.stride[s]), (short)0, (int)a.bytes[s], 0x00020000);
-        const int off0 = (int)(chunk * PF_CHUNK) + threadIdx.x * 16;
+        // unsigned offsets: past 2^31 - 1 they stay past the buffer's end (bytes < 2^31)
+        const uint32_t off0 = (uint32_t)(chunk * PF_CHUNK) + threadIdx.x * 16u;
         v4u32 v[PF_UNROLL];
 #pragma unroll
         for (int u = 0; u < PF_UNROLL; ++u)
-            v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + u * PF_THREADS * 16, 0, 0);
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off0 + (uint32_t)(u * PF_THREADS * 16)), 0, 0);
 #pragma unroll
         for (int u = 0; u < PF_UNROLL; ++u) asm volatile("" ::"v"(v[u]));
     }
