@@ -145,7 +145,7 @@ __global__ __launch_bounds__(THREADS, 2) void topk_rows_kernel(TopkRowsArgs a) {
     // as the full path needs them), candidate keys and 16-bit candidate
     // indices (n <= 65536).  Small enough for two 1024-thread workgroups of
     // 32 keys per thread on one CU.
-    constexpr bool SAMPLED = THREADS == 1024 && NPT >= 32;  // rows of 32 or 64 keys per thread (see topk_rows_sample_rank)
+    constexpr bool SAMPLED = NPT >= 16;  // rows of 16 or more keys per thread (see topk_rows_sample_rank)
     constexpr int CAP = SAMPLED ? TK_CAND_PER_THREAD * THREADS : 0;  // candidates the sampled pass can hold
     static_assert(TK_BINS % THREADS == 0 && TK_BINS <= 256 * COLS && TK_SAMPLES >= WAVE, "candidate bins");
     constexpr int FULL_WORDS = 256 * COLS + WAVES * 2 * TK_RING, SAMPLED_WORDS = TK_BINS + CAP + CAP / 2;
@@ -580,7 +580,7 @@ int topk_rows_npt(int n) {
 // costs twice as much and the sampled pass wins (one 65536-key row: 25.7 ->
 // 19 us).
 int topk_rows_sample_rank(int n, int k) {
-    if (topk_rows_threads(n) != 1024) return 0;
+    if (topk_rows_npt(n) < 16) return 0;
     // the samples are spread over the workgroup's key slots, those past n being padding
     const double slots = (double)topk_rows_threads(n) * topk_rows_npt(n);
     const double kf = (double)k * TK_SAMPLES / slots;
