@@ -92,3 +92,26 @@ def test_partial_experts_match_full():
 def test_smaller_T_is_prefix():
     cfg = configs.get("c3")
     assert (configs.gen_x(cfg, 2)[:1] == configs.gen_x(cfg, 1)).all()
+
+
+def test_lookahead_walk_statistics(orc):
+    """The look-ahead workload's tokens: each row keeps the spread of the
+    layer's activations, consecutive rows have correlation LOOKAHEAD_RHO, and
+    the oracle's router on one token picks about three quarters of the next
+    token's experts (the prediction rate the look-ahead stands in for)."""
+    import numpy as np
+    from synth import configs
+    cfg = configs.get("c2")
+    T = 160
+    x = configs.gen_x_walk(cfg, T, configs.LOOKAHEAD_RHO)
+    assert x.dtype == np.uint16 and x.shape == (T, cfg["d"])
+    f = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(f.std(axis=1) / cfg["x_sigma"] - 1.0) < 0.05)
+    corr = [np.corrcoef(f[t], f[t + 1])[0, 1] for t in range(T - 1)]
+    assert abs(np.mean(corr) - configs.LOOKAHEAD_RHO) < 0.005
+    _, idx, _ = orc.route(cfg, x, configs.gen_router(cfg), configs.gen_bias(cfg))
+    hit = np.mean([len(set(idx[t]) & set(idx[t + 1])) / cfg["k"] for t in range(T - 1)])
+    assert 0.65 < hit < 0.85, hit
+    # the f32 form is the same walk before rounding
+    xf = configs.gen_x_walk(configs.get("c1"), 8, 0.5)
+    assert xf.dtype == np.float32 and xf.shape == (8, 512)
