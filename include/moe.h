@@ -209,7 +209,8 @@ int moe_topk_rows(const float *scores, int32_t rows, int32_t n, int32_t k, int32
  * current layer: `workgroups` (1 .. MOE_PREFETCH_MAX_WORKGROUPS) fixes the
  * launch's size, so that it takes only part of the chip.
  * 0 <= n_ids <= MOE_PREFETCH_MAX_IDS (0 enqueues nothing), 1 <= which <= 7,
- * rows >= 0, the selected matrices as in moe_weights, else MOE_ERR_INVALID;
+ * rows >= 0, the selected matrices as in moe_weights with their scale
+ * arrays (MOE_DT_Q8B32) 16-byte aligned too, else MOE_ERR_INVALID;
  * an expert matrix of more than 2^31 - 1 bytes is MOE_ERR_UNSUPPORTED.  No
  * workspace.  events: NULL, or 2 hipEvent_t created by the caller (entries
  * may be NULL) that receive the start and end timestamps of the dispatch. */

@@ -328,6 +328,10 @@ int moe_prefetch_experts(const moe_config* cfg, const moe_weights* w, const int3
     if ((which & 1 && !mat_ok(cfg, w->gate)) || (which & 2 && !mat_ok(cfg, w->up)) ||
         (which & 4 && !mat_ok(cfg, w->down)))
         return MOE_ERR_INVALID;
+    if (cfg->w_dtype == MOE_DT_Q8B32 && ((which & 1 && !aligned16(w->gate.scale)) ||
+                                         (which & 2 && !aligned16(w->up.scale)) ||
+                                         (which & 4 && !aligned16(w->down.scale))))
+        return MOE_ERR_INVALID;  // the scales are read with 16-byte loads too
     if (n_ids == 0) return MOE_OK;
     if (!elt_ok(ids)) return MOE_ERR_INVALID;
     // every matrix of an expert holds F * d elements: gate and up F rows of d,

@@ -166,6 +166,10 @@ def test_prefetch_experts_arguments(moe):
     assert lib.moe_prefetch_experts(ctypes.byref(c), ctypes.byref(w_nodown), fake, 4, 4, 0, 64, None, None) == 1
     cq = _cfg(moe, w="q8b32")
     assert lib.moe_prefetch_experts(ctypes.byref(cq), W, fake, 4, 1, 0, 64, None, None) == 1
+    # int8 scales that are only 4-byte aligned: fine for the layer, not for the prefetch's 16-byte loads
+    mq = moe.binding.moe_mat(fake.value, fake.value + 4)
+    wq = moe.binding.moe_weights(fake.value, None, mq, mq, mq, mq, mq, mq)
+    assert lib.moe_prefetch_experts(ctypes.byref(cq), ctypes.byref(wq), fake, 4, 1, 0, 64, None, None) == 1
     # the down matrix is not read when not selected; no ids: nothing enqueued
     assert lib.moe_prefetch_experts(ctypes.byref(c), ctypes.byref(w_nodown), None, 0, 3, 0, 64, None, None) == 0
     # an expert matrix beyond one buffer descriptor
