@@ -570,21 +570,20 @@ int topk_rows_npt(int n) {
 }
 
 // Rank of the sampled threshold among the TK_SAMPLES samples: the expected
-// number of samples above the k-th largest key plus six standard deviations
-// and four, so that fewer than k keys reach it only for very unusual rows; 0
-// (no sampled pass) when the expected number of candidates would not fit
-// comfortably in the LDS room for them, and for rows of up to 32768 keys: with
-// 32 keys per thread the radix passes over all keys cost about what the
-// sampled pass's threshold, compaction and selection cost (measured on the
-// 512 x 32768 indexer workload), while with 64 keys per thread each full pass
-// costs twice as much and the sampled pass wins (one 65536-key row: 25.7 ->
-// 19 us).
+// number of samples above the k-th largest key plus four standard deviations
+// and three, so that fewer than k keys reach it (and the row takes the full
+// radix path) for about one row in 10^4 to 10^5 of random scores; 0 (no
+// sampled pass) for rows of fewer than 16 keys per thread, where the full
+// passes are short, and when the expected number of candidates would not fit
+// comfortably in the LDS room for them.  (A margin of six deviations and four
+// cost 3% more on the 512 x 32768, top-1024 and 1 x 65536, top-1024 indexer
+// workloads: more candidates to select from and to write out.)
 int topk_rows_sample_rank(int n, int k) {
     if (topk_rows_npt(n) < 16) return 0;
     // the samples are spread over the workgroup's key slots, those past n being padding
     const double slots = (double)topk_rows_threads(n) * topk_rows_npt(n);
     const double kf = (double)k * TK_SAMPLES / slots;
-    const int r = (int)std::ceil(kf + 6.0 * std::sqrt(kf) + 4.0);
+    const int r = (int)std::ceil(kf + 4.0 * std::sqrt(kf) + 3.0);
     const double expect = (double)r * slots / TK_SAMPLES;
     if (r > TK_SAMPLES / 2 || expect > 0.7 * TK_CAND_PER_THREAD * topk_rows_threads(n)) return 0;
     return r;
