@@ -176,6 +176,26 @@ int moe_combine(const moe_config *cfg, const float *slot_out, const float *share
 int moe_layer_forward(const moe_config *cfg, const void *x, const moe_weights *w, float *y,
                       moe_debug *dbg, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and kernels as moe_layer_forward, but
+ * no caller workspace: the library's own static device array of
+ * MOE_STATIC_SCRATCH_BYTES serves instead (one per GPU, held from the first
+ * call on that GPU until the process ends; the current device's copy is used,
+ * so `stream` must belong to the current device).  A config whose
+ * moe_workspace_bytes exceeds MOE_STATIC_SCRATCH_BYTES returns
+ * MOE_ERR_WORKSPACE and enqueues nothing (64 MiB covers every decode config
+ * here and prefill batches of a few hundred tokens at d_model 4096-6144).
+ * This call never allocates or frees.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents (nothing in it needs to start
+ * at zero: each call writes every word before reading it), so calls that
+ * overlap on one GPU - on two streams, or from two host threads without
+ * ordering - race and must not be issued.  MOE_ERR_DEVICE if the array's
+ * device address cannot be obtained. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_config *cfg, const void *x, const moe_weights *w, float *y,
+                              moe_debug *dbg, void *stream);
+
 /* Top-k over long candidate rows: the sparse attention indexer's selection of
  * the best 512 or 1024 entries of a long score row ("256 experts, 512 lines"
  * blog post, section "The constant that always said 256"), with the order of

@@ -59,7 +59,9 @@ class moe_debug(ctypes.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_select", "moe_permute", "moe_expert_ffn",
-           "moe_combine", "moe_layer_forward", "moe_topk_rows", "moe_prefetch_experts", "moe_status_str")
+           "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_topk_rows",
+           "moe_prefetch_experts", "moe_status_str")
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 TOPK_ROWS_MAX_N = 65536  # MOE_TOPK_ROWS_MAX_N
 PREFETCH_MAX_IDS = 65536  # MOE_PREFETCH_MAX_IDS
 PREFETCH_MAX_WORKGROUPS = 4096  # MOE_PREFETCH_MAX_WORKGROUPS
@@ -87,6 +89,7 @@ def load(path: str = LIB_PATH):
     lib.moe_expert_ffn.argtypes = [C, P, W, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_combine.argtypes = [C, P, P, P, P]
     lib.moe_layer_forward.argtypes = [C, P, W, P, ctypes.POINTER(moe_debug), P, ctypes.c_size_t, P]
+    lib.moe_layer_forward_noalloc.argtypes = [C, P, W, P, ctypes.POINTER(moe_debug), P]
     I = ctypes.c_int32
     lib.moe_topk_rows.argtypes = [P, I, I, I, P, P, ctypes.POINTER(ctypes.c_void_p), P]
     lib.moe_prefetch_experts.argtypes = [C, W, P, I, I, I, I, ctypes.POINTER(ctypes.c_void_p), P]
@@ -203,16 +206,31 @@ def moe_layer_forward(cfg, x, weights: moe_weights, y, ws, debug: dict | None = 
     """``stage_events``: optional ctypes array of STAGE_EVENTS hipEvent_t handles
     (start and end timestamps of each stage's kernels)."""
     lib = load()
-    dbg = None
-    if debug or stage_events is not None:
-        debug = debug or {}
-        dbg = moe_debug(*(ptr(debug.get(k)) for k in
-                          ("logits", "topk_idx", "topk_w", "offsets", "perm_rows", "inv_perm")))
-        if stage_events is not None:
-            dbg.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
+    dbg = _debug_struct(debug, stage_events)
     return _check(lib.moe_layer_forward(ctypes.byref(cfg), ptr(x), ctypes.byref(weights), ptr(y),
                                         ctypes.byref(dbg) if dbg else None, ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)), lib)
+
+
+def _debug_struct(debug, stage_events):
+    if not debug and stage_events is None:
+        return None
+    debug = debug or {}
+    dbg = moe_debug(*(ptr(debug.get(k)) for k in ("logits", "topk_idx", "topk_w", "offsets", "perm_rows",
+                                                  "inv_perm")))
+    if stage_events is not None:
+        dbg.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
+    return dbg
+
+
+def moe_layer_forward_noalloc(cfg, x, weights: moe_weights, y, debug: dict | None = None, stream=None,
+                              stage_events=None):
+    """moe_layer_forward over the library's static device scratch (no workspace
+    argument; configs needing more than STATIC_SCRATCH_BYTES are refused)."""
+    lib = load()
+    dbg = _debug_struct(debug, stage_events)
+    return _check(lib.moe_layer_forward_noalloc(ctypes.byref(cfg), ptr(x), ctypes.byref(weights), ptr(y),
+                                                ctypes.byref(dbg) if dbg else None, _stream(stream)), lib)
 
 
 def moe_topk_rows(scores, k, idx, vals=None, stream=None, events=None):

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "prefetch.h"
@@ -255,6 +257,57 @@ SelectArgs select_args(const moe_config* c, const float* logits, const float* bi
     return s;
 }
 
+
+// Arguments of a whole-layer call other than its workspace.
+int check_layer_args(const moe_config* cfg, const void* x, const moe_weights* w, const float* y,
+                     const moe_debug* dbg) {
+    int s = validate_config(cfg);
+    if (s) return s;
+    if ((s = check_weights(cfg, w, true))) return s;
+    if (!ptr_ok(x) || !ptr_ok(y)) return MOE_ERR_INVALID;
+    if (dbg && (!opt_elt_ok(dbg->logits) || !opt_elt_ok(dbg->topk_idx) || !opt_elt_ok(dbg->topk_w) ||
+                !opt_elt_ok(dbg->offsets) || !opt_elt_ok(dbg->perm_rows) || !opt_elt_ok(dbg->inv_perm)))
+        return MOE_ERR_INVALID;
+    const bool decode = cfg->path == MOE_PATH_DECODE ||
+                        (cfg->path == MOE_PATH_AUTO && cfg->n_tokens <= MOE_DECODE_MAX_TOKENS);
+    if (decode && cfg->n_tokens > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int enqueue_layer(const moe_config* cfg, const void* x, const moe_weights* w, float* y, moe_debug* dbg,
+                  void* ws, void* stream);
+
+// ---------------------------------------------------------------------------
+// The library's own scratch for moe_layer_forward_noalloc: one array per GPU
+// (every device that loads this code object holds its own copy, until the
+// process ends).  In host code `scratch` only names the symbol; its device
+// address is looked up once per device, with that device current, and only
+// that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// Device address of the current device's scratch array (looked up on the
+// first call made on that device).
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MOE_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return MOE_ERR_DEVICE;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -407,17 +460,31 @@ int moe_combine(const moe_config* cfg, const float* slot_out, const float* share
 
 int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w, float* y, moe_debug* dbg,
                       void* ws, size_t ws_bytes, void* stream) {
-    int s = validate_config(cfg);
+    int s = check_layer_args(cfg, x, w, y, dbg);
     if (s) return s;
-    if ((s = check_weights(cfg, w, true))) return s;
-    if (!ptr_ok(x) || !ptr_ok(y)) return MOE_ERR_INVALID;
-    if (dbg && (!opt_elt_ok(dbg->logits) || !opt_elt_ok(dbg->topk_idx) || !opt_elt_ok(dbg->topk_w) ||
-                !opt_elt_ok(dbg->offsets) || !opt_elt_ok(dbg->perm_rows) || !opt_elt_ok(dbg->inv_perm)))
-        return MOE_ERR_INVALID;
+    if ((s = check_ws(cfg, ws, ws_bytes))) return s;
+    return enqueue_layer(cfg, x, w, y, dbg, ws, stream);
+}
+
+int moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights* w, float* y,
+                              moe_debug* dbg, void* stream) {
+    int s = check_layer_args(cfg, x, w, y, dbg);
+    if (s) return s;
+    if (make_layout(cfg).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void* scratch_ptr = nullptr;
+    if ((s = static_scratch(&scratch_ptr))) return s;
+    return enqueue_layer(cfg, x, w, y, dbg, scratch_ptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The layer's launches over a workspace `ws` already checked to be large enough.
+int enqueue_layer(const moe_config* cfg, const void* x, const moe_weights* w, float* y, moe_debug* dbg,
+                  void* ws, void* stream) {
     const bool decode = cfg->path == MOE_PATH_DECODE ||
                         (cfg->path == MOE_PATH_AUTO && cfg->n_tokens <= MOE_DECODE_MAX_TOKENS);
-    if (decode && cfg->n_tokens > MOE_DECODE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
-    if ((s = check_ws(cfg, ws, ws_bytes))) return s;
     const Layout L = make_layout(cfg);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -465,4 +532,4 @@ int moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w
     return device_status(e);
 }
 
-}  // extern "C"
+}  // namespace
