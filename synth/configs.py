@@ -267,3 +267,99 @@ def gen_indexer_scores(spec, row0=0, rows=None):
     if spec.get("fmt", "f32") == "bf16":
         s = round_to_bf16(s)
     return np.ascontiguousarray(s, np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Exact-arithmetic layers: small-integer inputs for which every product and
+# every partial sum of the layer is an exactly representable number, so any
+# correct evaluation order gives the same bits.  Built from a numpy seeded
+# generator; no step of the method is computed here.
+#
+# x[t] holds, in its first E columns, the 0/1 indicator of a k-subset S_t of
+# the experts; column E ("lift") holds 32 and column E+1 ("one") holds 1; the
+# remaining columns are integers in [-2, 2].  The router gives expert e weight
+# 24 on column e plus three +-1 entries in the free columns, so a logit is
+# 24 + n (e in S_t) or n (otherwise) with |n| <= 6: the selected experts'
+# sigmoid scores round to exactly 1.0 (logit >= 18), every other score stays
+# below 1, and the renormalised weights are exactly 1/k.  Every gate row has 1
+# on the lift column plus six +-1 entries, so g is an integer in [20, 44],
+# where silu(g) rounds to g in fp32; every up row has 1 on the one column plus
+# two +-1 entries, so u is an integer in [-3, 5] and g*u an integer of at most
+# 220 in magnitude (exact in bf16); every down row has eight +-1 entries.  int8
+# layers store each weight as q * scale with a per-block scale of 1, 1/2 or
+# 1/4 (fp16) and q = weight / scale.
+# ---------------------------------------------------------------------------
+
+def _sparse_pm1(rng, n, rows, cols, per_row, forbid=()):
+    """[n, rows, cols] float64 with ``per_row`` entries of +-1 per row, at
+    distinct columns outside ``forbid``."""
+    allowed = np.setdiff1d(np.arange(cols), np.asarray(forbid, dtype=np.int64))
+    assert allowed.size >= per_row
+    pick = rng.integers(0, allowed.size, (n, rows, per_row))
+    while True:  # draw again the rows that hit a column twice
+        srt = np.sort(pick, axis=2)
+        dup = (srt[:, :, 1:] == srt[:, :, :-1]).any(axis=2)
+        if not dup.any():
+            break
+        pick[dup] = rng.integers(0, allowed.size, (int(dup.sum()), per_row))
+    out = np.zeros((n, rows, cols))
+    sign = rng.choice(np.array([-1.0, 1.0]), size=(n, rows, per_row))
+    np.put_along_axis(out, allowed[pick], sign, axis=2)
+    return out
+
+
+def _store(cfg, w, rng):
+    """Integer-valued float64 weights [n, rows, cols] in the workload's format."""
+    if cfg["w"] == "f32":
+        return np.ascontiguousarray(w.astype(np.float32))
+    if cfg["w"] == "bf16":
+        return np.ascontiguousarray((w.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    n, rows, cols = w.shape
+    shift = rng.integers(0, 3, (n, rows, cols // 32))            # scale 2^-shift
+    scale_bits = (0x3C00 - 0x0400 * shift).astype(np.uint16)      # fp16 1.0, 0.5, 0.25
+    q = w * np.repeat(2.0 ** shift, 32, axis=2)
+    return (np.ascontiguousarray(q.astype(np.int8)), np.ascontiguousarray(scale_bits))
+
+
+def exact_layer(T, d, E, k, F, Fs=None, n_shared=1, act="bf16", w="bf16", seed=0):
+    """A layer (dict as :func:`make_layer`, with its workload dict under
+    ``cfg``) on which the method's arithmetic is exact (see above).  Sigmoid
+    router, no bias, scale 1; k must be 1, 2, 4 or 8 and d >= E + 2."""
+    assert k in (1, 2, 4, 8) and k <= E and d >= E + 2 and d % 64 == 0
+    Fs = F if Fs is None else Fs
+    cfg = custom(T=T, d=d, E=E, k=k, F=F, Fs=Fs, n_shared=n_shared, score="sigmoid", scale=1.0, act=act,
+                 w=w, bias="none", name="exact")
+    rng = np.random.default_rng(seed)
+    lift, one = E, E + 1
+    x = np.zeros((T, d))
+    for t in range(T):
+        x[t, rng.choice(E, k, replace=False)] = 1.0
+    x[:, lift] = 32.0
+    x[:, one] = 1.0
+    x[:, E + 2:] = rng.integers(-2, 3, (T, d - E - 2))
+    wr = np.zeros((E, d))
+    wr[np.arange(E), np.arange(E)] = 24.0
+    wr += _sparse_pm1(rng, 1, E, d, 3, forbid=range(E + 2))[0]
+    L = dict(cfg=cfg, w_router=np.ascontiguousarray(wr.astype(np.float32)), bias=None)
+    if act == "f32":
+        L["x"] = np.ascontiguousarray(x.astype(np.float32))
+    else:
+        L["x"] = np.ascontiguousarray((x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+
+    def gate_up(n, rows):
+        g = _sparse_pm1(rng, n, rows, d, 6, forbid=(lift, one))
+        g[:, :, lift] = 1.0
+        u = _sparse_pm1(rng, n, rows, d, 2, forbid=(lift, one))
+        u[:, :, one] = 1.0
+        return g, u
+
+    g, u = gate_up(E, F)
+    L["gate"], L["up"] = _store(cfg, g, rng), _store(cfg, u, rng)
+    L["down"] = _store(cfg, _sparse_pm1(rng, E, d, F, 8), rng)
+    if n_shared:
+        g, u = gate_up(1, Fs)
+        L["s_gate"], L["s_up"] = _store(cfg, g, rng), _store(cfg, u, rng)
+        L["s_down"] = _store(cfg, _sparse_pm1(rng, 1, d, Fs, 8), rng)
+    else:
+        L["s_gate"] = L["s_up"] = L["s_down"] = None
+    return L

@@ -587,4 +587,56 @@ def pin_combine_definition(orc):
     assert (orc.combine(cfg, slot, None) == slot.reshape(T, k, d).sum(1)).all()
 
 
+def _exact_weights(cfg, m):
+    """Integer weights [n, rows, cols] (int64) of an exact_layer tensor."""
+    if cfg["w"] == "q8b32":
+        q, sc = m
+        shift = (0x3C00 - sc.astype(np.int64)) // 0x0400
+        assert np.all(sc.astype(np.int64) == 0x3C00 - 0x0400 * shift) and np.all((shift >= 0) & (shift <= 2))
+        q = q.astype(np.int64)
+        mult = np.repeat(2 ** shift, 32, axis=2)
+        assert np.all(q % mult == 0)
+        return q // mult
+    if cfg["w"] == "bf16":
+        return (m.astype(np.uint32) << 16).view(np.float32).astype(np.int64)
+    return m.astype(np.int64)
+
+
+def pin_exact_layers_integer_evaluation(orc):
+    """On the exact-arithmetic layers the GPU tests use (synth.configs.
+    exact_layer) the oracle's y equals an evaluation in exact integers: the
+    selected experts are the token's indicator set, each weight is 1/k, and
+    silu(g) = g for the integer gate sums g >= 20 at fp32 precision (e^-20 <
+    2^-25).  Pins the premise of the GPU's bit-exact tests, for bf16, int8 and
+    fp32 weights and for the decode and prefill shapes."""
+    from synth import configs
+    for spec in (dict(T=3, d=256, E=32, k=4, F=128), dict(T=40, d=256, E=16, k=4, F=128, w="q8b32"),
+                 dict(T=5, d=128, E=8, k=2, F=64, act="f32", w="f32"),
+                 dict(T=30, d=192, E=4, k=1, F=64, Fs=128, n_shared=0)):
+        L = configs.exact_layer(**spec, seed=11)
+        cfg = L["cfg"]
+        E, k = cfg["E"], cfg["k"]
+        x = L["x"]
+        xi = (x.astype(np.uint32) << 16).view(np.float32) if cfg["act"] == "bf16" else x
+        xi = xi.astype(np.int64)
+        ref = orc.layer_forward(cfg, L)
+        G, U, D = (_exact_weights(cfg, L[w]) for w in ("gate", "up", "down"))
+        want = np.zeros((cfg["T"], cfg["d"]), dtype=object)
+        for t in range(cfg["T"]):
+            sel = np.flatnonzero(xi[t, :E])
+            assert ref["topk_idx"][t].tolist() == sel.tolist()
+            acc = np.zeros(cfg["d"], dtype=object)
+            for e in sel:
+                g, u = G[e] @ xi[t], U[e] @ xi[t]
+                assert g.min() >= 20
+                acc = acc + (D[e] @ (g * u)).astype(object) * Fraction(1, k)
+            if cfg["n_shared"]:
+                g = _exact_weights(cfg, L["s_gate"])[0] @ xi[t]
+                u = _exact_weights(cfg, L["s_up"])[0] @ xi[t]
+                acc = acc + (_exact_weights(cfg, L["s_down"])[0] @ (g * u)).astype(object)
+            want[t] = acc
+        assert np.all(ref["topk_w"] == np.float32(1.0 / k))
+        assert np.array_equal(ref["y"].astype(np.float64), want.astype(np.float64)), spec
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

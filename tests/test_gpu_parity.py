@@ -3,9 +3,12 @@ the same seeded inputs.
 
 Bar: expert indices, offsets and permutation exact; logits and routing weights
 within one ulp; y within 2e-3 (bf16 / int8 layers) or 1e-5 (fp32 layers),
-row-normwise (see gpu_harness).  The full-size prefill workloads (4096 and
-512 tokens, d = 6144) check routing and the permutation on every token and y
-on a sample of tokens the oracle evaluates one by one.
+row-normwise (see gpu_harness).  Decode workloads run 32-64 steps of the
+benchmark's token stream, every token checked.  The full-size prefill
+workloads check routing and the permutation on every token and y on every
+token (c4, c2 with 512 tokens) or on a sample that reaches every row tile of
+the most and least loaded experts (c5, and the matrix-core supplements s1 and
+s2).  Bit-exact checks on exact-arithmetic layers are in test_gpu_exact.py.
 """
 import math
 import sys
@@ -49,56 +52,104 @@ def run_and_check(orc, cfg, L, path="auto", label=""):
 
 
 # ---------------------------------------------------------------------------
-# Workloads c1-c3 (decode sizes): full oracle on every token
+# Workloads c1-c3 (decode sizes): many decode steps of the benchmark's token
+# stream, the oracle on every token of every step
 # ---------------------------------------------------------------------------
 
-def _oracle_layer_for(orc, cfg, T):
-    """Layer inputs with only the experts the oracle's router selects filled
-    (the oracle never reads the others)."""
-    x = configs.gen_x(cfg, T)
-    _, idx, _ = orc.route(cfg, x, configs.gen_router(cfg), configs.gen_bias(cfg))
-    return configs.make_layer(cfg, T=T, experts=np.unique(idx))
+def _host_layer_on_device(cfg, T=None):
+    """The whole layer on the host (for the oracle) and its weights on the GPU."""
+    L = configs.make_layer(cfg, T=T)
+    return L, H.upload_layer(L)
 
 
-@pytest.mark.parametrize("name,T", [("c1", 4), ("c2", 1), ("c3", 1), ("c3", 2)])
-def test_decode_workloads(torch_cuda, orc, name, T):
-    cfg = configs.get(name, T=T)
-    say("case", name, "T", T, "(generating weights)")
-    W = H.upload_weights_chunked(cfg)
-    L = _oracle_layer_for(orc, cfg, T)
-    x = H.to_dev(L["x"])
-    got = H.layer_outputs(cfg, x, W)
-    ref = orc.layer_forward(cfg, L)
-    H.check_routing(got, ref, name)
-    err = H.check_y(got["y"], ref["y"], cfg, name)
-    say("   ok %s T=%d: y err %.2e" % (name, T, err))
-    # the same inputs through the prefill path: identical routing, y within tolerance
-    got_p = H.layer_outputs(cfg, x, W, path="prefill")
-    H.check_routing(got_p, ref, name + "/prefill")
-    H.check_y(got_p["y"], ref["y"], cfg, name + "/prefill")
+DECODE_STEPS = {"c1": ("c1", 4, 1), "c2": ("c2", 1, 64), "c3": ("c3", 1, 32), "c3t2": ("c3", 2, 32)}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", sorted(DECODE_STEPS))
+def test_decode_workloads(torch_cuda, orc, name):
+    """c2: 64 distinct tokens, c3: 32 one-token and 32 two-token (verify)
+    steps, all from the benchmark's decode token stream; c1 its own 4 tokens.
+    Every step through the decode path, the first two also through the
+    prefill path; routing exact and y within tolerance on every token."""
+    base, T, steps = DECODE_STEPS[name]
+    cfg = configs.get(base, T=T)
+    say("case", name, "T", T, "steps", steps, "(generating the layer)")
+    L, W = _host_layer_on_device(cfg)
+    if name == "c1":
+        xs = [L["x"]]
+    else:
+        xs = [configs.gen_x(cfg, T, stream=configs.S_DECODE, token0=i * T) for i in range(steps)]
+    got = [H.layer_outputs(cfg, H.to_dev(x), W) for x in xs]
+    say("   %d GPU steps done; oracle on %d tokens" % (len(xs), len(xs) * T))
+    Lr = dict(L)
+    Lr["x"] = np.ascontiguousarray(np.concatenate(xs))
+    ref = orc.layer_forward(cfg, Lr)
+    errs, unions = [], []
+    for i, g in enumerate(got):
+        sl = slice(i * T, (i + 1) * T)
+        r = dict(logits=ref["logits"][sl], topk_idx=ref["topk_idx"][sl], topk_w=ref["topk_w"][sl])
+        ro, rp, ri = orc.permute(cfg, r["topk_idx"])
+        r.update(offsets=ro, perm_rows=rp, inv_perm=ri)
+        H.check_routing(g, r, "%s step %d" % (name, i))
+        errs.append(H.check_y(g["y"], ref["y"][sl], cfg, "%s step %d" % (name, i)))
+        unions.append(len(np.unique(r["topk_idx"])))
+        if i < 2:
+            gp = H.layer_outputs(cfg, H.to_dev(xs[i]), W, path="prefill")
+            H.check_routing(gp, r, "%s step %d / prefill" % (name, i))
+            H.check_y(gp["y"], ref["y"][sl], cfg, "%s step %d / prefill" % (name, i))
+    say("   ok %s: %d steps, y err max %.2e median %.2e, expert union mean %.2f"
+        % (name, len(xs), max(errs), float(np.median(errs)), float(np.mean(unions))))
     del W
     torch_cuda.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
-# Full-size prefill workloads c4 / c5
+# Full-size prefill workloads: c4 / c5, c2's int8 layer with a 512-token
+# batch, and the two matrix-core supplements (s1: one dense expert over 4096
+# tokens at d = 6144, s2: c4's layer with 16384 tokens), all on the 256-,
+# 128- or 64-row tiles the library picks for them
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,T", [("c4", None), ("c5", None), ("c2", 512)])
-def test_prefill_workloads(torch_cuda, orc, name, T):
-    """c4 / c5, and the c2 layer (int8 weights) with a 512-token prefill batch
-    through the int8 grouped GEMMs."""
-    cfg = configs.get(name, T=T) if T else configs.get(name)
-    T = cfg["T"]
-    say("case", name, "T", T, "(generating the layer's weights)")
-    W = H.upload_weights_chunked(cfg)
-    x_np = configs.gen_x(cfg)
-    x = H.to_dev(x_np)
+PREFILL = {
+    "c4": dict(base="c4", sample="all"),
+    "c5": dict(base="c5", sample=512),
+    "c2p": dict(base="c2", T=512, sample="all"),
+    "s1": dict(base="c5", over=dict(E=1, k=1, n_shared=0, bias="none"), sample=96),
+    "s2": dict(base="c4", T=16384, sample=256),
+}
+
+
+def _tile_sample(off, perm, k, experts, step):
+    """One token from every ``step`` rows of each listed expert's segment of the
+    grouped order, plus the token of its last row (the ragged tail)."""
+    out = []
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = list(range(lo, hi, step)) + ([hi - 1] if hi > lo else [])
+        out += [int(perm[r]) // k for r in rows]
+    return out
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", sorted(PREFILL))
+def test_prefill_workloads(torch_cuda, orc, name):
+    """Routing and permutation exact on every token; y within tolerance on every
+    token of c4 and c2p, and on a seeded sample of c5, s1 and s2 that holds a
+    token from every 64 rows of the three most loaded experts (so every M tile
+    of every tile size and every slot of the XCD work order that serves them)
+    and of the shared expert, the last rows of the least loaded experts, and
+    seeded random tokens."""
+    spec = PREFILL[name]
+    cfg = configs.get(spec["base"], label=name, **({"T": spec["T"]} if "T" in spec else {}),
+                      **spec.get("over", {}))
+    T, k = cfg["T"], cfg["k"]
+    say("case", name, "T", T, "(generating the layer)")
+    L, W = _host_layer_on_device(cfg)
     say("   running the layer on the GPU")
-    got = H.layer_outputs(cfg, x, W)
-    # routing and permutation on every token
+    got = H.layer_outputs(cfg, W["x"], W)
     say("   oracle routing of all %d tokens" % T)
-    lg, idx, wts = orc.route(cfg, x_np, configs.gen_router(cfg), configs.gen_bias(cfg))
+    lg, idx, wts = orc.route(cfg, L["x"], L["w_router"], L["bias"])
     off, perm, inv = orc.permute(cfg, idx)
     ref = dict(logits=lg, topk_idx=idx, topk_w=wts, offsets=off, perm_rows=perm, inv_perm=inv)
     stats = H.check_routing(got, ref, name)
@@ -111,19 +162,29 @@ def test_prefill_workloads(torch_cuda, orc, name, T):
         share = np.isin(idx, np.where(ranks <= 10)[0]).mean()
         say("   hottest 10 experts receive %.1f%% of selections" % (100 * share))
         assert 0.26 <= share <= 0.34
-    # y on a sample of tokens: first, last, and tokens routed to the hottest expert
-    hot = int(np.argmax(counts))
-    hot_tok = np.where((idx == hot).any(1))[0]
-    sample = sorted(set([0, 1, T // 2, T - 1] + hot_tok[:2].tolist() + hot_tok[-2:].tolist()))
-    Ls = configs.make_layer(cfg, T=T, experts=np.unique(idx[sample]))
-    Ls["x"] = np.ascontiguousarray(x_np[sample])
-    say("   oracle y on tokens", sample)
+    assert np.isfinite(got["y"]).all()
+    if spec["sample"] == "all":
+        sample = np.arange(T)
+    else:
+        hot = np.argsort(-counts, kind="stable")[:3]
+        cold = [int(e) for e in np.argsort(counts, kind="stable") if counts[e] > 0][:3]
+        chosen = set(_tile_sample(off, perm, k, hot, 64) + _tile_sample(off, perm, k, cold, 64))
+        if cfg["n_shared"]:
+            chosen |= set(range(0, T, 64)) | {T - 1}
+        rng = np.random.default_rng(12345)
+        rest = rng.permutation(np.setdiff1d(np.arange(T), sorted(chosen)))
+        n_more = max(0, spec["sample"] - len(chosen))
+        sample = np.array(sorted(chosen | set(rest[:n_more].tolist())))
+        say("   sample: %d tokens (%d from the tiles of experts %s and %s and the shared expert)"
+            % (len(sample), len(chosen), hot.tolist(), cold))
+    Ls = dict(L)
+    Ls["x"] = np.ascontiguousarray(L["x"][sample])
+    say("   oracle y on %d tokens" % len(sample))
     ref_s = orc.layer_forward(cfg, Ls)
     assert np.array_equal(ref_s["topk_idx"], idx[sample])
     err = H.check_y(got["y"][sample], ref_s["y"], cfg, name)
-    say("   ok %s: sampled y err %.2e" % (name, err))
-    assert np.isfinite(got["y"]).all()
-    del W
+    say("   ok %s: y err %.2e over %d tokens" % (name, err, len(sample)))
+    del W, L
     torch_cuda.cuda.empty_cache()
 
 
