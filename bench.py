@@ -2,29 +2,37 @@
 """MoE-layer forward throughput on one MI355X.
 
 One step = one moe_layer_forward (router -> top-k -> grouping -> experts ->
-combine) over one batch of seeded synthetic input.  Default workload: c2, the
-DeepSeek-Flash-style decode layer (T = 1, d = 4096, 256 experts, top-6
-sqrt(softplus) x1.5, F = 2048 + a shared expert, int8 blocks of 32 with an
-fp16 scale, bf16 activations).
+combine) over one batch of seeded synthetic input.
+
+Default run: the headline line is c5, the largest single-GPU configuration
+(T = 4096 tokens, d = 6144, 256 experts top-8 sigmoid + a Zipf-skewed bias,
+F = 2048 + a shared expert, bf16 on the matrix cores); `--steps` / `--warmup`
+apply to it.  The c2 decode layer (T = 1, d = 4096, 256 experts, top-6
+sqrt(softplus) x1.5, int8 blocks of 32 with an fp16 scale, bf16
+activations) is measured after it in the same process, with its own step
+count, and carried in the same JSON line under "decode".  `--workload`
+measures one workload alone.
 
 Decode steps walk 1024 distinct tokens and rotate over several full copies of
 the layer's weights (27 GB for c2), so the 256 MB Infinity Cache cannot serve
 one step's expert weights to the next: every step reads its experts from HBM.
-Prefill workloads (--workload c4 / c5) run one layer copy (19 GB, far beyond
-any cache) on a fixed batch.
+Prefill workloads run one layer copy (19 GB, far beyond any cache) on a fixed
+batch.
 
 Output: one JSON line.  `value` = tokens per second of the whole timed region
 (inputs resident in HBM).  `roofline` describes the dominant kernel (the
-gate/up stage): algorithmic bytes per launch divided by its average duration.
-The durations come from HIP events that the library attaches to its own
-kernel dispatches on its stream (hipExtLaunchKernel start/stop timestamps, the
-same ones a kernel trace reads): during the timed steps for prefill, in a
-second eager pass of the same steps for decode, whose ~50 us steps those
-per-dispatch timestamps would slow by ~40 us.  `traffic` is
-the HBM byte count from rocprofv3 counters recorded in profiles/traffic.json,
-or null when that record was taken on a different version of the kernel
-source.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+gate/up stage): algorithmic bytes (or flops, when the launch's matrix-core
+time exceeds its HBM time) per launch divided by its average duration.  The
+durations come from HIP events that the library attaches to its own kernel
+dispatches on its stream (hipExtLaunchKernel start/stop timestamps, the same
+ones a kernel trace reads): during the timed steps for prefill, in a second
+eager pass of the same steps for decode, whose ~50 us steps those
+per-dispatch timestamps would slow by ~40 us.  `per_step_ms` (p50 / p90) comes
+from a third pass with an event between consecutive steps.  `traffic` is the
+HBM byte count from rocprofv3 counters recorded in profiles/traffic.json, or
+null when that record was taken on a different version of the kernel source.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload,
+on all host threads and on one.
 """
 from __future__ import annotations
 
@@ -284,32 +292,6 @@ def copy_probe(torch, hip, stream, mib):
     return round(3 * 2 * n * 4 / (ms * 1e-3) / 1e9, 1)
 
 
-def cpu_baseline(cfg, L, x_all, target_s=12.0):
-    """The oracle, as it stands, on a bounded sample of the workload: the
-    sample grows (8 tokens, then as the last call's rate suggests) until one
-    call takes at least half of ``target_s`` seconds; that call is reported."""
-    import numpy as np
-    from oracle import Oracle
-    orc = Oracle()
-    threads = orc.threads()
-
-    def run(n):
-        Ls = dict(L)
-        Ls["x"] = np.ascontiguousarray(x_all[:n])
-        t0 = time.perf_counter()
-        orc.layer_forward(cfg, Ls, debug=False)
-        return time.perf_counter() - t0
-
-    n, cap = 8, x_all.shape[0]
-    dt = run(n)
-    while dt < target_s / 2 and n < cap:
-        n = int(min(cap, max(2 * n, n * target_s / max(dt, 1e-3))))
-        dt = run(n)
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d tokens of the same workload in one call (token-major fp64 oracle, %d OpenMP threads),"
-                      " %.1f s wall" % (n, threads, dt)}
-
-
 def bench_topk_rows(args):
     """Row top-k (moe_topk_rows): one step = one call over every row of the
     workload.  value = rows per second; roofline: the kernel's algorithmic
@@ -432,12 +414,80 @@ def cpu_baseline_topk(spec, host, target_s=12.0):
                       "thread, %d threads), %.2f s wall" % (n_rows, reps, threads, dt)}
 
 
-def main():
+def dtype_of(cfg):
+    """The arithmetic the layer's expert kernels compute in."""
+    return {"q8b32": "int8xbf16", "bf16": "bf16", "f32": "f32"}[cfg["w"]]
+
+
+DTYPE_NOTE = {
+    "int8xbf16": "int8 weights in blocks of 32 with an fp16 scale, dequantised exactly in registers, times bf16 "
+                 "activations; fp32 accumulation; router fp32 weights with fp64 accumulation",
+    "bf16": "bf16 weights and activations on the bf16 matrix cores, fp32 accumulation; router fp32 weights with "
+            "fp64 accumulation",
+    "f32": "fp32 weights and activations, fp32 accumulation",
+}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, L, x_all, target_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the workload, on all the
+    host threads it was built for (OpenMP over tokens) and on one thread: the
+    sample grows (from 8 tokens, or 1 on one thread, as the last call's rate
+    suggests) until one call takes at least half of its target; that call is
+    reported.  One thread gets a third of ``target_s``."""
+    import numpy as np
+    from oracle import Oracle
+    orc = Oracle()
+    threads = orc.threads()
+
+    def run(n):
+        Ls = dict(L)
+        Ls["x"] = np.ascontiguousarray(x_all[:n])
+        t0 = time.perf_counter()
+        orc.layer_forward(cfg, Ls, debug=False)
+        return time.perf_counter() - t0
+
+    def grow(n, target):
+        cap = x_all.shape[0]
+        dt = run(n)
+        while dt < target / 2 and n < cap:
+            n = int(min(cap, max(2 * n, n * target / max(dt, 1e-3))))
+            dt = run(n)
+        return n, dt
+
+    n, dt = grow(min(8, x_all.shape[0]), target_s)
+    prev = orc.set_threads(1)
+    try:
+        n1, dt1 = grow(1, target_s / 3)
+    finally:
+        orc.set_threads(prev)
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d tokens of the same workload in one call (token-major fp64 oracle, %d OpenMP threads),"
+                      " %.1f s wall" % (n, threads, dt),
+            "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": "%d tokens in one call, %.1f s wall" % (n1, dt1)},
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS) + sorted(TOPK_WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(TOPK_WORKLOADS),
+                    help="one workload alone; default: c5 as the headline with the c2 decode layer beside it")
+    ap.add_argument("--no-decode", action="store_true", help="default run: leave out the c2 decode section")
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated across steps")
     ap.add_argument("--tokens", type=int, default=None,
                     help="tokens per step instead of the workload's (small-batch sweeps)")
@@ -461,18 +511,23 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv "
                          "files of a run made with --copy-probe-mib")
-    args = ap.parse_args()
-    if args.record_traffic and args.workload in TOPK_WORKLOADS:
-        record_traffic(args.workload, None, None, args.record_traffic[0], args.record_traffic[1],
-                       (args.copy_probe_mib or 1024) * (1 << 20))
-        return
+    return ap.parse_args(argv)
+
+
+def main():
+    args = parse_args()
     if args.record_traffic:
+        wl = args.workload or "c5"
+        if wl in TOPK_WORKLOADS:
+            record_traffic(wl, None, None, args.record_traffic[0], args.record_traffic[1],
+                           (args.copy_probe_mib or 1024) * (1 << 20))
+            return
         from synth import configs as _cf
         from sparse_moe_layer_02_amd.binding import DECODE_MAX_TOKENS
-        spec = WORKLOADS[args.workload]
-        cfg = _cf.get(spec["base"], T=spec["T"], **spec.get("over", {}))
+        spec = WORKLOADS[wl]
+        cfg = _cf.get(spec["base"], T=args.tokens or spec["T"], **spec.get("over", {}))
         dec = args.path == "decode" or (args.path == "auto" and cfg["T"] <= DECODE_MAX_TOKENS)
-        record_traffic(args.workload, "decode" if dec else "prefill", cfg["w"], args.record_traffic[0],
+        record_traffic(wl, "decode" if dec else "prefill", cfg["w"], args.record_traffic[0],
                        args.record_traffic[1], (args.copy_probe_mib or 1024) * (1 << 20), rpe=rows_per_expert(cfg))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -484,15 +539,35 @@ def main():
 
     if args.workload in TOPK_WORKLOADS:
         return bench_topk_rows(args)
+    if args.workload is not None:
+        out = measure_layer(args, args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
+        print(json.dumps(out), flush=True)
+        return
+    # Default: the largest configuration (c5, 4096-token skewed prefill) is the
+    # headline line; the c2 decode layer is measured in the same process after
+    # it (its own step count and weight copies) and carried under "decode".
+    out = measure_layer(args, "c5", args.steps, args.warmup, not args.no_cpu_baseline)
+    if not args.no_decode:
+        dec = measure_layer(args, "c2", None, None, not args.no_cpu_baseline)
+        keep = ("value", "unit", "steps", "warmup", "ms_per_step", "per_step_ms", "dtype", "dtype_note", "config",
+                "roofline", "layer_hbm_GBs", "layer_hbm_frac", "layer_bytes", "layer_roofline_frac",
+                "expert_union_mean", "stages_us", "cpu_baseline")
+        out["decode"] = {key: dec[key] for key in keep if key in dec}
+    print(json.dumps(out), flush=True)
 
+
+def measure_layer(args, wname, steps, warmup, with_cpu):
+    """One layer workload: warm-up, the timed steps (one pair of events around
+    all of them), the per-stage kernel times, a pass with an event between
+    steps for the per-step distribution, and the oracle on the host cores."""
     import numpy as np
     import torch
     import sparse_moe_layer_02_amd as moe
     from synth import configs
 
-    spec = WORKLOADS[args.workload]
-    steps = args.steps or spec["steps"]
-    warmup = spec["warmup"] if args.warmup is None else args.warmup
+    spec = WORKLOADS[wname]
+    steps = steps or spec["steps"]
+    warmup = spec["warmup"] if warmup is None else warmup
     cfg = configs.get(spec["base"], T=args.tokens or spec["T"], **spec.get("over", {}))
     T = cfg["T"]
     decode = args.path == "decode" or (args.path == "auto" and T <= moe.DECODE_MAX_TOKENS)
@@ -640,12 +715,25 @@ def main():
         torch.cuda.synchronize()
     stage_ms = np.zeros((steps, len(stage_names)))
     for i in range(steps):
-        for c, s in enumerate(stage_ids):
-            stage_ms[i, c] = hip.ms(ev[i][2 * s], ev[i][2 * s + 1])
+        for col, sid in enumerate(stage_ids):
+            stage_ms[i, col] = hip.ms(ev[i][2 * sid], ev[i][2 * sid + 1])
     for row in ev:
         for e in row:
             hip.destroy(e)
-    stages_us = {name: round(float(stage_ms[:, c].mean()) * 1e3, 2) for c, name in enumerate(stage_names)}
+    stages_us = {name: round(float(stage_ms[:, col].mean()) * 1e3, 2) for col, name in enumerate(stage_names)}
+
+    # ---- per-step distribution: the same steps with an event between steps --
+    sev = [hip.event() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    hold(0.2 * steps)
+    hip.record(sev[0], stream)
+    for i in range(steps):
+        step(warmup + i)
+        hip.record(sev[i + 1], stream)
+    hip.sync(sev[-1])
+    per_step = np.array([hip.ms(sev[i], sev[i + 1]) for i in range(steps)])
+    for e in sev:
+        hip.destroy(e)
 
     # ---- algorithmic work -------------------------------------------------
     idx_np = idx_log.cpu().numpy()
@@ -661,11 +749,16 @@ def main():
         gu_bytes = (n_exp * expert_bytes(cfg, 2) + T * cfg["d"] * act_bytes
                     + (T * cfg["k"] + T * cfg["n_shared"]) * cfg["F"] * act_bytes)
         flops_gu = 2.0 * (T * cfg["k"] + T * cfg["n_shared"]) * cfg["d"] * 2 * cfg["F"]
+    layer_flops = 2.0 * (T * cfg["k"] + T * cfg["n_shared"]) * cfg["d"] * 3 * cfg["F"]
     gu_us = stages_us["gate_up"]
     achieved = float(np.mean(gu_bytes)) / (gu_us * 1e-6) / 1e9
     path_kind = "decode" if decode else "prefill"
-    traffic = traffic_record(path_kind, cfg["w"], args.workload, rows_per_expert(cfg))
-    if spec.get("bound") == "mfma":
+    traffic = traffic_record(path_kind, cfg["w"], wname, rows_per_expert(cfg))
+    # the gate/up launch's own roofline: HBM time of its algorithmic bytes
+    # against matrix-core time of its flops (bf16 peak), whichever is longer
+    mfma_bound = spec.get("bound") == "mfma" or (
+        not decode and cfg["w"] == "bf16" and flops_gu / (BF16_PEAK_TFS * 1e12) > float(np.mean(gu_bytes)) / (HBM_PEAK_GBS * 1e9))
+    if mfma_bound:
         tfs = flops_gu / (gu_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_PEAK_TFS, "unit": "TFLOP/s",
                     "frac": round(tfs / BF16_PEAK_TFS, 4), "traffic": traffic,
@@ -682,7 +775,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32" if decode else "bf16",
+        "dtype": dtype_of(cfg), "dtype_note": DTYPE_NOTE[dtype_of(cfg)],
         "data": "synthetic (seeded counter-based generator; random-init weights of the layer's shape)",
         "config": {"workload": describe(cfg), "T": T, "d_model": cfg["d"], "n_expert": cfg["E"],
                    "top_k": cfg["k"], "d_ff": cfg["F"], "weights": cfg["w"], "activations": cfg["act"],
@@ -693,6 +786,13 @@ def main():
         "layer_hbm_GBs": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
         "layer_hbm_frac": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_bytes": float(np.mean(layer_bytes)),
+        "layer_roofline_frac": round(max(float(np.mean(layer_bytes)) / (HBM_PEAK_GBS * 1e9),
+                                         (layer_flops / (BF16_PEAK_TFS * 1e12)) if cfg["w"] == "bf16" else 0.0)
+                                     / (ms_per_step * 1e-3), 4),
+        "per_step_ms": {"p50": round(float(np.percentile(per_step, 50)), 5),
+                        "p90": round(float(np.percentile(per_step, 90)), 5),
+                        "min": round(float(per_step.min()), 5), "max": round(float(per_step.max()), 5),
+                        "note": "a separate eager pass of the same steps with an event between consecutive steps"},
         "expert_union_mean": float(unions.mean()),
         "stages_us": stages_us,
         "gate_up_tflops": round(flops_gu / (gu_us * 1e-6) / 1e12, 2),
@@ -718,11 +818,11 @@ def main():
         out["copy_probe_bytes"] = args.copy_probe_mib * (1 << 20)
 
     # ---- the oracle on the host cores -----------------------------------
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, L, x_all, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    out["cpu_baseline"] = cpu_baseline(cfg, L, x_all, args.cpu_seconds) if with_cpu else None
+    del copies, Wc, x_dev, ws, L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

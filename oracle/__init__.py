@@ -81,6 +81,8 @@ def load(path: str | None = None):
     lib.moe_ref_status_str.restype = ctypes.c_char_p
     lib.moe_ref_mutant.restype = ctypes.c_int
     lib.moe_ref_threads.restype = ctypes.c_int
+    lib.moe_ref_set_threads.argtypes = [ctypes.c_int]
+    lib.moe_ref_set_threads.restype = ctypes.c_int
     if path == _build.LIB:
         _lib, _lib_path = lib, path
     return lib
@@ -230,3 +232,7 @@ class Oracle:
 
     def threads(self):
         return self.lib.moe_ref_threads()
+
+    def set_threads(self, n):
+        """Threads of the token loops from now on; returns the previous count."""
+        return self.lib.moe_ref_set_threads(int(n))

@@ -36,6 +36,19 @@ int moe_ref_threads(void) {
 #endif
 }
 
+/* Threads of the token loops from now on (n >= 1); returns the previous count.
+ * Results do not depend on it: every output element is computed by one thread
+ * in a fixed order. */
+int moe_ref_set_threads(int n) {
+    const int prev = moe_ref_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}
+
 const char *moe_ref_status_str(int status) {
     switch (status) {
     case MOE_REF_OK: return "ok";

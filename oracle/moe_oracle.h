@@ -111,6 +111,7 @@ float moe_ref_score(int32_t score, float logit);
 const char *moe_ref_status_str(int status);
 int moe_ref_mutant(void); /* which planted mistake this compiled copy carries (0 = none) */
 int moe_ref_threads(void); /* OpenMP threads the token loops use */
+int moe_ref_set_threads(int n); /* set them (n >= 1); returns the previous count */
 
 #ifdef __cplusplus
 }
