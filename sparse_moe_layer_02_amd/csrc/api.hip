@@ -59,15 +59,32 @@ int ldh_of(const moe_config* c) {
     return c->n_shared ? (c->d_ff > c->d_ff_shared ? c->d_ff : c->d_ff_shared) : c->d_ff;
 }
 
-// Rows per grouped-GEMM tile: 256 (the LDS-copy kernels of
-// grouped_gemm_dma.hip) once experts average 256 rows or more, 128 from 96
-// rows (fewer re-reads of each weight tile, more MFMA work per LDS byte), else
-// 64.  int8 weights always take 64-row tiles (grouped_gemm_q8.hip).
-int gemm_bm(const moe_config* c) {
-    if (c->w_dtype == MOE_DT_Q8B32) return 64;
+// Grouped-GEMM tiles.  bm: rows per tile of the small-tile list; bm_big /
+// big_min: groups (experts, or the shared expert over all tokens) with at
+// least big_min rows take tiles of bm_big rows instead, in a second launch of
+// the LDS-copy kernels (grouped_gemm_dma.hip).
+//  - experts averaging 256 rows or more: every group on 256-row tiles;
+//  - 96 to 255 on average (a long or skewed prefill: a few hot experts hold
+//    most rows, the rest are bandwidth-bound): groups of SPLIT_BIG_MIN rows or
+//    more on 256-row tiles (compute-bound, fewer re-reads of each weight
+//    tile), the others on SPLIT_BM-row tiles;
+//  - fewer: 64-row tiles (every expert bandwidth-bound).
+//  int8 weights always take 64-row tiles (grouped_gemm_q8.hip).
+#ifndef SPLIT_BIG_MIN
+#define SPLIT_BIG_MIN 192
+#endif
+#ifndef SPLIT_BM
+#define SPLIT_BM 128
+#endif
+struct TilePlan {
+    int bm, bm_big, big_min;
+};
+TilePlan tile_plan(const moe_config* c) {
+    if (c->w_dtype == MOE_DT_Q8B32) return {64, 0, 0};
     const long n = (long)c->n_tokens * c->top_k;
-    if (n >= 256L * c->n_expert) return 256;
-    return n >= 96L * c->n_expert ? 128 : 64;
+    if (n >= 256L * c->n_expert) return {256, 0, 0};
+    if (n >= 96L * c->n_expert) return {SPLIT_BM, 256, SPLIT_BIG_MIN};
+    return {64, 0, 0};
 }
 
 // Upper bound on the tiles of bm rows: every expert's last tile may be partial.
@@ -166,7 +183,10 @@ PermArgs perm_args(const moe_config* c, const Layout& L, void* ws, const int32_t
     p.active = at<int32_t>(ws, L.active);
     p.tiles = at<int2>(ws, L.tiles);
     p.n_blk = L.n_blk;
-    p.bm = gemm_bm(c);
+    const TilePlan tp = tile_plan(c);
+    p.bm = tp.bm;
+    p.bm_big = tp.bm_big;
+    p.big_min = tp.big_min;
     return p;
 }
 
@@ -200,8 +220,12 @@ FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, 
     f.slot_out = at<float>(ws, L.slot_out);
     f.shared_out = c->n_shared ? at<float>(ws, L.shared_out) : nullptr;
     f.y = nullptr;
-    f.bm = gemm_bm(c);
+    const TilePlan tp = tile_plan(c);
+    f.bm = tp.bm;
     f.max_tiles = max_tiles_of(c, f.bm);
+    f.list = 0;
+    f.bm_big = tp.bm_big;
+    f.max_big_tiles = tp.bm_big ? max_tiles_of(c, tp.bm_big) : 0;
     f.shared_done = 0;
     f.grid_has_shared = 0;
     f.dslots = at<DecodeSlot>(ws, L.dslots);
@@ -216,12 +240,33 @@ bool q8_mfma(const FfnArgs& f) { return f.wdt == MOE_DT_Q8B32 && (long)f.T * f.k
 
 // Experts of the prefill path: MFMA for bf16 weights and for int8 weights with
 // enough rows per expert, GEMVs otherwise.
+// bf16 experts on the matrix cores: the big-tile list (if any) first, then the
+// small-tile list, for gate/up and then for down.  kt times the gate/up and
+// down stages from their first launch to their last.
+FfnArgs big_list(const FfnArgs& f) {
+    FfnArgs b = f;
+    b.list = 1;
+    b.bm = f.bm_big;
+    b.max_tiles = f.max_big_tiles;
+    return b;
+}
+hipError_t run_bf16_experts(const FfnArgs& f, hipStream_t st, const KTime& kg = KTime(),
+                            const KTime& kd = KTime()) {
+    hipError_t e;
+    if (f.bm_big) {
+        const FfnArgs b = big_list(f);
+        if ((e = launch_gateup_dma(b, st, kg.first())) != hipSuccess) return e;
+        if ((e = launch_gateup_mfma(f, st, kg.last())) != hipSuccess) return e;
+        if ((e = launch_down_dma(b, st, kd.first())) != hipSuccess) return e;
+        return launch_down_mfma(f, st, kd.last());
+    }
+    if ((e = launch_gateup_mfma(f, st, kg)) != hipSuccess) return e;
+    return launch_down_mfma(f, st, kd);
+}
+
 hipError_t run_expert_kernels(const FfnArgs& f, hipStream_t st) {
     hipError_t e;
-    if (f.wdt == MOE_DT_BF16) {
-        if ((e = launch_gateup_mfma(f, st)) != hipSuccess) return e;
-        return launch_down_mfma(f, st);
-    }
+    if (f.wdt == MOE_DT_BF16) return run_bf16_experts(f, st);
     if (q8_mfma(f)) {
         if ((e = launch_gateup_mfma_q8(f, st)) != hipSuccess) return e;
         return launch_down_mfma_q8(f, st);
@@ -516,8 +561,7 @@ int enqueue_layer(const moe_config* cfg, const void* x, const moe_weights* w, fl
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     FfnArgs f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
     if (f.wdt == MOE_DT_BF16) {
-        e = launch_gateup_mfma(f, st, kt[3]);
-        if (e == hipSuccess) e = launch_down_mfma(f, st, kt[4]);
+        e = run_bf16_experts(f, st, kt[3], kt[4]);
     } else if (q8_mfma(f)) {
         e = launch_gateup_mfma_q8(f, st, kt[3]);
         if (e == hipSuccess) e = launch_down_mfma_q8(f, st, kt[4]);

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + 2 * GU_BN) * ROWB];
     __shared__ int src_row[BM];
     int tile, ntile;
-    if (!work_item<BM == 128 ? 4 : 16>(a.meta[1], tile, ntile)) return;
+    if (!work_item<BM == 128 ? 4 : 16>(tile_count(a), tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
     int tile, ntile;
-    if (!work_item<BM == 128 ? 4 : 16>(a.meta[1], tile, ntile)) return;
+    if (!work_item<BM == 128 ? 4 : 16>(tile_count(a), tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;

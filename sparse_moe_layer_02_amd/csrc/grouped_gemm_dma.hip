@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t L3[GEO::STAGE];
     __shared__ int src_row[BM];
     int tile, ntile;
-    if (!work_item<4>(a.meta[1], tile, ntile)) return;
+    if (!work_item<4>(tile_count(a), tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
     int tile, ntile;
-    if (!work_item<4>(a.meta[1], tile, ntile)) return;
+    if (!work_item<4>(tile_count(a), tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_q8_kernel(FfnArgs a) {
     __shared__ float lsc[2][2 * GU_BN][2];  // per chunk: scale of (B row, block)
     __shared__ int src_row[BM];
     int tile, ntile;
-    if (!work_item<BM == 128 ? 4 : 16>(a.meta[1], tile, ntile)) return;
+    if (!work_item<BM == 128 ? 4 : 16>(tile_count(a), tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void down_mfma_q8_kernel(FfnArgs a) {
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
     int tile, ntile;
-    if (!work_item<BM == 128 ? 4 : 16>(a.meta[1], tile, ntile)) return;
+    if (!work_item<BM == 128 ? 4 : 16>(tile_count(a), tile, ntile)) return;
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;

@@ -321,10 +321,12 @@ def _store(cfg, w, rng):
     return (np.ascontiguousarray(q.astype(np.int8)), np.ascontiguousarray(scale_bits))
 
 
-def exact_layer(T, d, E, k, F, Fs=None, n_shared=1, act="bf16", w="bf16", seed=0):
+def exact_layer(T, d, E, k, F, Fs=None, n_shared=1, act="bf16", w="bf16", seed=0, skew=0.0):
     """A layer (dict as :func:`make_layer`, with its workload dict under
     ``cfg``) on which the method's arithmetic is exact (see above).  Sigmoid
-    router, no bias, scale 1; k must be 1, 2, 4 or 8 and d >= E + 2."""
+    router, no bias, scale 1; k must be 1, 2, 4 or 8 and d >= E + 2.  With
+    ``skew`` > 0 each token's expert subset is drawn with probabilities
+    proportional to (e + 1)^-skew, so low-numbered experts get many rows."""
     assert k in (1, 2, 4, 8) and k <= E and d >= E + 2 and d % 64 == 0
     Fs = F if Fs is None else Fs
     cfg = custom(T=T, d=d, E=E, k=k, F=F, Fs=Fs, n_shared=n_shared, score="sigmoid", scale=1.0, act=act,
@@ -332,8 +334,10 @@ def exact_layer(T, d, E, k, F, Fs=None, n_shared=1, act="bf16", w="bf16", seed=0
     rng = np.random.default_rng(seed)
     lift, one = E, E + 1
     x = np.zeros((T, d))
+    prob = (np.arange(E) + 1.0) ** -skew
+    prob /= prob.sum()
     for t in range(T):
-        x[t, rng.choice(E, k, replace=False)] = 1.0
+        x[t, rng.choice(E, k, replace=False, p=prob)] = 1.0
     x[:, lift] = 32.0
     x[:, one] = 1.0
     x[:, E + 2:] = rng.integers(-2, 3, (T, d - E - 2))

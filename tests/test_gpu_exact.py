@@ -42,6 +42,11 @@ CASES = {
     "prefill_bm64_no_shared": dict(T=70, d=192, E=8, k=2, F=64, n_shared=0),
     # 128-row tiles (96 to 255 rows per expert), odd 64-wide K chunks
     "prefill_bm128": dict(T=300, d=192, E=4, k=2, F=320, Fs=448),
+    # 96 to 255 rows per expert on average with skewed loads: experts with 256
+    # rows or more (and the shared expert) on the big-tile list, the rest on
+    # 128-row tiles
+    "prefill_split_skewed": dict(T=800, d=256, E=16, k=2, F=192, skew=1.2),
+    "prefill_split_no_shared": dict(T=700, d=192, E=12, k=2, F=128, n_shared=0, skew=1.0),
     # 256-row tiles through LDS copies (256 rows per expert or more)
     "prefill_bm256": dict(T=700, d=320, E=2, k=2, F=320, Fs=448),
     "prefill_bm256_d6144": dict(T=600, d=6144, E=2, k=1, F=2048),
@@ -81,7 +86,8 @@ def test_exact_layer_bitwise(orc, case):
             assert _bits_equal(got_p[key], ref[key]), (case, "prefill", key)
 
 
-@pytest.mark.parametrize("case", ["prefill_bm64", "prefill_bm256", "prefill_q8_mfma", "decode_q8_T5"])
+@pytest.mark.parametrize("case", ["prefill_bm64", "prefill_split_skewed", "prefill_bm256", "prefill_q8_mfma",
+                                  "decode_q8_T5"])
 def test_exact_split_entry_points(orc, case):
     """moe_expert_ffn and moe_combine alone, with caller routing weights that
     are powers of two: slot_out, shared_out and y bit for bit."""
