@@ -59,32 +59,18 @@ int ldh_of(const moe_config* c) {
     return c->n_shared ? (c->d_ff > c->d_ff_shared ? c->d_ff : c->d_ff_shared) : c->d_ff;
 }
 
-// Grouped-GEMM tiles.  bm: rows per tile of the small-tile list; bm_big /
-// big_min: groups (experts, or the shared expert over all tokens) with at
-// least big_min rows take tiles of bm_big rows instead, in a second launch of
-// the LDS-copy kernels (grouped_gemm_dma.hip).
-//  - experts averaging 256 rows or more: every group on 256-row tiles;
-//  - 96 to 255 on average (a long or skewed prefill: a few hot experts hold
-//    most rows, the rest are bandwidth-bound): groups of SPLIT_BIG_MIN rows or
-//    more on 256-row tiles (compute-bound, fewer re-reads of each weight
-//    tile), the others on SPLIT_BM-row tiles;
-//  - fewer: 64-row tiles (every expert bandwidth-bound).
-//  int8 weights always take 64-row tiles (grouped_gemm_q8.hip).
-#ifndef SPLIT_BIG_MIN
-#define SPLIT_BIG_MIN 192
-#endif
-#ifndef SPLIT_BM
-#define SPLIT_BM 128
-#endif
-struct TilePlan {
-    int bm, bm_big, big_min;
-};
-TilePlan tile_plan(const moe_config* c) {
-    if (c->w_dtype == MOE_DT_Q8B32) return {64, 0, 0};
+// Rows per grouped-GEMM tile.  256 (the LDS-copy kernels of
+// grouped_gemm_dma.hip) once experts average 96 rows or more: a long or skewed
+// prefill, where a few hot experts hold most rows (compute-bound) and the
+// rest are bandwidth-bound; those kernels compute only the 32-row blocks of a
+// tile that hold rows, so a short tile costs its weight stream, not a full
+// 256-row product.  Fewer rows per expert: 64-row tiles (every expert
+// bandwidth-bound; the register-staged kernels keep more loads in flight per
+// CU).  int8 weights always take 64-row tiles (grouped_gemm_q8.hip).
+int gemm_bm(const moe_config* c) {
+    if (c->w_dtype == MOE_DT_Q8B32) return 64;
     const long n = (long)c->n_tokens * c->top_k;
-    if (n >= 256L * c->n_expert) return {256, 0, 0};
-    if (n >= 96L * c->n_expert) return {SPLIT_BM, 256, SPLIT_BIG_MIN};
-    return {64, 0, 0};
+    return n >= 96L * c->n_expert ? 256 : 64;
 }
 
 // Upper bound on the tiles of bm rows: every expert's last tile may be partial.
@@ -183,10 +169,7 @@ PermArgs perm_args(const moe_config* c, const Layout& L, void* ws, const int32_t
     p.active = at<int32_t>(ws, L.active);
     p.tiles = at<int2>(ws, L.tiles);
     p.n_blk = L.n_blk;
-    const TilePlan tp = tile_plan(c);
-    p.bm = tp.bm;
-    p.bm_big = tp.bm_big;
-    p.big_min = tp.big_min;
+    p.bm = gemm_bm(c);
     return p;
 }
 
@@ -220,12 +203,8 @@ FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, 
     f.slot_out = at<float>(ws, L.slot_out);
     f.shared_out = c->n_shared ? at<float>(ws, L.shared_out) : nullptr;
     f.y = nullptr;
-    const TilePlan tp = tile_plan(c);
-    f.bm = tp.bm;
+    f.bm = gemm_bm(c);
     f.max_tiles = max_tiles_of(c, f.bm);
-    f.list = 0;
-    f.bm_big = tp.bm_big;
-    f.max_big_tiles = tp.bm_big ? max_tiles_of(c, tp.bm_big) : 0;
     f.shared_done = 0;
     f.grid_has_shared = 0;
     f.dslots = at<DecodeSlot>(ws, L.dslots);
@@ -240,26 +219,10 @@ bool q8_mfma(const FfnArgs& f) { return f.wdt == MOE_DT_Q8B32 && (long)f.T * f.k
 
 // Experts of the prefill path: MFMA for bf16 weights and for int8 weights with
 // enough rows per expert, GEMVs otherwise.
-// bf16 experts on the matrix cores: the big-tile list (if any) first, then the
-// small-tile list, for gate/up and then for down.  kt times the gate/up and
-// down stages from their first launch to their last.
-FfnArgs big_list(const FfnArgs& f) {
-    FfnArgs b = f;
-    b.list = 1;
-    b.bm = f.bm_big;
-    b.max_tiles = f.max_big_tiles;
-    return b;
-}
+// bf16 experts on the matrix cores: gate/up, then down.
 hipError_t run_bf16_experts(const FfnArgs& f, hipStream_t st, const KTime& kg = KTime(),
                             const KTime& kd = KTime()) {
     hipError_t e;
-    if (f.bm_big) {
-        const FfnArgs b = big_list(f);
-        if ((e = launch_gateup_dma(b, st, kg.first())) != hipSuccess) return e;
-        if ((e = launch_gateup_mfma(f, st, kg.last())) != hipSuccess) return e;
-        if ((e = launch_down_dma(b, st, kd.first())) != hipSuccess) return e;
-        return launch_down_mfma(f, st, kd.last());
-    }
     if ((e = launch_gateup_mfma(f, st, kg)) != hipSuccess) return e;
     return launch_down_mfma(f, st, kd);
 }

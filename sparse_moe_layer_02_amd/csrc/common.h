@@ -124,9 +124,8 @@ struct Layout {
     int max_tiles;   // capacity of the grouped-GEMM tile list
 };
 
-// Meta words at ws + meta: [0] n_active experts, [1] tiles of the small-tile
-// list (at tiles[0 ..]), [2] valid assignments, [3] tiles of the big-tile list,
-// [4] its first index in tiles[], the rest reserved.
+// Meta words at ws + meta: [0] n_active experts, [1] n_tiles, [2] valid
+// assignments, the rest reserved.
 constexpr int META_WORDS = 16;
 constexpr int PERM_BLOCK = 256;     // assignments per permutation block (one wave)
 constexpr int GEMM_BM = 64;         // rows per grouped-GEMM tile (tile list granularity)

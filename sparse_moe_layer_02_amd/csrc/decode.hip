@@ -204,8 +204,6 @@ __device__ void group_in_registers(const DecodeRouteArgs& a, const int32_t* s_id
     if (lane == 0) {
         a.p.meta[0] = na;
         a.p.meta[1] = 0;
-        a.p.meta[3] = 0;
-        a.p.meta[4] = 0;
         a.p.meta[2] = n;
     }
 }
@@ -267,8 +265,6 @@ __global__ __launch_bounds__(DS_THREADS) void decode_select_kernel(DecodeRouteAr
         a.p.offsets[E] = total;
         a.p.meta[0] = na;
         a.p.meta[1] = 0;
-        a.p.meta[3] = 0;
-        a.p.meta[4] = 0;
         a.p.meta[2] = total;
     }
     PermArgs p = a.p;

@@ -12,13 +12,13 @@ struct TileRows {
     int nrows;    // valid rows (<= BM)
 };
 
-// Tiles in the list this launch walks (the device-side count).
-__device__ __forceinline__ int tile_count(const FfnArgs& a) { return a.list ? a.meta[3] : a.meta[1]; }
+// Tiles in the list (the device-side count the permutation step wrote).
+__device__ __forceinline__ int tile_count(const FfnArgs& a) { return a.meta[1]; }
 
 template <int BM>
 __device__ __forceinline__ bool tile_rows(const FfnArgs& a, int tile, TileRows& tr) {
     if (tile >= tile_count(a)) return false;
-    const int2 t = a.tiles[(a.list ? a.meta[4] : 0) + tile];
+    const int2 t = a.tiles[tile];
     tr.g = t.x;
     if (t.x == a.E) {  // shared expert: rows are tokens
         tr.rbeg = a.T * a.k + t.y;

@@ -14,7 +14,8 @@
 // port").
 //
 // Work list: the permutation step writes tiles (group, first row) of bm rows
-// (128 when experts average 96 rows or more, else 64); the grid is (tile
+// (64; layers averaging 96 rows per expert or more take the LDS-copy
+// kernels of grouped_gemm_dma.hip instead); the grid is (tile
 // slot, N tile), remapped per XCD (work_item), and slots past the
 // device-side count exit at once.  A workgroup computes bm rows by 64 gate
 // + 64 up columns (gate/up) or by 128 output columns (down), K staged
@@ -335,18 +336,18 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
 
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     if (a.bm == 256) return launch_gateup_dma(a, st, kt);
+    if (a.bm != 64) return hipErrorInvalidValue;
     const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
     dim3 grid(a.max_tiles, (fmax + GU_BN - 1) / GU_BN);
-    if (a.bm == 128) launch_kernel(gateup_mfma_kernel<128>, grid, 256, st, kt, a);
-    else launch_kernel(gateup_mfma_kernel<64>, grid, 256, st, kt, a);
+    launch_kernel(gateup_mfma_kernel<64>, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     if (a.bm == 256) return launch_down_dma(a, st, kt);
+    if (a.bm != 64) return hipErrorInvalidValue;
     dim3 grid(a.max_tiles, (a.d + DN_BN - 1) / DN_BN);
-    if (a.bm == 128) launch_kernel(down_mfma_kernel<128>, grid, 256, st, kt, a);
-    else launch_kernel(down_mfma_kernel<64>, grid, 256, st, kt, a);
+    launch_kernel(down_mfma_kernel<64>, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
-// grouped_gemm_dma.hip - the prefill grouped GEMMs for experts with many rows:
-// one workgroup per CU, each wavefront a 64- or 128-row by 128-column block of
-// v_mfma_f32_32x32x16_bf16 accumulators, operands fed straight from global
-// memory into LDS.
+// grouped_gemm_dma.hip - the prefill grouped GEMMs for layers whose experts
+// average 96 rows or more (a long or skewed prefill: hot experts with
+// hundreds of rows beside cold ones with a few): one workgroup per CU, each
+// wavefront a 64- or 128-row by 128-column block of v_mfma_f32_32x32x16_bf16
+// accumulators, operands fed straight from global memory into LDS.
 //
 //   gate/up:  H_e = bf16( silu(A_e Wg[e]^T) * (A_e Wu[e]^T) ),  A_e = rows of x
 //             gathered through the permutation
@@ -27,6 +28,16 @@
 // fragments of the next stage are issued between the MFMAs of the second step
 // (instruction order pinned with scheduling barriers, since one wavefront per
 // SIMD has no other wavefront to hide latency behind).
+//
+// Short tiles.  A tile computes only its 32-row blocks that hold rows (an
+// expert's last tile, or an expert with few rows): row blocks are dealt to the
+// two wavefront rows in turn, so every SIMD keeps the same share of the
+// remaining MFMAs, and A-row copies that reach no row are not issued.  Each
+// wavefront runs the K loop instantiated for its number of live blocks
+// (0 .. MI) and the workgroup's number of live A copies, so the copy counts
+// the waits rely on stay compile-time constants.  A tile with one live block
+// costs about its weight stream (3.1 MB at d = 6144) instead of a full
+// 256-row product.
 //
 // LDS layout of a stage: rows of 64 bytes (32 bf16 of K), A rows first, then
 // 256 B rows.  The four 16-byte chunks of row r sit at slot c ^ f(r),
@@ -70,7 +81,7 @@ __device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
 // MFMA t are [spread(t), spread(t + 1)).
 template <int N, int A, int B>
 __device__ constexpr int spread(int t) {
-    return t <= A ? 0 : t >= B ? N : ((t - A) * N + (B - A) - 1) / (B - A);
+    return t <= A ? 0 : t >= B ? N : ((t - A) * N + (B - A) - 1) / (B > A ? B - A : 1);
 }
 
 // 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst
@@ -80,7 +91,9 @@ __device__ __forceinline__ void copy16(const uint8_t* src, uint8_t* dst) {
 }
 
 // Tile geometry: BM rows x 256 B rows, WV wavefronts in an MW x (WV / MW)
-// grid, each owning MI x NI blocks of 32 x 32.
+// grid, each owning MI x NI blocks of 32 x 32.  Row blocks are dealt to the
+// MW wavefront rows in turn (wavefront row mh owns blocks mh, mh + MW, ...),
+// so a tile with few rows leaves every SIMD the same share of matrix work.
 template <int BM_, int MW, int WV>
 struct Geo {
     static constexpr int BM = BM_, NW = WV / MW;
@@ -90,20 +103,28 @@ struct Geo {
     static constexpr int STAGE = ROWS * SROW;     // bytes per stage
     static constexpr int NCP = ROWS / (16 * WV);  // copies per wavefront per stage (16 rows each)
     static constexpr int NCA = BM / (16 * WV);    // ... of which A rows
-    static constexpr int NF = MI + NI;            // fragments per K16 step
-    static constexpr int NM = MI * NI;            // MFMAs per K16 step
     static_assert(MI >= 1 && NI >= 1 && NCA >= 1 && NCP * 16 * WV == ROWS && NCA * 16 * WV == BM, "geometry");
 };
 
+// First row of row block i of wavefront row mh.
+template <int MW>
+__device__ __forceinline__ int block_row(int i, int mh) { return 32 * (MW * i + mh); }
+
 // One tile's operand sources (copy lane addresses, fragment offsets) and its
-// accumulators.
-template <class GEO>
+// accumulators, for a wavefront that computes AI of its MI row blocks (the
+// blocks that hold rows of the tile; AI = 0: copies only) and issues NCAA of
+// the NCA A-row copies of a stage (those that reach rows of the tile).
+template <class GEO, int AI, int NCAA>
 struct Gemm {
-    static constexpr int MI = GEO::MI, NI = GEO::NI, NCP = GEO::NCP, NF = GEO::NF;
-    const uint8_t* src[NCP];  // per-lane source of each copy at K = 0
-    int dst[NCP];             // wave-uniform LDS byte offset of each copy in a stage
-    int fo[NF];               // per-lane LDS byte offset of each fragment (K16 step 0)
-    f32x16_t acc[MI][NI];
+    static constexpr int NI = GEO::NI, NCB = GEO::NCP - GEO::NCA;
+    static constexpr int NCPA = NCAA + NCB;           // copies issued per stage
+    static constexpr int NF = AI > 0 ? AI + NI : 0;   // fragments per K16 step
+    static constexpr int NM = AI * NI;                // MFMAs per K16 step
+    static constexpr int AIS = AI > 0 ? AI : 1, NFS = NF > 0 ? NF : 1;
+    const uint8_t* src[NCPA];  // per-lane source of each copy at K = 0
+    int dst[NCPA];             // wave-uniform LDS byte offset of each copy in a stage
+    int fo[NFS];               // per-lane LDS byte offset of each fragment (K16 step 0)
+    f32x16_t acc[AIS][NI];
 
     __device__ __forceinline__ void copy(uint8_t* S, int ci, size_t kb) const { copy16(src[ci] + kb, S + dst[ci]); }
     // step 1 reads logical chunk c + 2 of the same row: slot ^ 2
@@ -114,7 +135,7 @@ struct Gemm {
     // ordered A0, B0..B(NI-1), A1.. so that the first MFMAs wait least.
     static __device__ __forceinline__ int fa_idx(int i) { return i == 0 ? 0 : NI + i; }
     static __device__ __forceinline__ int fb_idx(int j) { return 1 + j; }
-    __device__ __forceinline__ void mfma(const bf16x8_t (&f)[NF], int t) {
+    __device__ __forceinline__ void mfma(const bf16x8_t (&f)[NFS], int t) {
         const int i = t / NI, j = t % NI;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[fa_idx(i)], f[fb_idx(j)], acc[i][j], 0, 0, 0);
     }
@@ -122,11 +143,10 @@ struct Gemm {
 
 // The K loop shared by both kernels.  nst = K / 32 stages; chunk c of the
 // operands is at byte offset c * 64 of every row.
-template <class GEO>
-__device__ __forceinline__ void k_loop(Gemm<GEO>& g, int nst, uint8_t* L0, uint8_t* L1, uint8_t* L2,
-                                       uint8_t* L3) {
-    constexpr int NCP = GEO::NCP, NF = GEO::NF, NM = GEO::NM;
-    bf16x8_t P[NF], Q[NF];
+template <class GM>
+__device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* L0, uint8_t* L1, uint8_t* L2, uint8_t* L3) {
+    constexpr int NCP = GM::NCPA, NF = GM::NF, NM = GM::NM, NFS = GM::NFS;
+    bf16x8_t P[NFS], Q[NFS];
     const int last = nst - 1;
     auto kb = [&](int c) { return (size_t)(c < last ? c : last) * SROW; };
     // Fragment reads go with the first three quarters of a step's MFMAs, so
@@ -151,6 +171,10 @@ __device__ __forceinline__ void k_loop(Gemm<GEO>& g, int nst, uint8_t* L0, uint8
         // step 1 MFMAs (Q) with the copy of chunk j + 4 into S and the first
         // fragment reads of the next stage (P)
         const size_t k4 = kb(j + 4);
+        if constexpr (NM == 0) {
+#pragma unroll
+            for (int q = 0; q < NCP; ++q) g.copy(S, q, k4);
+        }
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
             g.mfma(Q, t);
@@ -196,18 +220,48 @@ __device__ __forceinline__ void k_loop(Gemm<GEO>& g, int nst, uint8_t* L0, uint8
 __device__ __forceinline__ int copy_row(int q, int wv, int wave, int lane) { return (q * wv + wave) * 16 + (lane >> 2); }
 __device__ __forceinline__ int copy_col(int lane) { return ((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1)) * 8; }
 
+// Active copy index qa (0 .. NCPA-1) -> copy index of the full stage: the
+// first NCAA A-row copies, then every B-row copy.
+template <class GM, class GEO>
+__device__ __forceinline__ int copy_index(int qa) { return qa < GM::NCPA - GM::NCB ? qa : qa - (GM::NCPA - GM::NCB) + GEO::NCA; }
+
 // Per-lane fragment offsets: wavefront (mh, nh) reads A rows
-// mh * MI * 32 + 32 i + (lane & 31) and B rows brow[j] + (lane & 31).
-template <class GEO>
-__device__ __forceinline__ void frag_offsets(Gemm<GEO>& g, int mh, const int (&brow)[GEO::NI], int lane) {
-    using G = Gemm<GEO>;
-    const int r = lane & 31;
-    const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);  // chunk lane / 32 of row lane & 31
-    const int base = r * SROW + slot0 * 16;
+// block_row(i, mh) + (lane & 31) and B rows brow[j] + (lane & 31).
+template <class GEO, class GM, int MW>
+__device__ __forceinline__ void frag_offsets(GM& g, int mh, const int (&brow)[GEO::NI], int lane) {
+    if constexpr (GM::NF > 0) {
+        const int r = lane & 31;
+        const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);  // chunk lane / 32 of row lane & 31
+        const int base = r * SROW + slot0 * 16;
 #pragma unroll
-    for (int i = 0; i < GEO::MI; ++i) g.fo[G::fa_idx(i)] = (mh * GEO::MI * 32 + 32 * i) * SROW + base;
+        for (int i = 0; i < GM::AIS; ++i) g.fo[GM::fa_idx(i)] = block_row<MW>(i, mh) * SROW + base;
 #pragma unroll
-    for (int j = 0; j < GEO::NI; ++j) g.fo[G::fb_idx(j)] = (GEO::BM + brow[j]) * SROW + base;
+        for (int j = 0; j < GEO::NI; ++j) g.fo[GM::fb_idx(j)] = (GEO::BM + brow[j]) * SROW + base;
+    }
+}
+
+// Row blocks wavefront row mh computes for a tile of nrows rows, and A-row
+// copies a stage needs.
+template <class GEO, int MW, int WV>
+__device__ __forceinline__ int active_blocks(int nrows, int mh) {
+    const int mb = (nrows + 31) / 32;
+    return min(GEO::MI, max(0, (mb - mh + MW - 1) / MW));
+}
+template <class GEO, int WV>
+__device__ __forceinline__ int active_a_copies(int nrows) {
+    const int rows = (nrows + 31) / 32 * 32;
+    return min(GEO::NCA, max(1, (rows + 16 * WV - 1) / (16 * WV)));
+}
+
+// Calls body.template run<AI, NCAA>() for the runtime pair (ai, ncaa).
+template <class GEO, int AI, int NCAA, class B>
+__device__ __forceinline__ void dispatch(int ai, int ncaa, B& body) {
+    if (ai == AI && ncaa == NCAA) {
+        body.template run<AI, NCAA>();
+        return;
+    }
+    if constexpr (NCAA < GEO::NCA) dispatch<GEO, AI, NCAA + 1>(ai, ncaa, body);
+    else if constexpr (AI < GEO::MI) dispatch<GEO, AI + 1, 1>(ai, ncaa, body);
 }
 
 }  // namespace
@@ -216,10 +270,82 @@ __device__ __forceinline__ void frag_offsets(Gemm<GEO>& g, int mh, const int (&b
 // gate/up: BM rows x (128 gate + 128 up) columns per workgroup
 // ---------------------------------------------------------------------------
 template <int BM, int MW, int WV>
+struct GateUpTile {
+    using GEO = Geo<BM, MW, WV>;
+    const FfnArgs& a;
+    const TileRows& tr;
+    const int* src_row;
+    uint8_t *L0, *L1, *L2, *L3;
+    int F, n0, wave, lane;
+
+    template <int AI, int NCAA>
+    __device__ __forceinline__ void run() {
+        using G = Gemm<GEO, AI, NCAA>;
+        constexpr int NI = GEO::NI, NW = GEO::NW;
+        const bool shared = tr.g == a.E;
+        const int K = a.d;
+        G g;
+        const int cch = copy_col(lane);
+        const MatRef& Wg = shared ? a.s_gate : a.gate;
+        const MatRef& Wu = shared ? a.s_up : a.up;
+        const int ge = shared ? 0 : tr.g;
+        const uint16_t* gbase = static_cast<const uint16_t*>(Wg.q) + ((size_t)ge * F + n0) * K;
+        const uint16_t* ubase = static_cast<const uint16_t*>(Wu.q) + ((size_t)ge * F + n0) * K;
+        const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
+#pragma unroll
+        for (int qa = 0; qa < G::NCPA; ++qa) {
+            const int q = copy_index<G, GEO>(qa);
+            g.dst[qa] = (q * WV + wave) * 1024;
+            const int row = copy_row(q, WV, wave, lane);
+            if (q < GEO::NCA) {
+                // rows past the tile read token 0; their results are never stored
+                const int t = src_row[row];
+                g.src[qa] = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
+            } else {
+                const int br = row - BM;  // 0..255: gate rows, then up rows
+                const int n = br & 127;
+                const int rr = n0 + n < F ? n : 0;  // columns past F read row 0 and are never stored
+                const uint16_t* b = br < 128 ? gbase : ubase;
+                g.src[qa] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K + cch);
+            }
+        }
+        // wavefront (mh, nh): gate columns nh * 128/NW + 32 j' and the same up
+        // columns (blocks j < NI/2 are gate, j >= NI/2 up)
+        const int mh = wave % MW, nh = wave / MW;
+        int brow[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) brow[j] = (j < NI / 2 ? 0 : 128) + nh * (128 / NW) + 32 * (j % (NI / 2));
+        frag_offsets<GEO, G, MW>(g, mh, brow, lane);
+#pragma unroll
+        for (int i = 0; i < G::AIS; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
+
+        k_loop(g, K / SK, L0, L1, L2, L3);
+
+        // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each block
+        uint16_t* h = static_cast<uint16_t*>(a.h);
+#pragma unroll
+        for (int j = 0; j < NI / 2; ++j) {
+            const int col = n0 + brow[j] + (lane & 31);
+            if (col >= F) continue;
+#pragma unroll
+            for (int i = 0; i < AI; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = block_row<MW>(i, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    if (row < tr.nrows) {
+                        const float gv = g.acc[i][j][v], uv = g.acc[i][j + NI / 2][v];
+                        h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+                    }
+                }
+        }
+    }
+};
+
+template <int BM, int MW, int WV>
 __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     using GEO = Geo<BM, MW, WV>;
-    using G = Gemm<GEO>;
-    constexpr int MI = GEO::MI, NI = GEO::NI, NW = GEO::NW;
     __shared__ __attribute__((aligned(1024))) uint8_t L0[GEO::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t L1[GEO::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t L2[GEO::STAGE];
@@ -235,7 +361,6 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     if (n0 >= F) return;
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int K = a.d;
     for (int r = tid; r < BM; r += 64 * WV) {
         int t = -1;
         if (r < tr.nrows) {
@@ -249,72 +374,84 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
         src_row[r] = t;
     }
     __syncthreads();
-
-    G g;
-    const int cch = copy_col(lane);
-    const MatRef& Wg = shared ? a.s_gate : a.gate;
-    const MatRef& Wu = shared ? a.s_up : a.up;
-    const int ge = shared ? 0 : tr.g;
-    const uint16_t* gbase = static_cast<const uint16_t*>(Wg.q) + ((size_t)ge * F + n0) * K;
-    const uint16_t* ubase = static_cast<const uint16_t*>(Wu.q) + ((size_t)ge * F + n0) * K;
-    const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
-#pragma unroll
-    for (int q = 0; q < GEO::NCP; ++q) {
-        g.dst[q] = (q * WV + wave) * 1024;
-        const int row = copy_row(q, WV, wave, lane);
-        if (q < GEO::NCA) {
-            // rows past the tile read token 0; their results are never stored
-            const int t = src_row[row];
-            g.src[q] = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
-        } else {
-            const int br = row - BM;  // 0..255: gate rows, then up rows
-            const int n = br & 127;
-            const int rr = n0 + n < F ? n : 0;  // columns past F read row 0 and are never stored
-            const uint16_t* b = br < 128 ? gbase : ubase;
-            g.src[q] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K + cch);
-        }
-    }
-    // wavefront (mh, nh): gate columns nh * 128/NW + 32 j' and the same up
-    // columns (blocks j < NI/2 are gate, j >= NI/2 up)
-    const int mh = wave % MW, nh = wave / MW;
-    int brow[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) brow[j] = (j < NI / 2 ? 0 : 128) + nh * (128 / NW) + 32 * (j % (NI / 2));
-    frag_offsets<GEO>(g, mh, brow, lane);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
-
-    k_loop(g, K / SK, L0, L1, L2, L3);
-
-    // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each block
-    uint16_t* h = static_cast<uint16_t*>(a.h);
-#pragma unroll
-    for (int j = 0; j < NI / 2; ++j) {
-        const int col = n0 + brow[j] + (lane & 31);
-        if (col >= F) continue;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = mh * MI * 32 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < tr.nrows) {
-                    const float gv = g.acc[i][j][v], uv = g.acc[i][j + NI / 2][v];
-                    h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
-                }
-            }
-    }
+    GateUpTile<BM, MW, WV> body{a, tr, src_row, L0, L1, L2, L3, F, n0, wave, lane};
+    dispatch<GEO, 0, 1>(active_blocks<GEO, MW, WV>(tr.nrows, wave % MW), active_a_copies<GEO, WV>(tr.nrows), body);
 }
 
 // ---------------------------------------------------------------------------
 // down + weighted scatter: BM rows x 256 output columns per workgroup
 // ---------------------------------------------------------------------------
 template <int BM, int MW, int WV>
+struct DownTile {
+    using GEO = Geo<BM, MW, WV>;
+    const FfnArgs& a;
+    const TileRows& tr;
+    const int* dst_row;
+    const float* wrow;
+    uint8_t *L0, *L1, *L2, *L3;
+    int n0, wave, lane;
+
+    template <int AI, int NCAA>
+    __device__ __forceinline__ void run() {
+        using G = Gemm<GEO, AI, NCAA>;
+        constexpr int NI = GEO::NI, NW = GEO::NW;
+        const bool shared = tr.g == a.E;
+        const int K = shared ? a.Fs : a.F;
+        const int N = a.d;
+        G g;
+        const int cch = copy_col(lane);
+        const MatRef& D = shared ? a.s_down : a.down;
+        const int ge = shared ? 0 : tr.g;
+        const uint16_t* dbase = static_cast<const uint16_t*>(D.q) + ((size_t)ge * N + n0) * K;
+        const uint16_t* hbase = static_cast<const uint16_t*>(a.h) + (size_t)tr.rbeg * a.ldh;
+#pragma unroll
+        for (int qa = 0; qa < G::NCPA; ++qa) {
+            const int q = copy_index<G, GEO>(qa);
+            g.dst[qa] = (q * WV + wave) * 1024;
+            const int row = copy_row(q, WV, wave, lane);
+            if (q < GEO::NCA) {
+                const int rr = row < tr.nrows ? row : 0;  // rows past the tile: never stored
+                g.src[qa] = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
+            } else {
+                const int br = row - BM;
+                const int rr = n0 + br < N ? br : 0;
+                g.src[qa] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K + cch);
+            }
+        }
+        const int mh = wave % MW, nh = wave / MW;
+        int brow[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) brow[j] = nh * (SBN / NW) + 32 * j;
+        frag_offsets<GEO, G, MW>(g, mh, brow, lane);
+#pragma unroll
+        for (int i = 0; i < G::AIS; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
+
+        k_loop(g, K / SK, L0, L1, L2, L3);
+
+        float* out = shared ? a.shared_out : a.slot_out;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = block_row<MW>(i, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < tr.nrows && dst_row[row] >= 0) {
+                    const size_t base = (size_t)dst_row[row] * N;
+                    const float w = wrow[row];
+#pragma unroll
+                    for (int j = 0; j < NI; ++j) {
+                        const int col = n0 + brow[j] + (lane & 31);
+                        if (col < N) out[base + col] = w * g.acc[i][j][v];
+                    }
+                }
+            }
+    }
+};
+
+template <int BM, int MW, int WV>
 __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     using GEO = Geo<BM, MW, WV>;
-    using G = Gemm<GEO>;
-    constexpr int MI = GEO::MI, NI = GEO::NI, NW = GEO::NW;
     __shared__ __attribute__((aligned(1024))) uint8_t L0[GEO::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t L1[GEO::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t L2[GEO::STAGE];
@@ -326,8 +463,6 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     TileRows tr;
     if (!tile_rows<BM>(a, tile, tr)) return;
     const bool shared = tr.g == a.E;
-    const int K = shared ? a.Fs : a.F;
-    const int N = a.d;
     const int n0 = ntile * SBN;
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -350,54 +485,8 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
         wrow[r] = w;
     }
     __syncthreads();
-
-    G g;
-    const int cch = copy_col(lane);
-    const MatRef& D = shared ? a.s_down : a.down;
-    const int ge = shared ? 0 : tr.g;
-    const uint16_t* dbase = static_cast<const uint16_t*>(D.q) + ((size_t)ge * N + n0) * K;
-    const uint16_t* hbase = static_cast<const uint16_t*>(a.h) + (size_t)tr.rbeg * a.ldh;
-#pragma unroll
-    for (int q = 0; q < GEO::NCP; ++q) {
-        g.dst[q] = (q * WV + wave) * 1024;
-        const int row = copy_row(q, WV, wave, lane);
-        if (q < GEO::NCA) {
-            const int rr = row < tr.nrows ? row : 0;  // rows past the tile: never stored
-            g.src[q] = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
-        } else {
-            const int br = row - BM;
-            const int rr = n0 + br < N ? br : 0;
-            g.src[q] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K + cch);
-        }
-    }
-    const int mh = wave % MW, nh = wave / MW;
-    int brow[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) brow[j] = nh * (SBN / NW) + 32 * j;
-    frag_offsets<GEO>(g, mh, brow, lane);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
-
-    k_loop(g, K / SK, L0, L1, L2, L3);
-
-    float* out = shared ? a.shared_out : a.slot_out;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = mh * MI * 32 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (row < tr.nrows && dst_row[row] >= 0) {
-                const size_t base = (size_t)dst_row[row] * N;
-                const float w = wrow[row];
-#pragma unroll
-                for (int j = 0; j < NI; ++j) {
-                    const int col = n0 + brow[j] + (lane & 31);
-                    if (col < N) out[base + col] = w * g.acc[i][j][v];
-                }
-            }
-        }
+    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, L0, L1, L2, L3, n0, wave, lane};
+    dispatch<GEO, 0, 1>(active_blocks<GEO, MW, WV>(tr.nrows, wave % MW), active_a_copies<GEO, WV>(tr.nrows), body);
 }
 
 // wavefront grid of the kernels launched: DMA_MW x (DMA_WV / DMA_MW)
@@ -406,15 +495,15 @@ constexpr int DMA_MW = 2, DMA_WV = 8;
 hipError_t launch_gateup_dma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
     dim3 grid(a.max_tiles, (fmax + SBN / 2 - 1) / (SBN / 2));
-    if (a.bm == 256) launch_kernel(gateup_dma_kernel<256, DMA_MW, DMA_WV>, grid, 64 * DMA_WV, st, kt, a);
-    else launch_kernel(gateup_dma_kernel<128, DMA_MW, DMA_WV>, grid, 64 * DMA_WV, st, kt, a);
+    if (a.bm != 256) return hipErrorInvalidValue;
+    launch_kernel(gateup_dma_kernel<256, DMA_MW, DMA_WV>, grid, 64 * DMA_WV, st, kt, a);
     return hipGetLastError();
 }
 
 hipError_t launch_down_dma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     dim3 grid(a.max_tiles, (a.d + SBN - 1) / SBN);
-    if (a.bm == 256) launch_kernel(down_dma_kernel<256, DMA_MW, DMA_WV>, grid, 64 * DMA_WV, st, kt, a);
-    else launch_kernel(down_dma_kernel<128, DMA_MW, DMA_WV>, grid, 64 * DMA_WV, st, kt, a);
+    if (a.bm != 256) return hipErrorInvalidValue;
+    launch_kernel(down_dma_kernel<256, DMA_MW, DMA_WV>, grid, 64 * DMA_WV, st, kt, a);
     return hipGetLastError();
 }
 

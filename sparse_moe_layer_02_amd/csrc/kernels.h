@@ -60,9 +60,7 @@ struct PermArgs {
     int32_t* active;     // [E] experts with rows, ascending
     int2* tiles;         // [max_tiles] (group, first row) for the grouped GEMM
     int n_blk;
-    int bm;              // tile rows of the (small-tile) list
-    int bm_big;          // tile rows of the big-tile list (0: no big list)
-    int big_min;         // groups with at least this many rows go to the big list
+    int bm;              // tile rows for the tile list
 };
 hipError_t launch_permute(const PermArgs& a, hipStream_t st, const KTime& kt = KTime());
 // active / tile lists from existing offsets (offsets and perm_rows untouched)
@@ -106,9 +104,6 @@ struct FfnArgs {
     float* y;               // [T, d] (fused combine)
     int max_tiles;          // grid bound of the grouped GEMMs (tiles of bm rows)
     int bm;                 // rows per grouped-GEMM tile: 64, 128 or 256
-    int list;               // tile list a grouped-GEMM launch walks: 0 small tiles, 1 big tiles
-    int bm_big;             // rows per big tile (0: no big list)
-    int max_big_tiles;      // grid bound of the big-tile launches
     int shared_done;        // the shared expert's h rows were already produced (decode route kernel)
     DecodeSlot* dslots;     // decode slot table (decode path only)
     int n_dslots;           // its capacity: n_shared + min(E, T*k)

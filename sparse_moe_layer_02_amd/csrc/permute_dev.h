@@ -64,43 +64,26 @@ __device__ __forceinline__ void multisplit_rank(int e, bool valid, int nbits, in
 // Called by all 1024 threads; thread e < E holds count c.  `own` = this call
 // produced the permutation (write offsets and the perm_rows tail), as opposed
 // to deriving the lists from a caller's offsets.
-//
-// Tiles come in two lists.  A group (expert, or the shared expert over all T
-// tokens) with at least big_min rows is cut into tiles of bm_big rows (the
-// big-tile list, when bm_big > 0), every other group into tiles of bm rows
-// (the small-tile list).  tiles[] holds the small list from index 0 (routed
-// groups ascending, then the shared expert), then the big list in the same
-// order; meta[1] / meta[3] count them and meta[4] is the big list's start.
 __device__ void emit_lists(const PermArgs& a, int c, int* smem, int* off_out, bool own = true) {
     const int e = threadIdx.x, E = a.E;
-    int total, n_active, n_rtiles, n_rbig;
+    int total, n_active, n_rtiles;
     const int off = block_excl_scan_1024(e < E ? c : 0, smem, &total);
     const int act = (e < E && c > 0) ? 1 : 0;
     const int apos = block_excl_scan_1024(act, smem, &n_active);
-    const bool big = e < E && a.bm_big > 0 && c >= a.big_min;
-    const int nt = (e < E && a.bm > 0 && !big) ? (c + a.bm - 1) / a.bm : 0;  // bm == 0: no tile list
-    const int nb = big ? (c + a.bm_big - 1) / a.bm_big : 0;
+    const int nt = (e < E && a.bm > 0) ? (c + a.bm - 1) / a.bm : 0;  // bm == 0: no tile list
     const int tbase = block_excl_scan_1024(nt, smem, &n_rtiles);
-    const int bbase = block_excl_scan_1024(nb, smem, &n_rbig);
-    const bool s_big = a.n_shared && a.bm_big > 0 && a.T >= a.big_min;
-    const int s_tiles = (a.n_shared && a.bm > 0 && !s_big) ? (a.T + a.bm - 1) / a.bm : 0;
-    const int s_btiles = s_big ? (a.T + a.bm_big - 1) / a.bm_big : 0;
-    const int big0 = n_rtiles + s_tiles;  // first index of the big list
     if (e < E) {
         if (own) a.offsets[e] = off;
         if (act) a.active[apos] = e;
         for (int i = 0; i < nt; ++i) a.tiles[tbase + i] = make_int2(e, i * a.bm);
-        for (int i = 0; i < nb; ++i) a.tiles[big0 + bbase + i] = make_int2(e, i * a.bm_big);
     }
+    const int s_tiles = (a.n_shared && a.bm > 0) ? (a.T + a.bm - 1) / a.bm : 0;
     for (int i = e; i < s_tiles; i += blockDim.x) a.tiles[n_rtiles + i] = make_int2(E, i * a.bm);
-    for (int i = e; i < s_btiles; i += blockDim.x) a.tiles[big0 + n_rbig + i] = make_int2(E, i * a.bm_big);
     if (e == 0) {
         if (own) a.offsets[E] = total;
         a.meta[0] = n_active;
         a.meta[1] = n_rtiles + s_tiles;
         a.meta[2] = total;
-        a.meta[3] = n_rbig + s_btiles;
-        a.meta[4] = big0;
     }
     if (own) {
         const int n = a.T * a.k;

@@ -9,9 +9,9 @@ The gate pre-activations g are integers in [20, 44], where silu(g) rounds to g
 in fp32, so h = g * u is an exact integer: a wrong gate or up sum (a K chunk
 dropped, repeated or taken from the wrong rows) changes h, and with it y, by
 a whole number.  Every expert kernel family is reached: the decode GEMVs
-(bf16, int8, fp32), the grouped MFMA GEMMs with 64-, 128- and 256-row tiles
-(the last through LDS copies, also at d = 6144), the int8 grouped GEMMs, and
-the prefill GEMVs (int8 with few rows per expert, fp32).
+(bf16, int8, fp32), the grouped MFMA GEMMs with 64- and 256-row tiles (the
+latter through LDS copies, with short tiles, also at d = 6144), the int8
+grouped GEMMs, and the prefill GEMVs (int8 with few rows per expert, fp32).
 """
 import sys
 
@@ -40,14 +40,13 @@ CASES = {
     # prefill: 64-row tiles (fewer than 96 rows per expert)
     "prefill_bm64": dict(T=40, d=256, E=16, k=4, F=128),
     "prefill_bm64_no_shared": dict(T=70, d=192, E=8, k=2, F=64, n_shared=0),
-    # 128-row tiles (96 to 255 rows per expert), odd 64-wide K chunks
-    "prefill_bm128": dict(T=300, d=192, E=4, k=2, F=320, Fs=448),
-    # 96 to 255 rows per expert on average with skewed loads: experts with 256
-    # rows or more (and the shared expert) on the big-tile list, the rest on
-    # 128-row tiles
-    "prefill_split_skewed": dict(T=800, d=256, E=16, k=2, F=192, skew=1.2),
-    "prefill_split_no_shared": dict(T=700, d=192, E=12, k=2, F=128, n_shared=0, skew=1.0),
-    # 256-row tiles through LDS copies (256 rows per expert or more)
+    # 256-row tiles through LDS copies (96 rows per expert or more on
+    # average): odd 32-wide K stages, experts of 140-160 rows (one full and
+    # one short tile each), skewed loads from 17 to 506 rows (tiles with 1 to
+    # 8 live 32-row blocks, one or two live A-row copies)
+    "prefill_bm256_short_tiles": dict(T=300, d=192, E=4, k=2, F=320, Fs=448),
+    "prefill_bm256_skewed": dict(T=800, d=256, E=16, k=2, F=192, skew=1.2),
+    "prefill_bm256_skewed_no_shared": dict(T=700, d=192, E=12, k=2, F=128, n_shared=0, skew=1.0),
     "prefill_bm256": dict(T=700, d=320, E=2, k=2, F=320, Fs=448),
     "prefill_bm256_d6144": dict(T=600, d=6144, E=2, k=1, F=2048),
     # int8 grouped GEMMs (2 rows per expert or more) and int8 GEMVs (fewer)
@@ -86,7 +85,7 @@ def test_exact_layer_bitwise(orc, case):
             assert _bits_equal(got_p[key], ref[key]), (case, "prefill", key)
 
 
-@pytest.mark.parametrize("case", ["prefill_bm64", "prefill_split_skewed", "prefill_bm256", "prefill_q8_mfma",
+@pytest.mark.parametrize("case", ["prefill_bm64", "prefill_bm256_skewed", "prefill_bm256", "prefill_q8_mfma",
                                   "decode_q8_T5"])
 def test_exact_split_entry_points(orc, case):
     """moe_expert_ffn and moe_combine alone, with caller routing weights that

@@ -223,12 +223,13 @@ EDGE = {
     "f32_decode_T3": dict(T=3, d=512, E=32, k=4, F=256, act="f32", w="f32", x_sigma=0.5, w_sigma=0.1),
     "no_shared_prefill": dict(T=33, d=128, E=8, k=3, F=64, n_shared=0),
     "shared_wider_than_routed": dict(T=12, d=128, E=8, k=2, F=64, Fs=192),
-    # 128-row GEMM tiles (experts average >= 96 rows): odd numbers of 64-wide
-    # K chunks (d = 192, F = 320), ragged last tiles, shared expert wider
-    # than the routed ones, a tile list longer than one tile per expert
-    "bm128_odd_chunks": dict(T=300, d=192, E=4, k=2, F=320, Fs=448),
-    "bm128_single_chunk": dict(T=200, d=64, E=2, k=1, F=64, Fs=64),
-    "bm128_many_tiles": dict(T=700, d=256, E=6, k=3, F=128, Fs=128),
+    # 256-row LDS-copy tiles whose last tile is short (experts average
+    # 96-255 rows): odd numbers of 32-wide K stages (d = 192, F = 320), short
+    # tiles with 1 to 7 live 32-row blocks, shared expert wider than the
+    # routed ones, experts of one full and one short tile
+    "bm256_short_odd_stages": dict(T=300, d=192, E=4, k=2, F=320, Fs=448),
+    "bm256_short_single_stage_pair": dict(T=200, d=64, E=2, k=1, F=64, Fs=64),
+    "bm256_short_many_tiles": dict(T=700, d=256, E=6, k=3, F=128, Fs=128),
     # 256-row tiles fed through LDS copies (experts average >= 256 rows):
     # 32-wide K stages in groups of four with a tail (d = 320 -> 10 stages,
     # Fs = 448 -> 14), a partial last N tile of gate/up (F = 320) and of down
