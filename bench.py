@@ -128,6 +128,14 @@ class Hip:
         assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
         return out.value
 
+    def ms_or_none(self, a, b):
+        """Elapsed time between two events, or None if either was never recorded."""
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0:
+            return out.value
+        self.lib.hipGetLastError()  # clear it, so the library's next launch check does not see it
+        return None
+
     def wait(self, stream, e):
         assert self.lib.hipStreamWaitEvent(ctypes.c_void_p(stream), e, 0) == 0
 
@@ -713,14 +721,18 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
         for i in range(steps):
             step(warmup + i, events=ev_arr[i], dbg={"topk_idx": idx_log[i]})
         torch.cuda.synchronize()
-    stage_ms = np.zeros((steps, len(stage_names)))
+    # a stage whose kernels the path does not launch has unrecorded events
+    # and is left out
+    stage_ms = np.full((steps, len(stage_names)), np.nan)
     for i in range(steps):
         for col, sid in enumerate(stage_ids):
-            stage_ms[i, col] = hip.ms(ev[i][2 * sid], ev[i][2 * sid + 1])
+            v = hip.ms_or_none(ev[i][2 * sid], ev[i][2 * sid + 1])
+            stage_ms[i, col] = np.nan if v is None else v
     for row in ev:
         for e in row:
             hip.destroy(e)
-    stages_us = {name: round(float(stage_ms[:, col].mean()) * 1e3, 2) for col, name in enumerate(stage_names)}
+    stages_us = {name: round(float(stage_ms[:, col].mean()) * 1e3, 2) for col, name in enumerate(stage_names)
+                 if not np.isnan(stage_ms[:, col]).any()}
 
     # ---- per-step distribution: the same steps with an event between steps --
     sev = [hip.event() for _ in range(steps + 1)]
@@ -742,7 +754,7 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
     router_bytes = cfg["E"] * cfg["d"] * 4
     act_bytes = 2 if cfg["act"] == "bf16" else 4
     layer_bytes = n_exp * expert_bytes(cfg) + router_bytes + T * cfg["d"] * (act_bytes + 4)
-    if decode:  # the routed gate/up launch; the shared expert's gate/up runs beside the selection
+    if decode:  # the routed gate/up launch; the shared expert's gate/up runs beside the router
         gu_bytes = unions.astype(np.float64) * expert_bytes(cfg, 2)
         flops_gu = 2.0 * T * cfg["k"] * cfg["d"] * 2 * cfg["F"]
     else:  # routed + shared gate/up; the GEMM also reads the gathered rows of x and writes h
