@@ -59,19 +59,51 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(PermArgs a) {
     for (int e = tid; e < E; e += blockDim.x) a.blk_hist[(size_t)b * E + e] = cnt[e];
 }
 
+// Column sums and column prefix sums of the [n_blk, E] block histogram.  The
+// 1024 threads split into SCAN_PARTS groups of 1024 / SCAN_PARTS lanes; lane e
+// of group p owns expert columns e, e + 1024 / SCAN_PARTS, ... and adds the
+// blocks p, p + SCAN_PARTS, ... (independent loads, many in flight), so the
+// per-expert totals come from SCAN_PARTS partial sums in LDS instead of one
+// serial walk over the blocks.  The bases then walk the blocks again, each
+// group over its own contiguous range of blocks, starting from the totals of
+// the ranges before it.
+constexpr int SCAN_PARTS = 4;
+
 __global__ __launch_bounds__(1024) void perm_scan_kernel(PermArgs a) {
     __shared__ int smem[17];
-    const int e = threadIdx.x, E = a.E;
+    __shared__ int part[SCAN_PARTS][1024];  // partial column sums per block range
+    const int tid = threadIdx.x, E = a.E, nb = a.n_blk;
+    constexpr int LANES = 1024 / SCAN_PARTS;
+    const int g = tid / LANES, l = tid % LANES;
+    const int bper = (nb + SCAN_PARTS - 1) / SCAN_PARTS;  // blocks of group g: [g*bper, min(nb, (g+1)*bper))
+    const int b0 = g * bper, b1 = min(nb, b0 + bper);
+    for (int e = l; e < E; e += LANES) {
+        int c = 0;
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b) c += a.blk_hist[(size_t)b * E + e];
+        part[g][e] = c;
+    }
+    __syncthreads();
     int c = 0;
-    if (e < E)
-        for (int b = 0; b < a.n_blk; ++b) c += a.blk_hist[(size_t)b * E + e];
+    if (tid < E)
+        for (int q = 0; q < SCAN_PARTS; ++q) c += part[q][tid];
     int off;
-    emit_lists(a, c, smem, &off);
-    if (e < E) {
+    emit_lists(a, c, smem, &off);  // (its block scans synchronise the workgroup)
+    if (tid < E) {  // offset of expert tid, then the group prefixes: part[q] becomes the start of range q
         int run = off;
-        for (int b = 0; b < a.n_blk; ++b) {
+        for (int q = 0; q < SCAN_PARTS; ++q) {
+            const int v = part[q][tid];
+            part[q][tid] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+    for (int e = l; e < E; e += LANES) {
+        int run = part[g][e];
+        for (int b = b0; b < b1; ++b) {
+            const int h = a.blk_hist[(size_t)b * E + e];
             a.blk_base[(size_t)b * E + e] = run;
-            run += a.blk_hist[(size_t)b * E + e];
+            run += h;
         }
     }
 }
