@@ -44,6 +44,8 @@
 // f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1): the sixteen lanes that a 128-bit LDS
 // read serves per cycle (sixteen consecutive rows, one chunk) hit sixteen
 // different 16-byte bank groups (measured: no bank-conflict cycles).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "gemm_dev.h"
@@ -54,6 +56,7 @@ namespace {
 constexpr int SK = 32;        // K per stage
 constexpr int SROW = SK * 2;  // LDS bytes per row of a stage
 constexpr int SBN = 256;      // B rows per tile
+constexpr int XS = SBN * SROW;  // bytes of one LDS array: one stage's A rows or its B rows (16 KB)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -126,9 +129,15 @@ struct Gemm {
     int fo[NFS];               // per-lane LDS byte offset of each fragment (K16 step 0)
     f32x16_t acc[AIS][NI];
 
-    __device__ __forceinline__ void copy(uint8_t* S, int ci, size_t kb) const { copy16(src[ci] + kb, S + dst[ci]); }
+    // A rows of a stage live in one LDS array, its B rows in another: the
+    // first NCAA copies and the A fragments go to SA, the rest to SB (dst and
+    // fo are offsets inside their own array)
+    __device__ __forceinline__ void copy(uint8_t* SA, uint8_t* SB, int ci, size_t kb) const {
+        copy16(src[ci] + kb, (ci < NCAA ? SA : SB) + dst[ci]);
+    }
     // step 1 reads logical chunk c + 2 of the same row: slot ^ 2
-    __device__ __forceinline__ bf16x8_t frag(const uint8_t* S, int fi, int ks) const {
+    __device__ __forceinline__ bf16x8_t frag(const uint8_t* SA, const uint8_t* SB, int fi, int ks) const {
+        const uint8_t* S = (fi == 0 || fi > NI) ? SA : SB;
         return *reinterpret_cast<const bf16x8_t*>(S + (ks ? (fo[fi] ^ 32) : fo[fi]));
     }
     // MFMA t of a K16 step: block (i, j) = (t / NI, t % NI); fragments are
@@ -144,7 +153,8 @@ struct Gemm {
 // The K loop shared by both kernels.  nst = K / 32 stages; chunk c of the
 // operands is at byte offset c * 64 of every row.
 template <class GM>
-__device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* L0, uint8_t* L1, uint8_t* L2, uint8_t* L3) {
+__device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* A0, uint8_t* B0, uint8_t* A1, uint8_t* B1,
+                                       uint8_t* A2, uint8_t* B2, uint8_t* A3, uint8_t* B3) {
     constexpr int NCP = GM::NCPA, NF = GM::NF, NM = GM::NM, NFS = GM::NFS;
     bf16x8_t P[NFS], Q[NFS];
     const int last = nst - 1;
@@ -154,14 +164,14 @@ __device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* L0, uint8_t* L1,
     // quarters.
     constexpr int RD = (NM * 3 + 3) / 4, CP = NM / 4;
 
-    // one stage: S holds chunk j, N is the stage of chunk j + 1
-    auto stage = [&](uint8_t* S, uint8_t* N, int j) {
+    // one stage: (SA, SB) holds chunk j, (NA, NB) is the stage of chunk j + 1
+    auto stage = [&](uint8_t* SA, uint8_t* SB, uint8_t* NA, uint8_t* NB, int j) {
         // step 0 MFMAs (fragments P) with step 1's fragment reads (Q)
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
             g.mfma(P, t);
 #pragma unroll
-            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q) Q[q] = g.frag(S, q, 1);
+            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q) Q[q] = g.frag(SA, SB, q, 1);
             pin();
         }
         // every read of S done, chunk j + 1 landed (two later chunks may be in flight)
@@ -173,43 +183,43 @@ __device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* L0, uint8_t* L1,
         const size_t k4 = kb(j + 4);
         if constexpr (NM == 0) {
 #pragma unroll
-            for (int q = 0; q < NCP; ++q) g.copy(S, q, k4);
+            for (int q = 0; q < NCP; ++q) g.copy(SA, SB, q, k4);
         }
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
             g.mfma(Q, t);
 #pragma unroll
-            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q) P[q] = g.frag(N, q, 0);
+            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q) P[q] = g.frag(NA, NB, q, 0);
 #pragma unroll
-            for (int q = spread<NCP, CP, NM>(t); q < spread<NCP, CP, NM>(t + 1); ++q) g.copy(S, q, k4);
+            for (int q = spread<NCP, CP, NM>(t); q < spread<NCP, CP, NM>(t + 1); ++q) g.copy(SA, SB, q, k4);
             pin();
         }
     };
 
     // prologue: chunks 0..3 into stages 0..3, wait for chunk 0
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(L0, q, kb(0));
+    for (int q = 0; q < NCP; ++q) g.copy(A0, B0, q, kb(0));
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(L1, q, kb(1));
+    for (int q = 0; q < NCP; ++q) g.copy(A1, B1, q, kb(1));
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(L2, q, kb(2));
+    for (int q = 0; q < NCP; ++q) g.copy(A2, B2, q, kb(2));
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(L3, q, kb(3));
+    for (int q = 0; q < NCP; ++q) g.copy(A3, B3, q, kb(3));
     wait_vm<3 * NCP>();
     barrier_nofence();
 #pragma unroll
-    for (int q = 0; q < NF; ++q) P[q] = g.frag(L0, q, 0);
+    for (int q = 0; q < NF; ++q) P[q] = g.frag(A0, B0, q, 0);
 
     int j = 0;
     for (; j + 4 <= nst; j += 4) {
-        stage(L0, L1, j);
-        stage(L1, L2, j + 1);
-        stage(L2, L3, j + 2);
-        stage(L3, L0, j + 3);
+        stage(A0, B0, A1, B1, j);
+        stage(A1, B1, A2, B2, j + 1);
+        stage(A2, B2, A3, B3, j + 2);
+        stage(A3, B3, A0, B0, j + 3);
     }
-    if (j < nst) stage(L0, L1, j);
-    if (j + 1 < nst) stage(L1, L2, j + 1);
-    if (j + 2 < nst) stage(L2, L3, j + 2);
+    if (j < nst) stage(A0, B0, A1, B1, j);
+    if (j + 1 < nst) stage(A1, B1, A2, B2, j + 1);
+    if (j + 2 < nst) stage(A2, B2, A3, B3, j + 2);
     // no copy may still be writing LDS when the workgroup ends
     wait_vm<0>();
 }
@@ -236,7 +246,7 @@ __device__ __forceinline__ void frag_offsets(GM& g, int mh, const int (&brow)[GE
 #pragma unroll
         for (int i = 0; i < GM::AIS; ++i) g.fo[GM::fa_idx(i)] = block_row<MW>(i, mh) * SROW + base;
 #pragma unroll
-        for (int j = 0; j < GEO::NI; ++j) g.fo[GM::fb_idx(j)] = (GEO::BM + brow[j]) * SROW + base;
+        for (int j = 0; j < GEO::NI; ++j) g.fo[GM::fb_idx(j)] = brow[j] * SROW + base;
     }
 }
 
@@ -264,6 +274,130 @@ __device__ __forceinline__ void dispatch(int ai, int ncaa, B& body) {
     else if constexpr (AI < GEO::MI) dispatch<GEO, AI + 1, 1>(ai, ncaa, body);
 }
 
+// ---------------------------------------------------------------------------
+// Cold tiles: tiles of at most COLD_ROWS rows (an expert with few rows, or
+// the short tail of a hot one).  Their matrix work is a sliver of their weight
+// stream, so what bounds them is how many weight bytes a CU keeps in flight:
+// with the hot tiles' four K32 stages (A and B rows in each) three stages are
+// in flight, about 22 GB/s per CU.  A cold tile uses the same eight LDS arrays
+// as eight B-only K32 stages, seven of them in flight, and takes its A
+// fragments (one 32-row block per wavefront at most) straight from memory into
+// a ring of registers, loaded together with the B rows of the same chunk so
+// one vector-memory count covers both.
+// ---------------------------------------------------------------------------
+#ifndef COLD_ROWS_MAX
+#define COLD_ROWS_MAX 32
+#endif
+constexpr int COLD_ROWS = COLD_ROWS_MAX;
+
+template <class GEO, int AI>
+struct GemmCold {
+    static_assert(AI == 0 || AI == 1, "a cold tile gives a wavefront at most one row block");
+    static constexpr int NI = GEO::NI, NCB = GEO::NCP - GEO::NCA;  // B-row copies per wavefront per stage
+    static constexpr int NCP = 2 * AI + NCB;                       // vector-memory operations per stage
+    const uint8_t* asrc;   // this lane's A fragment source at K = 0 (row lane & 31 of its block, K half lane / 32)
+    const uint8_t* src[NCB];
+    int dst[NCB];          // offsets in a B array
+    int fo[NI];            // B fragment offsets (K16 step 0)
+    f32x16_t acc[NI];
+};
+
+template <int K>
+using ic = std::integral_constant<int, K>;
+
+// The K loop of a cold tile: nst = K / 32 stages in eight slots; slot s holds
+// the B rows of chunk c = s mod 8, ring[s] that chunk's two A fragments.
+// Chunks are fetched in pairs (2m, 2m + 1): the two 64-byte halves of every
+// 128-byte line of a row go out back to back, so the memory sees whole lines
+// rather than halves a stage apart.  At an even stage j: the pair (j, j + 1)
+// has landed (the pairs of chunks j + 2 .. j + 5 may still be in flight) and
+// every wavefront has finished reading slots j - 2 and j - 1, which then
+// receive the pair (j + 6, j + 7); odd stages only compute.
+template <class GC>
+__device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t* X1, uint8_t* X2, uint8_t* X3,
+                                            uint8_t* X4, uint8_t* X5, uint8_t* X6, uint8_t* X7) {
+    constexpr int NCP = GC::NCP, NI = GC::NI, NCB = GC::NCB;
+    constexpr bool HAS_A = GC::NCP > GC::NCB;
+    bf16x8_t ring[8][2];
+    const int last = nst - 1;
+    auto kb = [&](int c) { return (size_t)(c < last ? c : last) * SROW; };
+    auto slot = [&](auto kc) -> uint8_t* {
+        constexpr int K = decltype(kc)::value;
+        if constexpr (K == 0) return X0;
+        else if constexpr (K == 1) return X1;
+        else if constexpr (K == 2) return X2;
+        else if constexpr (K == 3) return X3;
+        else if constexpr (K == 4) return X4;
+        else if constexpr (K == 5) return X5;
+        else if constexpr (K == 6) return X6;
+        else return X7;
+    };
+    // chunks c, c + 1 into slots K, K + 1 (K even): A fragments, then the B
+    // rows, each row's two halves back to back
+    auto issue_pair = [&](auto kc, int c) {
+        constexpr int K = decltype(kc)::value;
+        static_assert(K % 2 == 0, "pairs start at even slots");
+        const size_t o0 = kb(c), o1 = kb(c + 1);
+        if constexpr (HAS_A) {
+            ring[K][0] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o0);
+            ring[K][1] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o0 + 32);
+            ring[K + 1][0] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o1);
+            ring[K + 1][1] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o1 + 32);
+        }
+#pragma unroll
+        for (int q = 0; q < NCB; ++q) {
+            copy16(g.src[q] + o0, slot(kc) + g.dst[q]);
+            copy16(g.src[q] + o1, slot(ic<K + 1>()) + g.dst[q]);
+        }
+    };
+    auto stage = [&](auto kc, int j) {
+        constexpr int K = decltype(kc)::value;
+        if constexpr (K % 2 == 0) {
+            wait_lgkm0();
+            wait_vm<4 * NCP>();
+            barrier_nofence();
+            issue_pair(ic<(K + 6) % 8>(), j + 6);
+        }
+        if constexpr (HAS_A) {
+            const uint8_t* S = slot(kc);
+            bf16x8_t b[2][NI];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int jj = 0; jj < NI; ++jj)
+                    b[s][jj] = *reinterpret_cast<const bf16x8_t*>(S + (s ? (g.fo[jj] ^ 32) : g.fo[jj]));
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int jj = 0; jj < NI; ++jj)
+                    g.acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[K][s], b[s][jj], g.acc[jj], 0, 0, 0);
+        }
+    };
+    issue_pair(ic<0>(), 0);
+    issue_pair(ic<2>(), 2);
+    issue_pair(ic<4>(), 4);
+    int j = 0;
+    for (; j + 8 <= nst; j += 8) {
+        stage(ic<0>(), j);
+        stage(ic<1>(), j + 1);
+        stage(ic<2>(), j + 2);
+        stage(ic<3>(), j + 3);
+        stage(ic<4>(), j + 4);
+        stage(ic<5>(), j + 5);
+        stage(ic<6>(), j + 6);
+        stage(ic<7>(), j + 7);
+    }
+    if (j < nst) stage(ic<0>(), j);
+    if (j + 1 < nst) stage(ic<1>(), j + 1);
+    if (j + 2 < nst) stage(ic<2>(), j + 2);
+    if (j + 3 < nst) stage(ic<3>(), j + 3);
+    if (j + 4 < nst) stage(ic<4>(), j + 4);
+    if (j + 5 < nst) stage(ic<5>(), j + 5);
+    if (j + 6 < nst) stage(ic<6>(), j + 6);
+    // no copy may still be writing LDS when the workgroup ends
+    wait_vm<0>();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -275,7 +409,7 @@ struct GateUpTile {
     const FfnArgs& a;
     const TileRows& tr;
     const int* src_row;
-    uint8_t *L0, *L1, *L2, *L3;
+    uint8_t *X0, *X1, *X2, *X3, *X4, *X5, *X6, *X7;
     int F, n0, wave, lane;
 
     template <int AI, int NCAA>
@@ -295,7 +429,7 @@ struct GateUpTile {
 #pragma unroll
         for (int qa = 0; qa < G::NCPA; ++qa) {
             const int q = copy_index<G, GEO>(qa);
-            g.dst[qa] = (q * WV + wave) * 1024;
+            g.dst[qa] = (q * WV + wave) * 1024 - (q < GEO::NCA ? 0 : BM * SROW);
             const int row = copy_row(q, WV, wave, lane);
             if (q < GEO::NCA) {
                 // rows past the tile read token 0; their results are never stored
@@ -321,7 +455,7 @@ struct GateUpTile {
 #pragma unroll
             for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
 
-        k_loop(g, K / SK, L0, L1, L2, L3);
+        k_loop(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
 
         // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each block
         uint16_t* h = static_cast<uint16_t*>(a.h);
@@ -341,15 +475,84 @@ struct GateUpTile {
                 }
         }
     }
+
+    // a tile of at most COLD_ROWS rows (see k_loop_cold)
+    template <int AI>
+    __device__ __forceinline__ void run_cold() {
+        using G = GemmCold<GEO, AI>;
+        constexpr int NI = GEO::NI, NW = GEO::NW;
+        const bool shared = tr.g == a.E;
+        const int K = a.d;
+        G g;
+        const int cch = copy_col(lane);
+        const MatRef& Wg = shared ? a.s_gate : a.gate;
+        const MatRef& Wu = shared ? a.s_up : a.up;
+        const int ge = shared ? 0 : tr.g;
+        const uint16_t* gbase = static_cast<const uint16_t*>(Wg.q) + ((size_t)ge * F + n0) * K;
+        const uint16_t* ubase = static_cast<const uint16_t*>(Wu.q) + ((size_t)ge * F + n0) * K;
+        const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
+#pragma unroll
+        for (int qb = 0; qb < G::NCB; ++qb) {
+            const int q = GEO::NCA + qb;
+            g.dst[qb] = (q * WV + wave) * 1024 - BM * SROW;
+            const int br = copy_row(q, WV, wave, lane) - BM;  // 0..255: gate rows, then up rows
+            const int n = br & 127;
+            const int rr = n0 + n < F ? n : 0;  // columns past F read row 0 and are never stored
+            const uint16_t* b = br < 128 ? gbase : ubase;
+            g.src[qb] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K + cch);
+        }
+        const int mh = wave % MW, nh = wave / MW;
+        {   // A fragment rows: block mh, row lane & 31, K half lane / 32 (rows past the tile read token 0)
+            const int t = src_row[block_row<MW>(0, mh) + (lane & 31)];
+            g.asrc = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K) + 16 * (lane >> 5);
+        }
+        int brow[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) brow[j] = (j < NI / 2 ? 0 : 128) + nh * (128 / NW) + 32 * (j % (NI / 2));
+        const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
+            g.acc[j] = f32x16_t{};
+        }
+
+        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
+
+        if constexpr (AI == 1) {
+            uint16_t* h = static_cast<uint16_t*>(a.h);
+#pragma unroll
+            for (int j = 0; j < NI / 2; ++j) {
+                const int col = n0 + brow[j] + (lane & 31);
+                if (col >= F) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = block_row<MW>(0, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    if (row < tr.nrows) {
+                        const float gv = g.acc[j][v], uv = g.acc[j + NI / 2][v];
+                        h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+                    }
+                }
+            }
+        }
+    }
 };
 
 template <int BM, int MW, int WV>
 __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     using GEO = Geo<BM, MW, WV>;
-    __shared__ __attribute__((aligned(1024))) uint8_t L0[GEO::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t L1[GEO::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t L2[GEO::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t L3[GEO::STAGE];
+    static_assert(BM * SROW == XS, "a stage's A rows fill one LDS array");
+    // eight separate arrays (separate objects, so the compiler can tell a
+    // read of one from the copies still landing in the others): hot tiles
+    // use them as four K32 stages of (A rows, B rows), cold tiles as eight
+    // B-row stages
+    __shared__ __attribute__((aligned(1024))) uint8_t X0[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X1[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X2[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X3[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X4[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X5[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X6[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X7[XS];
     __shared__ int src_row[BM];
     int tile, ntile;
     if (!work_item<4>(tile_count(a), tile, ntile)) return;
@@ -374,8 +577,14 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
         src_row[r] = t;
     }
     __syncthreads();
-    GateUpTile<BM, MW, WV> body{a, tr, src_row, L0, L1, L2, L3, F, n0, wave, lane};
-    dispatch<GEO, 0, 1>(active_blocks<GEO, MW, WV>(tr.nrows, wave % MW), active_a_copies<GEO, WV>(tr.nrows), body);
+    GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, F, n0, wave, lane};
+    const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
+    if (tr.nrows <= COLD_ROWS) {
+        if (ai) body.template run_cold<1>();
+        else body.template run_cold<0>();
+    } else {
+        dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -388,7 +597,7 @@ struct DownTile {
     const TileRows& tr;
     const int* dst_row;
     const float* wrow;
-    uint8_t *L0, *L1, *L2, *L3;
+    uint8_t *X0, *X1, *X2, *X3, *X4, *X5, *X6, *X7;
     int n0, wave, lane;
 
     template <int AI, int NCAA>
@@ -407,7 +616,7 @@ struct DownTile {
 #pragma unroll
         for (int qa = 0; qa < G::NCPA; ++qa) {
             const int q = copy_index<G, GEO>(qa);
-            g.dst[qa] = (q * WV + wave) * 1024;
+            g.dst[qa] = (q * WV + wave) * 1024 - (q < GEO::NCA ? 0 : BM * SROW);
             const int row = copy_row(q, WV, wave, lane);
             if (q < GEO::NCA) {
                 const int rr = row < tr.nrows ? row : 0;  // rows past the tile: never stored
@@ -428,7 +637,7 @@ struct DownTile {
 #pragma unroll
             for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
 
-        k_loop(g, K / SK, L0, L1, L2, L3);
+        k_loop(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
 
         float* out = shared ? a.shared_out : a.slot_out;
 #pragma unroll
@@ -447,15 +656,82 @@ struct DownTile {
                 }
             }
     }
+
+    // a tile of at most COLD_ROWS rows (see k_loop_cold)
+    template <int AI>
+    __device__ __forceinline__ void run_cold() {
+        using G = GemmCold<GEO, AI>;
+        constexpr int NI = GEO::NI, NW = GEO::NW;
+        const bool shared = tr.g == a.E;
+        const int K = shared ? a.Fs : a.F;
+        const int N = a.d;
+        G g;
+        const int cch = copy_col(lane);
+        const MatRef& D = shared ? a.s_down : a.down;
+        const int ge = shared ? 0 : tr.g;
+        const uint16_t* dbase = static_cast<const uint16_t*>(D.q) + ((size_t)ge * N + n0) * K;
+        const uint16_t* hbase = static_cast<const uint16_t*>(a.h) + (size_t)tr.rbeg * a.ldh;
+#pragma unroll
+        for (int qb = 0; qb < G::NCB; ++qb) {
+            const int q = GEO::NCA + qb;
+            g.dst[qb] = (q * WV + wave) * 1024 - BM * SROW;
+            const int br = copy_row(q, WV, wave, lane) - BM;
+            const int rr = n0 + br < N ? br : 0;
+            g.src[qb] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K + cch);
+        }
+        const int mh = wave % MW, nh = wave / MW;
+        {   // A fragment rows: block mh, row lane & 31, K half lane / 32 (rows past the tile: never stored)
+            const int row = block_row<MW>(0, mh) + (lane & 31);
+            const int rr = row < tr.nrows ? row : 0;
+            g.asrc = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh) + 16 * (lane >> 5);
+        }
+        int brow[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) brow[j] = nh * (SBN / NW) + 32 * j;
+        const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
+            g.acc[j] = f32x16_t{};
+        }
+
+        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
+
+        if constexpr (AI == 1) {
+            float* out = shared ? a.shared_out : a.slot_out;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = block_row<MW>(0, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < tr.nrows && dst_row[row] >= 0) {
+                    const size_t base = (size_t)dst_row[row] * N;
+                    const float w = wrow[row];
+#pragma unroll
+                    for (int j = 0; j < NI; ++j) {
+                        const int col = n0 + brow[j] + (lane & 31);
+                        if (col < N) out[base + col] = w * g.acc[j][v];
+                    }
+                }
+            }
+        }
+    }
 };
 
 template <int BM, int MW, int WV>
 __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     using GEO = Geo<BM, MW, WV>;
-    __shared__ __attribute__((aligned(1024))) uint8_t L0[GEO::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t L1[GEO::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t L2[GEO::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t L3[GEO::STAGE];
+    static_assert(BM * SROW == XS, "a stage's A rows fill one LDS array");
+    // eight separate arrays (separate objects, so the compiler can tell a
+    // read of one from the copies still landing in the others): hot tiles
+    // use them as four K32 stages of (A rows, B rows), cold tiles as eight
+    // B-row stages
+    __shared__ __attribute__((aligned(1024))) uint8_t X0[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X1[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X2[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X3[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X4[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X5[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X6[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t X7[XS];
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
     int tile, ntile;
@@ -485,8 +761,14 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
         wrow[r] = w;
     }
     __syncthreads();
-    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, L0, L1, L2, L3, n0, wave, lane};
-    dispatch<GEO, 0, 1>(active_blocks<GEO, MW, WV>(tr.nrows, wave % MW), active_a_copies<GEO, WV>(tr.nrows), body);
+    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, n0, wave, lane};
+    const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
+    if (tr.nrows <= COLD_ROWS) {
+        if (ai) body.template run_cold<1>();
+        else body.template run_cold<0>();
+    } else {
+        dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
+    }
 }
 
 // wavefront grid of the kernels launched: DMA_MW x (DMA_WV / DMA_MW)
