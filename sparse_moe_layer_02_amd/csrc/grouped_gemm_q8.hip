@@ -59,6 +59,39 @@ __device__ __forceinline__ void q8_to_bf16(u32x4 w, u32x4& lo, u32x4& hi) {
 
 __device__ __forceinline__ u32x4 ld16b(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// The K loop of both kernels.  Chunk c (BK wide) is computed from LDS buffer
+// c & 1; meanwhile the loads of chunks c + 1 .. c + NR sit in a ring of NR
+// register stages (the one of chunk c + 1 issued NR - 1 chunks ago).  After
+// chunk c's MFMAs, stage (c + 1) % NR is widened into the other buffer and
+// reloaded with chunk c + 1 + NR; one barrier per chunk then separates the
+// reads of a buffer from its next fill.
+#ifndef Q8_RING
+#define Q8_RING 4
+#endif
+constexpr int NR = Q8_RING;
+
+template <class St, class GL, class LS, class CP>
+__device__ __forceinline__ void q8_k_loop(int nch, St (&R)[NR], GL gload, LS lstore, CP compute) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+        if (i < nch) gload(R[i], i * BK);
+    lstore(R[0], 0);
+    if (NR < nch) gload(R[0], NR * BK);
+    __syncthreads();
+    for (int c0 = 0; c0 < nch; c0 += NR) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+            const int c = c0 + q;
+            if (c < nch) {
+                compute(q & 1);
+                if (c + 1 < nch) lstore(R[(q + 1) % NR], (q + 1) & 1);
+                if (c + 1 + NR < nch) gload(R[(q + 1) % NR], (c + 1 + NR) * BK);
+                __syncthreads();
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gate/up
 // ---------------------------------------------------------------------------
@@ -178,24 +211,11 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_q8_kernel(FfnArgs a) {
             }
         }
     };
-    Stage R0, R1;
-    gload(R0, 0);
-    if (BK < K) gload(R1, BK);
-    lstore(R0, 0);
-    __syncthreads();
-    for (int k0 = 0; k0 < K; k0 += 2 * BK) {
-        if (k0 + 2 * BK < K) gload(R0, k0 + 2 * BK);
-        compute(0, 0);
-        compute(0, 1);
-        if (k0 + BK < K) lstore(R1, 1);
-        __syncthreads();
-        if (k0 + BK >= K) break;
-        if (k0 + 3 * BK < K) gload(R1, k0 + 3 * BK);
-        compute(1, 0);
-        compute(1, 1);
-        if (k0 + 2 * BK < K) lstore(R0, 0);
-        __syncthreads();
-    }
+    Stage R[NR];
+    q8_k_loop(K / BK, R, gload, lstore, [&](int b) {
+        compute(b, 0);
+        compute(b, 1);
+    });
 
     const int col = n0 + 32 * nh + (lane & 31);
     if (col < F) {
@@ -337,24 +357,11 @@ __global__ __launch_bounds__(256, 2) void down_mfma_q8_kernel(FfnArgs a) {
             }
         }
     };
-    Stage R0, R1;
-    gload(R0, 0);
-    if (BK < K) gload(R1, BK);
-    lstore(R0, 0);
-    __syncthreads();
-    for (int k0 = 0; k0 < K; k0 += 2 * BK) {
-        if (k0 + 2 * BK < K) gload(R0, k0 + 2 * BK);
-        compute(0, 0);
-        compute(0, 1);
-        if (k0 + BK < K) lstore(R1, 1);
-        __syncthreads();
-        if (k0 + BK >= K) break;
-        if (k0 + 3 * BK < K) gload(R1, k0 + 3 * BK);
-        compute(1, 0);
-        compute(1, 1);
-        if (k0 + 2 * BK < K) lstore(R0, 0);
-        __syncthreads();
-    }
+    Stage R[NR];
+    q8_k_loop(K / BK, R, gload, lstore, [&](int b) {
+        compute(b, 0);
+        compute(b, 1);
+    });
 
     float* out = shared ? a.shared_out : a.slot_out;
     const int c0 = n0 + 64 * nh + (lane & 31);

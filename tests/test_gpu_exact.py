@@ -11,7 +11,8 @@ dropped, repeated or taken from the wrong rows) changes h, and with it y, by
 a whole number.  Every expert kernel family is reached: the decode GEMVs
 (bf16, int8, fp32), the grouped MFMA GEMMs with 64- and 256-row tiles (the
 latter through LDS copies, with short tiles, also at d = 6144), the int8
-grouped GEMMs, and the prefill GEMVs (int8 with few rows per expert, fp32).
+grouped GEMMs (K loops of whole and partial register rings), and the
+prefill GEMVs (int8 with few rows per expert, fp32).
 """
 import sys
 
@@ -52,6 +53,10 @@ CASES = {
     # int8 grouped GEMMs (2 rows per expert or more) and int8 GEMVs (fewer)
     "prefill_q8_mfma": dict(T=64, d=320, E=16, k=4, F=192, Fs=256, w="q8b32"),
     "prefill_q8_gemv": dict(T=9, d=256, E=32, k=2, F=128, w="q8b32"),
+    # int8 grouped GEMMs with K a multiple of the register ring (4 chunks of
+    # 64): full and partial 64-row tiles, skewed loads from 4 to 108 rows
+    "prefill_q8_ring": dict(T=96, d=512, E=8, k=2, F=256, Fs=512, w="q8b32"),
+    "prefill_q8_ring_skewed": dict(T=200, d=256, E=16, k=2, F=512, w="q8b32", skew=1.0),
     # fp32 prefill (GEMVs over the grouped rows)
     "prefill_f32": dict(T=40, d=128, E=8, k=2, F=64, act="f32", w="f32"),
 }
@@ -86,7 +91,7 @@ def test_exact_layer_bitwise(orc, case):
 
 
 @pytest.mark.parametrize("case", ["prefill_bm64", "prefill_bm256_skewed", "prefill_bm256", "prefill_q8_mfma",
-                                  "decode_q8_T5"])
+                                  "prefill_q8_ring", "decode_q8_T5"])
 def test_exact_split_entry_points(orc, case):
     """moe_expert_ffn and moe_combine alone, with caller routing weights that
     are powers of two: slot_out, shared_out and y bit for bit."""
