@@ -141,12 +141,14 @@ struct Gemm {
         return *reinterpret_cast<const bf16x8_t*>(S + (ks ? (fo[fi] ^ 32) : fo[fi]));
     }
     // MFMA t of a K16 step: block (i, j) = (t / NI, t % NI); fragments are
-    // ordered A0, B0..B(NI-1), A1.. so that the first MFMAs wait least.
+    // ordered A0, B0..B(NI-1), A1.. so that the first MFMAs wait least.  The
+    // weight fragment goes in as the instruction's first operand, so a lane's
+    // accumulators hold one row of the tile (see the epilogues).
     static __device__ __forceinline__ int fa_idx(int i) { return i == 0 ? 0 : NI + i; }
     static __device__ __forceinline__ int fb_idx(int j) { return 1 + j; }
     __device__ __forceinline__ void mfma(const bf16x8_t (&f)[NFS], int t) {
         const int i = t / NI, j = t % NI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[fa_idx(i)], f[fb_idx(j)], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[fb_idx(j)], f[fa_idx(i)], acc[i][j], 0, 0, 0);
     }
 };
 
@@ -370,7 +372,7 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int jj = 0; jj < NI; ++jj)
-                    g.acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[K][s], b[s][jj], g.acc[jj], 0, 0, 0);
+                    g.acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[s][jj], ring[K][s], g.acc[jj], 0, 0, 0);
         }
     };
     issue_pair(ic<0>(), 0);
@@ -399,6 +401,27 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
 }
 
 }  // namespace
+
+// Epilogue layout.  With the weight fragment as the MFMA's first operand, the
+// 32 x 32 block's lane l holds tile row (l & 31) of its row block and the 16
+// columns 8 * (v / 4) + 4 * (l / 32) + v % 4, v = 0..15 of its column block:
+// four runs of four adjacent columns, so each run leaves in one 8-byte (h,
+// bf16) or 16-byte (slot_out, fp32) store, and the two lanes of a row
+// together write 16 or 32 contiguous bytes per run pair.
+__device__ __forceinline__ int run_col(int q, int lane) { return 8 * q + 4 * (lane >> 5); }
+
+// h = bf16(silu(g) * u) of four adjacent columns as one 8-byte store.
+__device__ __forceinline__ void store_h4(uint16_t* dst, const f32x16_t& g, const f32x16_t& u, int q) {
+    uint32_t w[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float g0 = g[4 * q + 2 * e], u0 = u[4 * q + 2 * e];
+        const float g1 = g[4 * q + 2 * e + 1], u1 = u[4 * q + 2 * e + 1];
+        w[e] = (uint32_t)f32_to_bf16(g0 / (1.0f + expf(-g0)) * u0) |
+               ((uint32_t)f32_to_bf16(g1 / (1.0f + expf(-g1)) * u1) << 16);
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+}
 
 // ---------------------------------------------------------------------------
 // gate/up: BM rows x (128 gate + 128 up) columns per workgroup
@@ -457,22 +480,19 @@ struct GateUpTile {
 
         k_loop(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
 
-        // epilogue: lane holds column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4 of each block
+        // epilogue: lane holds row (lane & 31) of each row block (see run_col)
         uint16_t* h = static_cast<uint16_t*>(a.h);
 #pragma unroll
-        for (int j = 0; j < NI / 2; ++j) {
-            const int col = n0 + brow[j] + (lane & 31);
-            if (col >= F) continue;
+        for (int i = 0; i < AI; ++i) {
+            const int row = block_row<MW>(i, mh) + (lane & 31);
+            if (row >= tr.nrows) continue;
+            uint16_t* hrow = h + (size_t)(tr.rbeg + row) * a.ldh + n0;
 #pragma unroll
-            for (int i = 0; i < AI; ++i)
+            for (int j = 0; j < NI / 2; ++j) {
+                if (n0 + brow[j] >= F) continue;  // (F is a multiple of 64: whole blocks)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = block_row<MW>(i, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    if (row < tr.nrows) {
-                        const float gv = g.acc[i][j][v], uv = g.acc[i][j + NI / 2][v];
-                        h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
-                    }
-                }
+                for (int q = 0; q < 4; ++q) store_h4(hrow + brow[j] + run_col(q, lane), g.acc[i][j], g.acc[i][j + NI / 2], q);
+            }
         }
     }
 
@@ -519,18 +539,14 @@ struct GateUpTile {
         k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
 
         if constexpr (AI == 1) {
-            uint16_t* h = static_cast<uint16_t*>(a.h);
+            const int row = block_row<MW>(0, mh) + (lane & 31);
+            if (row < tr.nrows) {
+                uint16_t* hrow = static_cast<uint16_t*>(a.h) + (size_t)(tr.rbeg + row) * a.ldh + n0;
 #pragma unroll
-            for (int j = 0; j < NI / 2; ++j) {
-                const int col = n0 + brow[j] + (lane & 31);
-                if (col >= F) continue;
+                for (int j = 0; j < NI / 2; ++j) {
+                    if (n0 + brow[j] >= F) continue;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = block_row<MW>(0, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    if (row < tr.nrows) {
-                        const float gv = g.acc[j][v], uv = g.acc[j + NI / 2][v];
-                        h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
-                    }
+                    for (int q = 0; q < 4; ++q) store_h4(hrow + brow[j] + run_col(q, lane), g.acc[j], g.acc[j + NI / 2], q);
                 }
             }
         }
@@ -639,22 +655,24 @@ struct DownTile {
 
         k_loop(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
 
+        // epilogue: lane holds row (lane & 31) of each row block (see run_col)
         float* out = shared ? a.shared_out : a.slot_out;
 #pragma unroll
-        for (int i = 0; i < AI; ++i)
+        for (int i = 0; i < AI; ++i) {
+            const int row = block_row<MW>(i, mh) + (lane & 31);
+            if (row >= tr.nrows || dst_row[row] < 0) continue;
+            float* orow = out + (size_t)dst_row[row] * N + n0;
+            const float w = wrow[row];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = block_row<MW>(i, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < tr.nrows && dst_row[row] >= 0) {
-                    const size_t base = (size_t)dst_row[row] * N;
-                    const float w = wrow[row];
+            for (int j = 0; j < NI; ++j) {
+                if (n0 + brow[j] >= N) continue;  // (d is a multiple of 64: whole blocks)
 #pragma unroll
-                    for (int j = 0; j < NI; ++j) {
-                        const int col = n0 + brow[j] + (lane & 31);
-                        if (col < N) out[base + col] = w * g.acc[i][j][v];
-                    }
-                }
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4*>(orow + brow[j] + run_col(q, lane)) =
+                        make_float4(w * g.acc[i][j][4 * q], w * g.acc[i][j][4 * q + 1], w * g.acc[i][j][4 * q + 2],
+                                    w * g.acc[i][j][4 * q + 3]);
             }
+        }
     }
 
     // a tile of at most COLD_ROWS rows (see k_loop_cold)
@@ -698,18 +716,18 @@ struct DownTile {
         k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
 
         if constexpr (AI == 1) {
-            float* out = shared ? a.shared_out : a.slot_out;
+            const int row = block_row<MW>(0, mh) + (lane & 31);
+            if (row < tr.nrows && dst_row[row] >= 0) {
+                float* orow = (shared ? a.shared_out : a.slot_out) + (size_t)dst_row[row] * N + n0;
+                const float w = wrow[row];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = block_row<MW>(0, mh) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < tr.nrows && dst_row[row] >= 0) {
-                    const size_t base = (size_t)dst_row[row] * N;
-                    const float w = wrow[row];
+                for (int j = 0; j < NI; ++j) {
+                    if (n0 + brow[j] >= N) continue;
 #pragma unroll
-                    for (int j = 0; j < NI; ++j) {
-                        const int col = n0 + brow[j] + (lane & 31);
-                        if (col < N) out[base + col] = w * g.acc[j][v];
-                    }
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<float4*>(orow + brow[j] + run_col(q, lane)) =
+                            make_float4(w * g.acc[j][4 * q], w * g.acc[j][4 * q + 1], w * g.acc[j][4 * q + 2],
+                                        w * g.acc[j][4 * q + 3]);
                 }
             }
         }
