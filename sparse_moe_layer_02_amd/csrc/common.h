@@ -33,6 +33,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// silu(g) = g / (1 + e^-g) in fp32 with the hardware exponential and
+// reciprocal (a few ulp of fp32, far below the bf16 rounding of h).  Large
+// negative g gives e^-g = inf, a reciprocal of 0 and silu = -0, as the
+// division would.
+__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 // IEEE binary16 bits -> fp32 (hardware conversion; subnormals preserved).
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);

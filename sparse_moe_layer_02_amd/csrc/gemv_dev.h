@@ -145,7 +145,7 @@ __device__ __forceinline__ void row_ptrs(const MatRef& m, int e, int rows, int c
     s = (WF == MOE_DT_Q8B32) ? m.scale + grow * (cols / 32) : nullptr;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+__device__ __forceinline__ float silu_mul(float g, float u) { return silu_f32(g) * u; }
 
 template <int AF>
 __device__ __forceinline__ void store_h(void* h, size_t idx, float v) {

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
                 const int row = (BM / 2) * mh + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (row < tr.nrows) {
                     const float g = accg[i][v], u = accu[i][v];
-                    h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+                    h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(silu_f32(g) * u);
                 }
             }
     }

@@ -417,8 +417,7 @@ __device__ __forceinline__ void store_h4(uint16_t* dst, const f32x16_t& g, const
     for (int e = 0; e < 2; ++e) {
         const float g0 = g[4 * q + 2 * e], u0 = u[4 * q + 2 * e];
         const float g1 = g[4 * q + 2 * e + 1], u1 = u[4 * q + 2 * e + 1];
-        w[e] = (uint32_t)f32_to_bf16(g0 / (1.0f + expf(-g0)) * u0) |
-               ((uint32_t)f32_to_bf16(g1 / (1.0f + expf(-g1)) * u1) << 16);
+        w[e] = (uint32_t)f32_to_bf16(silu_f32(g0) * u0) | ((uint32_t)f32_to_bf16(silu_f32(g1) * u1) << 16);
     }
     *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
 }
