@@ -174,6 +174,50 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_q8_kernel(FfnArgs a) {
         lsc[s][srow][sblk] = f16_to_f32(R.s);
     };
 
+    if (BM == 64 && tr.nrows <= 32) {
+        // A tile of at most 32 rows: wavefront w computes every row for gate
+        // columns 16w .. 16w + 15 and the same up columns, as one 32 x 32
+        // block whose B rows are those 16 gate rows, then those 16 up rows
+        // (lane l holds column l & 31 of the block: gate for l & 31 < 16),
+        // so no wavefront computes an empty row block.
+        const int r32 = lane & 31;
+        const bool up = r32 >= 16;
+        const int brow = (up ? GU_BN : 0) + 16 * wave + (r32 & 15);  // B row of this lane's column
+        f32x16_t acc = f32x16_t{};
+        auto compute1 = [&](int s, int blk) {
+            const uint8_t* L = lds[s];
+            bf16x8_t fb[2], fa[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = 2 * (2 * blk + j) + (lane >> 5);
+                fb[j] = lds_frag(L, BM + brow, c);
+                fa[j] = lds_frag(L, r32, c);
+            }
+            const float sc = lsc[s][brow][blk];
+            f32x16_t p = f32x16_t{};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j], fb[j], p, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = fmaf(sc, p[v], acc[v]);
+        };
+        Stage R[NR];
+        q8_k_loop(K / BK, R, gload, lstore, [&](int b) {
+            compute1(b, 0);
+            compute1(b, 1);
+        });
+        // lane l (l & 31 < 16) holds gate column 16w + (l & 15) of rows
+        // 8*(v/4) + 4*(l/32) + v%4; lane l + 16 the same up column
+        const int col = n0 + 16 * wave + (r32 & 15);
+        uint16_t* h = static_cast<uint16_t*>(a.h);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float u = __shfl_xor(acc[v], 16);
+            const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (!up && col < F && row < tr.nrows)
+                h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(silu_f32(acc[v]) * u);
+        }
+        return;
+    }
     const int mh = wave & 1, nh = wave >> 1;
     f32x16_t accg[MT], accu[MT];
 #pragma unroll
@@ -322,6 +366,44 @@ __global__ __launch_bounds__(256, 2) void down_mfma_q8_kernel(FfnArgs a) {
         lsc[s][srow][sblk] = f16_to_f32(R.s);
     };
 
+    float* out = shared ? a.shared_out : a.slot_out;
+    if (BM == 64 && tr.nrows <= 32) {
+        // A tile of at most 32 rows: wavefront w computes every row for
+        // output columns 32w .. 32w + 31 (one 32 x 32 block), so no
+        // wavefront computes an empty row block.
+        const int r32 = lane & 31;
+        f32x16_t acc = f32x16_t{};
+        auto compute1 = [&](int s, int blk) {
+            const uint8_t* L = lds[s];
+            bf16x8_t fb[2], fa[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = 2 * (2 * blk + j) + (lane >> 5);
+                fb[j] = lds_frag(L, BM + 32 * wave + r32, c);
+                fa[j] = lds_frag(L, r32, c);
+            }
+            const float sc = lsc[s][32 * wave + r32][blk];
+            f32x16_t p = f32x16_t{};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j], fb[j], p, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = fmaf(sc, p[v], acc[v]);
+        };
+        Stage R[NR];
+        q8_k_loop(K / BK, R, gload, lstore, [&](int b) {
+            compute1(b, 0);
+            compute1(b, 1);
+        });
+        const int col = n0 + 32 * wave + r32;
+        if (col < N) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < tr.nrows && dst_row[row] >= 0) out[(size_t)dst_row[row] * N + col] = wrow[row] * acc[v];
+            }
+        }
+        return;
+    }
     const int mh = wave & 1, nh = wave >> 1;
     f32x16_t acc0[MT], acc1[MT];
 #pragma unroll
@@ -363,7 +445,6 @@ __global__ __launch_bounds__(256, 2) void down_mfma_q8_kernel(FfnArgs a) {
         compute(b, 1);
     });
 
-    float* out = shared ? a.shared_out : a.slot_out;
     const int c0 = n0 + 64 * nh + (lane & 31);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
