@@ -203,11 +203,12 @@ DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it 
 def dominant(path_kind, w, rows_per_expert=None):
     """The gate/up kernel a layer launches.  bf16 prefill layers whose experts
     average 96 rows or more run the 256-row-tile kernels (the library's tile
-    rule: T * k >= 96 * E); int8 prefill layers run the int8 grouped GEMMs
-    from two rows per expert (T * k >= 2 * E), the GEMVs below."""
+    rule: T * k >= 96 * E); int8 prefill layers run their gate/up on the int8
+    grouped GEMM from 1.5 rows per expert (2 * T * k >= 3 * E), on the GEMVs
+    below."""
     if path_kind == "prefill" and w == "bf16" and rows_per_expert is not None and rows_per_expert >= 96:
         return DOMINANT[("prefill", "bf16", "256")]
-    if path_kind == "prefill" and w == "q8b32" and (rows_per_expert is None or rows_per_expert < 2):
+    if path_kind == "prefill" and w == "q8b32" and (rows_per_expert is None or rows_per_expert < 1.5):
         return DOMINANT[("prefill", "any")]  # int8 layers with few rows per expert: the GEMVs
     return DOMINANT.get((path_kind, w)) or DOMINANT[(path_kind, "any")]
 

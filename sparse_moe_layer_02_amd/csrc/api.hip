@@ -212,10 +212,16 @@ FfnArgs ffn_args(const moe_config* c, const Layout& L, void* ws, const void* x, 
     return f;
 }
 
-// int8 prefill layers go to the grouped MFMA GEMMs once experts average two
-// rows or more: below that the GEMVs over the grouped rows are faster (they
-// read each weight once per row, the GEMMs widen every weight tile to bf16).
-bool q8_mfma(const FfnArgs& f) { return f.wdt == MOE_DT_Q8B32 && (long)f.T * f.k >= 2L * f.E; }
+// int8 prefill layers: each product goes to the grouped MFMA GEMM once the
+// experts average enough rows for it, else to the GEMVs over the grouped rows
+// (they read each weight once per row; the GEMMs widen every weight tile to
+// bf16 and pad the tile to 32 rows).  Measured at c2's shape: the down GEMM
+// wins from about half a row per expert (32 tokens: 0.32 against 0.37 ms),
+// the gate/up GEMM from about 1.5 rows (64 tokens: 0.91 against 0.92 ms; 48
+// tokens: 0.80 against 0.75 ms).  The two products may take different kinds
+// of kernel: both read and write h and slot_out in the same layout.
+bool q8_mfma_gateup(const FfnArgs& f) { return f.wdt == MOE_DT_Q8B32 && 2L * f.T * f.k >= 3L * f.E; }
+bool q8_mfma_down(const FfnArgs& f) { return f.wdt == MOE_DT_Q8B32 && 2L * f.T * f.k >= (long)f.E; }
 
 // Experts of the prefill path: MFMA for bf16 weights and for int8 weights with
 // enough rows per expert, GEMVs otherwise.
@@ -230,12 +236,9 @@ hipError_t run_bf16_experts(const FfnArgs& f, hipStream_t st, const KTime& kg = 
 hipError_t run_expert_kernels(const FfnArgs& f, hipStream_t st) {
     hipError_t e;
     if (f.wdt == MOE_DT_BF16) return run_bf16_experts(f, st);
-    if (q8_mfma(f)) {
-        if ((e = launch_gateup_mfma_q8(f, st)) != hipSuccess) return e;
-        return launch_down_mfma_q8(f, st);
-    }
-    if ((e = launch_gateup_gemv(f, st)) != hipSuccess) return e;
-    return launch_down_slots_gemv(f, st);
+    e = q8_mfma_gateup(f) ? launch_gateup_mfma_q8(f, st) : launch_gateup_gemv(f, st);
+    if (e != hipSuccess) return e;
+    return q8_mfma_down(f) ? launch_down_mfma_q8(f, st) : launch_down_slots_gemv(f, st);
 }
 
 // The caller's stage events (if any) as per-stage kernel timings.
@@ -525,12 +528,9 @@ int enqueue_layer(const moe_config* cfg, const void* x, const moe_weights* w, fl
     FfnArgs f = ffn_args(cfg, L, ws, x, w, off, perm, wts);
     if (f.wdt == MOE_DT_BF16) {
         e = run_bf16_experts(f, st, kt[3], kt[4]);
-    } else if (q8_mfma(f)) {
-        e = launch_gateup_mfma_q8(f, st, kt[3]);
-        if (e == hipSuccess) e = launch_down_mfma_q8(f, st, kt[4]);
     } else {
-        e = launch_gateup_gemv(f, st, kt[3]);
-        if (e == hipSuccess) e = launch_down_slots_gemv(f, st, kt[4]);
+        e = q8_mfma_gateup(f) ? launch_gateup_mfma_q8(f, st, kt[3]) : launch_gateup_gemv(f, st, kt[3]);
+        if (e == hipSuccess) e = q8_mfma_down(f) ? launch_down_mfma_q8(f, st, kt[4]) : launch_down_slots_gemv(f, st, kt[4]);
     }
     if (e == hipSuccess) {
         CombineArgs c{f.slot_out, f.shared_out, y, cfg->n_tokens, cfg->top_k, cfg->d_model};

@@ -50,9 +50,11 @@ CASES = {
     "prefill_bm256_skewed_no_shared": dict(T=700, d=192, E=12, k=2, F=128, n_shared=0, skew=1.0),
     "prefill_bm256": dict(T=700, d=320, E=2, k=2, F=320, Fs=448),
     "prefill_bm256_d6144": dict(T=600, d=6144, E=2, k=1, F=2048),
-    # int8 grouped GEMMs (2 rows per expert or more) and int8 GEMVs (fewer)
+    # int8: grouped GEMMs for both products (1.5 rows per expert or more),
+    # GEMV gate/up beside the GEMM down (0.5 to 1.5 rows), GEMVs for both
     "prefill_q8_mfma": dict(T=64, d=320, E=16, k=4, F=192, Fs=256, w="q8b32"),
     "prefill_q8_gemv": dict(T=9, d=256, E=32, k=2, F=128, w="q8b32"),
+    "prefill_q8_gemv_only": dict(T=9, d=256, E=64, k=2, F=128, w="q8b32"),
     # int8 grouped GEMMs with K a multiple of the register ring (4 chunks of
     # 64): full and partial 64-row tiles, skewed loads from 4 to 108 rows
     "prefill_q8_ring": dict(T=96, d=512, E=8, k=2, F=256, Fs=512, w="q8b32"),
