@@ -193,9 +193,12 @@ DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it 
                         [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h", "kernels.h")]),
     ("prefill", "bf16"): ("gateup_mfma_kernel", [_CSRC + f for f in ("grouped_gemm.hip", "gemm_dev.h", "common.h")]),
     ("prefill", "bf16", "256"): ("gateup_dma_kernel",
-                                 [_CSRC + f for f in ("grouped_gemm_dma.hip", "gemm_dev.h", "common.h")]),
+                                 [_CSRC + f for f in ("grouped_gemm_dma.hip", "dma_dev.h", "gemm_dev.h", "common.h")]),
     ("prefill", "q8b32"): ("gateup_mfma_q8_kernel",
                            [_CSRC + f for f in ("grouped_gemm_q8.hip", "gemm_dev.h", "common.h")]),
+    ("prefill", "q8b32", "lds"): ("gateup_q8_dma_kernel",
+                                  [_CSRC + f for f in ("grouped_gemm_q8_dma.hip", "dma_dev.h", "gemm_dev.h",
+                                                       "common.h")]),
     ("prefill", "any"): ("gateup_gemv_kernel", [_CSRC + f for f in ("gemv_ffn.hip", "gemv_dev.h", "common.h")]),
 }
 
@@ -203,13 +206,16 @@ DOMINANT = {  # (path, weights) -> dominant (gate/up) kernel and the sources it 
 def dominant(path_kind, w, rows_per_expert=None):
     """The gate/up kernel a layer launches.  bf16 prefill layers whose experts
     average 96 rows or more run the 256-row-tile kernels (the library's tile
-    rule: T * k >= 96 * E); int8 prefill layers run their gate/up on the int8
-    grouped GEMM from 1.5 rows per expert (2 * T * k >= 3 * E), on the GEMVs
-    below."""
+    rule: T * k >= 96 * E); int8 prefill layers run their gate/up on the GEMVs
+    below 1.5 rows per expert (2 * T * k < 3 * E), on the LDS-copy int8 GEMM up
+    to 16 rows (when K is a multiple of 128, as in every int8 workload here),
+    on the register-staged one above."""
     if path_kind == "prefill" and w == "bf16" and rows_per_expert is not None and rows_per_expert >= 96:
         return DOMINANT[("prefill", "bf16", "256")]
     if path_kind == "prefill" and w == "q8b32" and (rows_per_expert is None or rows_per_expert < 1.5):
         return DOMINANT[("prefill", "any")]  # int8 layers with few rows per expert: the GEMVs
+    if path_kind == "prefill" and w == "q8b32" and rows_per_expert <= 16:
+        return DOMINANT[("prefill", "q8b32", "lds")]
     return DOMINANT.get((path_kind, w)) or DOMINANT[(path_kind, "any")]
 
 

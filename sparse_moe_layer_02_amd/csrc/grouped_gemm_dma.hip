@@ -44,11 +44,10 @@
 // f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1): the sixteen lanes that a 128-bit LDS
 // read serves per cycle (sixteen consecutive rows, one chunk) hit sixteen
 // different 16-byte bank groups (measured: no bank-conflict cycles).
-#include <type_traits>
-
 #include "common.h"
-#include "kernels.h"
+#include "dma_dev.h"
 #include "gemm_dev.h"
+#include "kernels.h"
 
 namespace moe {
 namespace {
@@ -58,39 +57,11 @@ constexpr int SROW = SK * 2;  // LDS bytes per row of a stage
 constexpr int SBN = 256;      // B rows per tile
 constexpr int XS = SBN * SROW;  // bytes of one LDS array: one stage's A rows or its B rows (16 KB)
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt immediates (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8);
-// a field at its maximum does not wait.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
-// Workgroup barrier without a memory fence (a fence would wait for every copy
-// in flight); the empty asm statements keep the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void barrier_nofence() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
-
 // N items spread evenly over MFMAs [A, B) of a K16 step: the items issued with
 // MFMA t are [spread(t), spread(t + 1)).
 template <int N, int A, int B>
 __device__ constexpr int spread(int t) {
     return t <= A ? 0 : t >= B ? N : ((t - A) * N + (B - A) - 1) / (B > A ? B - A : 1);
-}
-
-// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst
-// wave-uniform).
-__device__ __forceinline__ void copy16(const uint8_t* src, uint8_t* dst) {
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(dst), 16, 0, 0);
 }
 
 // Tile geometry: BM rows x 256 B rows, WV wavefronts in an MW x (WV / MW)
@@ -226,11 +197,8 @@ __device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* A0, uint8_t* B0,
     wait_vm<0>();
 }
 
-// Copy lanes: lane l of copy q of wavefront w fills stage row
-// r = (q * WV + w) * 16 + l / 4, slot l & 3, which holds logical chunk
-// (l & 3) ^ f(r); f(r) = ((l >> 3) & 3) ^ ((l >> 5) & 1) since r = l / 4 mod 16.
-__device__ __forceinline__ int copy_row(int q, int wv, int wave, int lane) { return (q * wv + wave) * 16 + (lane >> 2); }
-__device__ __forceinline__ int copy_col(int lane) { return ((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1)) * 8; }
+// Element offset of a copy lane's 16-byte chunk within a row (bf16).
+__device__ __forceinline__ int copy_col(int lane) { return copy_chunk(lane) * 8; }
 
 // Active copy index qa (0 .. NCPA-1) -> copy index of the full stage: the
 // first NCAA A-row copies, then every B-row copy.
@@ -303,9 +271,6 @@ struct GemmCold {
     int fo[NI];            // B fragment offsets (K16 step 0)
     f32x16_t acc[NI];
 };
-
-template <int K>
-using ic = std::integral_constant<int, K>;
 
 // The K loop of a cold tile: nst = K / 32 stages in eight slots; slot s holds
 // the B rows of chunk c = s mod 8, ring[s] that chunk's two A fragments.

@@ -1,0 +1,364 @@
+// grouped_gemm_q8_dma.hip - the int8 grouped GEMMs for layers whose experts
+// average few rows (a short prefill spreads its tokens over all experts: about
+// a dozen rows each), weights copied straight from global memory into LDS.
+//
+//   gate/up:  H_e = bf16( silu(A_e Wg[e]^T) * (A_e Wu[e]^T) ),  A_e = rows of x
+//   down:     slot_out[f, :] = w_f * (H_e Wd[e]^T)[row of f]
+// with W[n, k] = scale[n, k / 32] * q[n, k] (blocks of 32 along K, one fp16
+// scale each): the operation of grouped_gemm_q8.hip, on the same tile list.
+//
+// Why a second design.  The register-staged kernels widen every weight to
+// bf16 through registers into LDS, one 64-wide K chunk per barrier, two
+// workgroups per CU; on these tiles their matrix work is a sliver and that
+// staging, not HBM, sets their pace.  Here the int8 rows go into LDS with the
+// buffer-load-to-LDS path (no VGPRs, no LDS store instructions), eight
+// 64-wide K stages deep, and each wavefront widens only the 8 bytes per lane
+// its MFMA step reads.
+//
+// Pass: at most 32 rows (a 64-row tile of the list takes two) x 256 weight rows.  Gate/up: 128 gate columns and the
+// same 128 up columns; wavefront w owns gate columns 16w .. 16w + 15 and the
+// same up columns as one 32 x 32 MFMA block (B rows: those 16 gate rows, then
+// those 16 up rows).  Down: wavefront w owns output columns 32w .. 32w + 31.
+// A (the tile's bf16 rows of x or h, 128 bytes per row and stage) is copied
+// into LDS beside the weight rows by wavefronts 0-3, one 1 KB copy each, and
+// read by all eight.
+//
+// Exactness as in grouped_gemm_q8.hip: q is exact in bf16, every MFMA
+// product q * x is exact, each block's two K16 steps accumulate into fresh
+// registers and the block's scale multiplies that partial sum.  In the
+// 32 x 32 layout a lane holds one column (one weight row), so one scale per
+// lane and block.
+#include "common.h"
+#include "dma_dev.h"
+#include "gemm_dev.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int QWV = 8;                   // wavefronts per workgroup
+constexpr int QSK = 64;                  // K per stage: 64 int8 = 64 bytes of each weight row
+constexpr int QBN = 256;                 // weight rows per tile
+constexpr int QXS = QBN * QSK;           // bytes of one stage's weight rows (16 KB)
+constexpr int QNCB = QXS / (1024 * QWV); // 1 KB weight copies per wavefront per stage (2)
+constexpr int QROWS = 32;                // rows of a tile these kernels take
+constexpr int QAS = QROWS * QSK * 2;     // bytes of one stage's A rows (4 KB: 32 rows x 64 bf16)
+constexpr int QAW = QAS / 1024;          // wavefronts that copy A rows (one 1 KB copy each)
+static_assert(QNCB * 1024 * QWV == QXS && QAW <= QWV, "copy geometry");
+
+// Eight int8 -> eight bf16 (exact: |q| <= 127).
+__device__ __forceinline__ bf16x8_t widen8(uint32_t lo, uint32_t hi) {
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int32_t v = (int32_t)(j ? hi : lo);
+        const float f0 = (float)((v << 24) >> 24), f1 = (float)((v << 16) >> 24);
+        const float f2 = (float)((v << 8) >> 24), f3 = (float)(v >> 24);
+        out[2 * j] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+        out[2 * j + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+    }
+    bf16x8_t r;
+    __builtin_memcpy(&r, out, 16);
+    return r;
+}
+
+// Per-lane sources and LDS offsets of one tile.
+struct QTile {
+    const uint8_t* asrc;     // A bytes this copy lane fetches at K = 0 (wavefronts < QAW)
+    int adst;                // wave-uniform offset of that copy in an A stage
+    const uint8_t* src[QNCB];// weight-row bytes each copy lane fetches at K = 0
+    int dst[QNCB];           // wave-uniform offset of each copy in a stage
+    const uint32_t* scp;     // two fp16 block scales of the lane's weight row per stage
+    int fo;                  // LDS offset of the lane's weight fragment (row, half h) in a stage
+    int fsw;                 // that row's chunk swizzle
+    int ao;                  // LDS offset of the lane's A row (lane & 31) in an A stage
+    f32x16_t acc;
+};
+
+// A rows in LDS: 128 bytes (eight 16-byte chunks) per row; chunk c of row r
+// sits at slot c ^ (r & 7), so the 32 rows a fragment read covers spread
+// over the banks.  Copy lane l of A copy q fills row 8q + l / 8, slot l % 8.
+__device__ __forceinline__ int a_copy_row(int q, int lane) { return 8 * q + (lane >> 3); }
+__device__ __forceinline__ int a_copy_chunk(int lane) { return (lane & 7) ^ ((lane >> 3) & 7); }
+
+// The K loop: nst = K / 64 stages (even) in eight slots; slot s holds the
+// weight rows (X) and A rows (Y) of chunk c = s mod 8, sc[s] the lane's block
+// scales of that chunk.  Chunks are fetched in pairs (2m, 2m + 1): the two
+// 64-byte halves of every 128-byte line of a weight row go out back to back.
+// At an even stage j the pair (j, j + 1) has landed (the pairs of chunks
+// j + 2 .. j + 5 may still be in flight) and every wavefront has finished
+// reading slots j - 2 and j - 1, which then receive the pair (j + 6, j + 7).
+// HASA: this wavefront copies A rows (one more vector-memory operation per
+// chunk, so its wait counts differ).
+template <bool HASA>
+__device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
+    constexpr int NCP = QNCB + 1 + (HASA ? 1 : 0);  // vector-memory operations per chunk
+    uint32_t sc[8];
+    const int last = nst - 1;
+    auto kc = [&](int c) { return c < last ? c : last; };  // chunks past the end re-read the last (unused)
+    auto issue_pair = [&](auto kk, int c) {
+        constexpr int K = decltype(kk)::value;
+        static_assert(K % 2 == 0, "pairs start at even slots");
+        const int c0 = kc(c), c1 = kc(c + 1);
+        sc[K] = g.scp[c0];
+        sc[K + 1] = g.scp[c1];
+        if constexpr (HASA) {
+            copy16(g.asrc + (size_t)c0 * 128, Y[K] + g.adst);
+            copy16(g.asrc + (size_t)c1 * 128, Y[K + 1] + g.adst);
+        }
+#pragma unroll
+        for (int q = 0; q < QNCB; ++q) {
+            copy16(g.src[q] + (size_t)c0 * QSK, X[K] + g.dst[q]);
+            copy16(g.src[q] + (size_t)c1 * QSK, X[K + 1] + g.dst[q]);
+        }
+    };
+    auto stage = [&](auto kk, int j) {
+        constexpr int K = decltype(kk)::value;
+        if constexpr (K % 2 == 0) {
+            wait_lgkm0();
+            wait_vm<4 * NCP>();
+            barrier_nofence();
+            issue_pair(ic<(K + 6) % 8>(), j + 6);
+        }
+        const uint8_t* S = X[K];
+        const uint8_t* A = Y[K];
+        uint2 wq[4];
+        bf16x8_t fa[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            wq[s] = *reinterpret_cast<const uint2*>(S + g.fo + ((s ^ g.fsw) << 4));
+            fa[s] = *reinterpret_cast<const bf16x8_t*>(A + g.ao + (((2 * s + (threadIdx.x >> 5 & 1)) ^ (threadIdx.x & 7)) << 4));
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            f32x16_t p = f32x16_t{};
+#pragma unroll
+            for (int s = 2 * b; s < 2 * b + 2; ++s)
+                p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], widen8(wq[s].x, wq[s].y), p, 0, 0, 0);
+            const float scv = f16_to_f32((uint16_t)(sc[K] >> (16 * b)));
+#pragma unroll
+            for (int v = 0; v < 16; ++v) g.acc[v] = fmaf(scv, p[v], g.acc[v]);
+        }
+    };
+    issue_pair(ic<0>(), 0);
+    issue_pair(ic<2>(), 2);
+    issue_pair(ic<4>(), 4);
+    int j = 0;
+    for (; j + 8 <= nst; j += 8) {
+        stage(ic<0>(), j);
+        stage(ic<1>(), j + 1);
+        stage(ic<2>(), j + 2);
+        stage(ic<3>(), j + 3);
+        stage(ic<4>(), j + 4);
+        stage(ic<5>(), j + 5);
+        stage(ic<6>(), j + 6);
+        stage(ic<7>(), j + 7);
+    }
+    if (j < nst) stage(ic<0>(), j);
+    if (j + 1 < nst) stage(ic<1>(), j + 1);
+    if (j + 2 < nst) stage(ic<2>(), j + 2);
+    if (j + 3 < nst) stage(ic<3>(), j + 3);
+    if (j + 4 < nst) stage(ic<4>(), j + 4);
+    if (j + 5 < nst) stage(ic<5>(), j + 5);
+    if (j + 6 < nst) stage(ic<6>(), j + 6);
+    // no copy may still be writing LDS when the workgroup ends
+    wait_vm<0>();
+}
+
+// Copy and fragment set-up shared by both kernels.  wrow(sr) is the global
+// address of stage row sr's weight bytes at K = 0, srow(br) the scale row of
+// fragment row br, arow(r) the global address of A row r (r < 32) at K = 0.
+template <class WR, class SR, class AR>
+__device__ __forceinline__ void q8_dma_setup(QTile& g, int wave, int lane, int br, WR wrow, SR srow, AR arow) {
+#pragma unroll
+    for (int q = 0; q < QNCB; ++q) {
+        const int sr = copy_row(q, QWV, wave, lane);
+        g.src[q] = wrow(sr) + copy_chunk(lane) * 16;
+        g.dst[q] = (q * QWV + wave) * 1024;
+    }
+    const int aq = wave < QAW ? wave : 0;
+    g.asrc = arow(a_copy_row(aq, lane)) + a_copy_chunk(lane) * 16;
+    g.adst = aq * 1024;
+    g.fsw = slot_swz(br);
+    g.fo = br * QSK + 8 * (lane >> 5);
+    g.ao = (lane & 31) * 128;
+    g.scp = srow(br);
+    g.acc = f32x16_t{};
+}
+
+// Eight weight stages of 16 KB and eight A stages of 4 KB: the whole 160 KB.
+#define Q8_DMA_LDS                                                                 \
+    __shared__ __attribute__((aligned(1024))) uint8_t X0[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t X1[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t X2[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t X3[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t X4[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t X5[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t X6[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t X7[QXS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y0[QAS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y1[QAS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y2[QAS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y3[QAS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y4[QAS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y5[QAS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y6[QAS];                     \
+    __shared__ __attribute__((aligned(1024))) uint8_t Y7[QAS];                     \
+    uint8_t* const X[8] = {X0, X1, X2, X3, X4, X5, X6, X7};                        \
+    uint8_t* const Y[8] = {Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7}
+
+__device__ __forceinline__ void q8_run(QTile& g, int nst, int wave, uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
+    if (wave < QAW) q8_k_loop_dma<true>(g, nst, X, Y);
+    else q8_k_loop_dma<false>(g, nst, X, Y);
+}
+
+// One pass of a gate/up tile: rows [tr.rbeg, tr.rbeg + tr.nrows), at most 32.
+__device__ __forceinline__ void gateup_q8_dma_pass(const FfnArgs& a, const TileRows& tr, int F, int n0, int wave,
+                                                   int lane, uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
+    const bool shared = tr.g == a.E;
+    const int K = a.d, KB = K / 32;
+    const int r32 = lane & 31;
+    const MatRef& G = shared ? a.s_gate : a.gate;
+    const MatRef& U = shared ? a.s_up : a.up;
+    const size_t e0 = (size_t)(shared ? 0 : tr.g) * F;
+    // stage rows 0..127: gate rows n0 + r, 128..255: up rows n0 + r - 128 (rows past F read row n0)
+    auto grow = [&](int sr) -> size_t { const int n = n0 + (sr & 127); return e0 + (n < F ? n : n0); };
+    // A row r: the token of tile row r (rows past the tile read token 0; their results are never stored)
+    auto arow = [&](int r) -> const uint8_t* {
+        int t = 0;
+        if (r < tr.nrows) {
+            if (shared) {
+                t = tr.rbeg - a.T * a.k + r;
+            } else {
+                const int f = a.perm_rows[tr.rbeg + r];
+                t = (f >= 0 && f < a.T * a.k) ? f / a.k : 0;
+            }
+        }
+        return reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.x) + (size_t)t * K);
+    };
+    QTile g;
+    const int br = (r32 < 16 ? 0 : 128) + 16 * wave + (r32 & 15);
+    q8_dma_setup(
+        g, wave, lane, br,
+        [&](int sr) { return static_cast<const uint8_t*>(sr < 128 ? G.q : U.q) + grow(sr) * K; },
+        [&](int b) { return reinterpret_cast<const uint32_t*>((b < 128 ? G.scale : U.scale) + grow(b) * KB); },
+        arow);
+    q8_run(g, K / QSK, wave, X, Y);
+
+    // lane l (l & 31 < 16) holds gate column n0 + 16w + (l & 15) of rows
+    // 8*(v/4) + 4*(l/32) + v%4; lane l ^ 16 the same up column
+    const int col = n0 + 16 * wave + (r32 & 15);
+    uint16_t* h = static_cast<uint16_t*>(a.h);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const float u = __shfl_xor(g.acc[v], 16);
+        const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r32 < 16 && col < F && row < tr.nrows)
+            h[(size_t)(tr.rbeg + row) * a.ldh + col] = f32_to_bf16(silu_f32(g.acc[v]) * u);
+    }
+}
+
+// One pass of a down tile: rows [tr.rbeg, tr.rbeg + tr.nrows), at most 32.
+__device__ __forceinline__ void down_q8_dma_pass(const FfnArgs& a, const TileRows& tr, int n0, int wave, int lane,
+                                                 uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
+    const bool shared = tr.g == a.E;
+    const int N = a.d;
+    const int K = shared ? a.Fs : a.F, KB = K / 32;
+    const int r32 = lane & 31;
+    const MatRef& D = shared ? a.s_down : a.down;
+    const size_t e0 = (size_t)(shared ? 0 : tr.g) * N;
+    auto drow = [&](int sr) -> size_t { const int n = n0 + sr; return e0 + (n < N ? n : n0); };
+    QTile g;
+    const int br = 32 * wave + r32;
+    q8_dma_setup(
+        g, wave, lane, br, [&](int sr) { return static_cast<const uint8_t*>(D.q) + drow(sr) * K; },
+        [&](int b) { return reinterpret_cast<const uint32_t*>(D.scale + drow(b) * KB); },
+        [&](int r) {  // rows past the tile: never stored
+            return reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.h) +
+                                                    (size_t)(tr.rbeg + (r < tr.nrows ? r : 0)) * a.ldh);
+        });
+    q8_run(g, K / QSK, wave, X, Y);
+
+    const int col = n0 + br;
+    float* out = shared ? a.shared_out : a.slot_out;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row >= tr.nrows || col >= N) continue;
+        int dst = -1;
+        float w = 0.0f;
+        if (shared) {
+            dst = tr.rbeg - a.T * a.k + row;
+            w = 1.0f;
+        } else {
+            const int f = a.perm_rows[tr.rbeg + row];
+            if (f >= 0 && f < a.T * a.k) {
+                dst = f;
+                w = a.topk_w[f];
+            }
+        }
+        if (dst >= 0) out[(size_t)dst * N + col] = w * g.acc[v];
+    }
+}
+
+// A 64-row tile of the list runs as passes of at most 32 rows (its weights
+// are then read once per pass); the barrier between passes keeps the next
+// pass's copies out of stages other wavefronts may still be reading.
+__global__ __launch_bounds__(64 * QWV, 1) void gateup_q8_dma_kernel(FfnArgs a) {
+    Q8_DMA_LDS;
+    int tile, ntile;
+    if (!work_item<16>(tile_count(a), tile, ntile)) return;
+    TileRows t64;
+    if (!tile_rows<64>(a, tile, t64)) return;
+    const int F = t64.g == a.E ? a.Fs : a.F;
+    const int n0 = ntile * (QBN / 2);
+    if (n0 >= F) return;
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    for (int p = 0; p * QROWS < t64.nrows; ++p) {
+        if (p) __syncthreads();
+        const TileRows tr{t64.g, t64.rbeg + p * QROWS, min(QROWS, t64.nrows - p * QROWS)};
+        gateup_q8_dma_pass(a, tr, F, n0, wave, lane, X, Y);
+    }
+}
+
+__global__ __launch_bounds__(64 * QWV, 1) void down_q8_dma_kernel(FfnArgs a) {
+    Q8_DMA_LDS;
+    int tile, ntile;
+    if (!work_item<16>(tile_count(a), tile, ntile)) return;
+    TileRows t64;
+    if (!tile_rows<64>(a, tile, t64)) return;
+    const int n0 = ntile * QBN;
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    for (int p = 0; p * QROWS < t64.nrows; ++p) {
+        if (p) __syncthreads();
+        const TileRows tr{t64.g, t64.rbeg + p * QROWS, min(QROWS, t64.nrows - p * QROWS)};
+        down_q8_dma_pass(a, tr, n0, wave, lane, X, Y);
+    }
+}
+
+}  // namespace
+
+// The kernels apply when both products' K is a whole number of stage pairs
+// (K % 128 == 0) and the block scales of every weight row start on a 4-byte
+// boundary (two scales per stage load).
+bool q8_dma_ok(const FfnArgs& a) {
+    const bool ks = a.d % 128 == 0 && a.F % 128 == 0 && (!a.n_shared || a.Fs % 128 == 0);
+    return a.bm == 64 && ks;
+}
+
+hipError_t launch_gateup_q8_dma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
+    if (!q8_dma_ok(a)) return hipErrorInvalidValue;
+    const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
+    dim3 grid(a.max_tiles, (fmax + QBN / 2 - 1) / (QBN / 2));
+    launch_kernel(gateup_q8_dma_kernel, grid, 64 * QWV, st, kt, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_q8_dma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
+    if (!q8_dma_ok(a)) return hipErrorInvalidValue;
+    dim3 grid(a.max_tiles, (a.d + QBN - 1) / QBN);
+    launch_kernel(down_q8_dma_kernel, grid, 64 * QWV, st, kt, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -122,6 +122,9 @@ hipError_t launch_gateup_dma(const FfnArgs& a, hipStream_t st, const KTime& kt =
 // grouped MFMA GEMMs for int8 (blocks of 32 + fp16 scale) weights, 64- or 128-row tiles
 hipError_t launch_gateup_mfma_q8(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 hipError_t launch_down_mfma_q8(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+bool q8_dma_ok(const FfnArgs& a);
+hipError_t launch_gateup_q8_dma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
+hipError_t launch_down_q8_dma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 hipError_t launch_down_dma(const FfnArgs& a, hipStream_t st, const KTime& kt = KTime());
 
 // The decode path (T <= MOE_DECODE_MAX_TOKENS) in four launches: router;
