@@ -68,7 +68,7 @@ struct QTile {
     int adst;                // wave-uniform offset of that copy in an A stage
     const uint8_t* src[QNCB];// weight-row bytes each copy lane fetches at K = 0
     int dst[QNCB];           // wave-uniform offset of each copy in a stage
-    const uint32_t* scp;     // two fp16 block scales of the lane's weight row per stage
+    const uint4* scp;        // the lane's weight row's block scales, eight (four stages) per 16 bytes
     int fo;                  // LDS offset of the lane's weight fragment (row, half h) in a stage
     int fsw;                 // that row's chunk swizzle
     int ao;                  // LDS offset of the lane's A row (lane & 31) in an A stage
@@ -81,9 +81,12 @@ struct QTile {
 __device__ __forceinline__ int a_copy_row(int q, int lane) { return 8 * q + (lane >> 3); }
 __device__ __forceinline__ int a_copy_chunk(int lane) { return (lane & 7) ^ ((lane >> 3) & 7); }
 
-// The K loop: nst = K / 64 stages (even) in eight slots; slot s holds the
-// weight rows (X) and A rows (Y) of chunk c = s mod 8, sc[s] the lane's block
-// scales of that chunk.  Chunks are fetched in pairs (2m, 2m + 1): the two
+// The K loop: nst = K / 64 stages (a multiple of 4) in eight slots; slot s
+// holds the weight rows (X) and A rows (Y) of chunk c = s mod 8.  The lane's
+// block scales come 16 bytes (four chunks) per load: sc[0] serves slots 0-3
+// and is reloaded at stage 4 for the next round, sc[1] serves slots 4-7 and
+// is reloaded at stage 0 of its round; each load goes out after every use of
+// the values it replaces.  Chunks are fetched in pairs (2m, 2m + 1): the two
 // 64-byte halves of every 128-byte line of a weight row go out back to back.
 // At an even stage j the pair (j, j + 1) has landed (the pairs of chunks
 // j + 2 .. j + 5 may still be in flight) and every wavefront has finished
@@ -92,16 +95,14 @@ __device__ __forceinline__ int a_copy_chunk(int lane) { return (lane & 7) ^ ((la
 // chunk, so its wait counts differ).
 template <bool HASA>
 __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
-    constexpr int NCP = QNCB + 1 + (HASA ? 1 : 0);  // vector-memory operations per chunk
-    uint32_t sc[8];
+    constexpr int NC = QNCB + (HASA ? 1 : 0);  // copies per chunk
+    uint4 sc[2];
     const int last = nst - 1;
     auto kc = [&](int c) { return c < last ? c : last; };  // chunks past the end re-read the last (unused)
     auto issue_pair = [&](auto kk, int c) {
         constexpr int K = decltype(kk)::value;
         static_assert(K % 2 == 0, "pairs start at even slots");
         const int c0 = kc(c), c1 = kc(c + 1);
-        sc[K] = g.scp[c0];
-        sc[K + 1] = g.scp[c1];
         if constexpr (HASA) {
             copy16(g.asrc + (size_t)c0 * 128, Y[K] + g.adst);
             copy16(g.asrc + (size_t)c1 * 128, Y[K + 1] + g.adst);
@@ -115,9 +116,14 @@ __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const 
     auto stage = [&](auto kk, int j) {
         constexpr int K = decltype(kk)::value;
         if constexpr (K % 2 == 0) {
+            // the pair (j, j + 1) has landed, and at stages 0 and 4 also the
+            // scale load before it: what may still be in flight is the two
+            // later pairs, plus a scale load at stages 2 and 6
             wait_lgkm0();
-            wait_vm<4 * NCP>();
+            wait_vm<K % 4 == 0 ? 4 * NC : 4 * NC + 1>();
             barrier_nofence();
+            if constexpr (K == 0) sc[1] = g.scp[kc(j + 4) >> 2];
+            if constexpr (K == 4) sc[0] = g.scp[kc(j + 4) >> 2];
             issue_pair(ic<(K + 6) % 8>(), j + 6);
         }
         const uint8_t* S = X[K];
@@ -135,11 +141,14 @@ __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const 
 #pragma unroll
             for (int s = 2 * b; s < 2 * b + 2; ++s)
                 p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], widen8(wq[s].x, wq[s].y), p, 0, 0, 0);
-            const float scv = f16_to_f32((uint16_t)(sc[K] >> (16 * b)));
+            const uint4 q4 = sc[K / 4];
+            const uint32_t w2 = (K % 4 == 0) ? q4.x : (K % 4 == 1) ? q4.y : (K % 4 == 2) ? q4.z : q4.w;
+            const float scv = f16_to_f32((uint16_t)(w2 >> (16 * b)));
 #pragma unroll
             for (int v = 0; v < 16; ++v) g.acc[v] = fmaf(scv, p[v], g.acc[v]);
         }
     };
+    sc[0] = g.scp[0];
     issue_pair(ic<0>(), 0);
     issue_pair(ic<2>(), 2);
     issue_pair(ic<4>(), 4);
@@ -241,7 +250,7 @@ __device__ __forceinline__ void gateup_q8_dma_pass(const FfnArgs& a, const TileR
     q8_dma_setup(
         g, wave, lane, br,
         [&](int sr) { return static_cast<const uint8_t*>(sr < 128 ? G.q : U.q) + grow(sr) * K; },
-        [&](int b) { return reinterpret_cast<const uint32_t*>((b < 128 ? G.scale : U.scale) + grow(b) * KB); },
+        [&](int b) { return reinterpret_cast<const uint4*>((b < 128 ? G.scale : U.scale) + grow(b) * KB); },
         arow);
     q8_run(g, K / QSK, wave, X, Y);
 
@@ -272,7 +281,7 @@ __device__ __forceinline__ void down_q8_dma_pass(const FfnArgs& a, const TileRow
     const int br = 32 * wave + r32;
     q8_dma_setup(
         g, wave, lane, br, [&](int sr) { return static_cast<const uint8_t*>(D.q) + drow(sr) * K; },
-        [&](int b) { return reinterpret_cast<const uint32_t*>(D.scale + drow(b) * KB); },
+        [&](int b) { return reinterpret_cast<const uint4*>(D.scale + drow(b) * KB); },
         [&](int r) {  // rows past the tile: never stored
             return reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.h) +
                                                     (size_t)(tr.rbeg + (r < tr.nrows ? r : 0)) * a.ldh);
@@ -338,11 +347,11 @@ __global__ __launch_bounds__(64 * QWV, 1) void down_q8_dma_kernel(FfnArgs a) {
 
 }  // namespace
 
-// The kernels apply when both products' K is a whole number of stage pairs
-// (K % 128 == 0) and the block scales of every weight row start on a 4-byte
-// boundary (two scales per stage load).
+// The kernels apply when both products' K is a whole number of four-stage
+// scale loads (K % 256 == 0: every weight row's scales then start on a
+// 16-byte boundary, the scale arrays being 16-byte aligned).
 bool q8_dma_ok(const FfnArgs& a) {
-    const bool ks = a.d % 128 == 0 && a.F % 128 == 0 && (!a.n_shared || a.Fs % 128 == 0);
+    const bool ks = a.d % 256 == 0 && a.F % 256 == 0 && (!a.n_shared || a.Fs % 256 == 0);
     return a.bm == 64 && ks;
 }
 

@@ -56,10 +56,10 @@ CASES = {
     "prefill_q8_gemv": dict(T=9, d=256, E=32, k=2, F=128, w="q8b32"),
     "prefill_q8_gemv_only": dict(T=9, d=256, E=64, k=2, F=128, w="q8b32"),
     # int8 LDS-copy grouped GEMMs (up to 8 rows per expert on average, K a
-    # multiple of 128): 32-row passes, a 40-row shared tile in two passes,
-    # skewed experts of up to 60 rows
-    "prefill_q8_dma": dict(T=40, d=256, E=16, k=2, F=256, Fs=384, w="q8b32"),
-    "prefill_q8_dma_skewed": dict(T=60, d=512, E=16, k=2, F=128, w="q8b32", skew=1.2),
+    # multiple of 256): 32-row passes, a 40-row shared tile in two passes,
+    # skewed experts of up to 37 rows, partial and whole eight-stage rounds
+    "prefill_q8_dma": dict(T=40, d=256, E=16, k=2, F=256, Fs=512, w="q8b32"),
+    "prefill_q8_dma_skewed": dict(T=60, d=768, E=16, k=2, F=256, w="q8b32", skew=1.2),
     # int8 grouped GEMMs with K a multiple of the register ring (4 chunks of
     # 64): full and partial 64-row tiles, skewed loads from 4 to 108 rows
     "prefill_q8_ring": dict(T=96, d=512, E=8, k=2, F=256, Fs=512, w="q8b32"),
