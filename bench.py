@@ -208,13 +208,13 @@ def dominant(path_kind, w, rows_per_expert=None):
     average 96 rows or more run the 256-row-tile kernels (the library's tile
     rule: T * k >= 96 * E); int8 prefill layers run their gate/up on the GEMVs
     below 1.5 rows per expert (2 * T * k < 3 * E), on the LDS-copy int8 GEMM up
-    to 16 rows (when K is a multiple of 128, as in every int8 workload here),
+    to 28 rows (when K is a multiple of 256, as in every int8 workload here),
     on the register-staged one above."""
     if path_kind == "prefill" and w == "bf16" and rows_per_expert is not None and rows_per_expert >= 96:
         return DOMINANT[("prefill", "bf16", "256")]
     if path_kind == "prefill" and w == "q8b32" and (rows_per_expert is None or rows_per_expert < 1.5):
         return DOMINANT[("prefill", "any")]  # int8 layers with few rows per expert: the GEMVs
-    if path_kind == "prefill" and w == "q8b32" and rows_per_expert <= 16:
+    if path_kind == "prefill" and w == "q8b32" and rows_per_expert <= 28:
         return DOMINANT[("prefill", "q8b32", "lds")]
     return DOMINANT.get((path_kind, w)) or DOMINANT[(path_kind, "any")]
 

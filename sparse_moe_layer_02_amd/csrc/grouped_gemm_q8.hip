@@ -466,13 +466,13 @@ __global__ __launch_bounds__(256, 2) void down_mfma_q8_kernel(FfnArgs a) {
 // variants of these kernels would need more than 256 VGPRs).  Layers whose
 // experts average few rows take the LDS-copy kernels of
 // grouped_gemm_q8_dma.hip instead (a 64-row tile there is two passes of 32
-// rows, reading its weights twice): gate/up up to 16 rows per expert, down
-// up to 8.  Measured at c2's shape (ms per launch, LDS-copy against these):
-// gate/up 0.77 / 0.90 at 64 tokens, 1.11 / 1.21 at 512, 1.27 / 1.28 at 1024,
-// 2.12 / 1.49 at 2048; down 0.42 / 0.47 at 64 tokens, 0.57 / 0.61 at 256,
-// 0.64 / 0.63 at 512, 0.75 / 0.67 at 1024.
-static bool dma_gateup(const FfnArgs& a) { return q8_dma_ok(a) && (long)a.T * a.k <= 16L * a.E; }
-static bool dma_down(const FfnArgs& a) { return q8_dma_ok(a) && (long)a.T * a.k <= 8L * a.E; }
+// rows, reading its weights twice): gate/up up to 28 rows per expert, down
+// up to 20.  Measured at c2's shape (ms per launch, LDS-copy against these):
+// gate/up 0.66 / 0.90 at 64 tokens, 1.08 / 1.28 at 1024 (24 rows), 1.50 /
+// 1.38 at 1536 (36 rows); down 0.56 / 0.64 at 512 (12 rows), 0.61 / 0.65 at
+// 768, 0.66 / 0.67 at 1024, 0.89 / 0.74 at 1536.
+static bool dma_gateup(const FfnArgs& a) { return q8_dma_ok(a) && (long)a.T * a.k <= 28L * a.E; }
+static bool dma_down(const FfnArgs& a) { return q8_dma_ok(a) && (long)a.T * a.k <= 20L * a.E; }
 
 hipError_t launch_gateup_mfma_q8(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     if (a.bm != 64) return hipErrorInvalidValue;
