@@ -250,30 +250,54 @@ __device__ __forceinline__ void dispatch(int ai, int ncaa, B& body) {
 // stream, so what bounds them is how many weight bytes a CU keeps in flight:
 // with the hot tiles' four K32 stages (A and B rows in each) three stages are
 // in flight, about 22 GB/s per CU.  A cold tile uses the same eight LDS arrays
-// as eight B-only K32 stages, seven of them in flight, and takes its A
-// fragments (one 32-row block per wavefront at most) straight from memory into
-// a ring of registers, loaded together with the B rows of the same chunk so
-// one vector-memory count covers both.
+// as eight B-only K32 stages, seven of them in flight.  Its 32 A rows per
+// stage go to eight small arrays of their own (2 KB each), copied by two of
+// the wavefronts that hold no row block (one 16-row copy each per chunk):
+// the A rows then cross the load path once per workgroup, in copies of 16
+// rows, rather than once per computing wavefront in fragment loads that each
+// touch 32 rows (about 3% of the cold tiles' time at d = 6144).
 // ---------------------------------------------------------------------------
 #ifndef COLD_ROWS_MAX
 #define COLD_ROWS_MAX 32
 #endif
 constexpr int COLD_ROWS = COLD_ROWS_MAX;
+static_assert(COLD_ROWS <= 32, "a cold tile is one 32-row block");
+constexpr int YS = 32 * SROW;  // bytes of one cold A array: one stage's 32 A rows (2 KB)
 
-template <class GEO, int AI>
+// AI: row blocks this wavefront computes (0 or 1); NA: 16-row A copies it
+// issues per stage (0 or 1; only wavefronts with no row block copy A rows).
+template <class GEO, int AI, int NA>
 struct GemmCold {
     static_assert(AI == 0 || AI == 1, "a cold tile gives a wavefront at most one row block");
+    static_assert(NA == 0 || (NA == 1 && AI == 0), "A rows are copied by wavefronts that compute nothing");
+    static constexpr int BLOCKS = AI, ACOPIES = NA;
     static constexpr int NI = GEO::NI, NCB = GEO::NCP - GEO::NCA;  // B-row copies per wavefront per stage
-    static constexpr int NCP = 2 * AI + NCB;                       // vector-memory operations per stage
-    const uint8_t* asrc;   // this lane's A fragment source at K = 0 (row lane & 31 of its block, K half lane / 32)
+    static constexpr int NCP = NA + NCB;                           // copies per wavefront per stage
+    const uint8_t* asrc;   // NA: this lane's A-row copy source at K = 0
+    int adst;              // NA: wave-uniform offset of the copy in an A array
+    int fa;                // AI: A fragment offset in an A array (K16 step 0)
     const uint8_t* src[NCB];
     int dst[NCB];          // offsets in a B array
     int fo[NI];            // B fragment offsets (K16 step 0)
     f32x16_t acc[NI];
 };
 
+// Array K of eight.
+template <int K>
+__device__ __forceinline__ uint8_t* pick8(uint8_t* a0, uint8_t* a1, uint8_t* a2, uint8_t* a3, uint8_t* a4,
+                                          uint8_t* a5, uint8_t* a6, uint8_t* a7) {
+    if constexpr (K == 0) return a0;
+    else if constexpr (K == 1) return a1;
+    else if constexpr (K == 2) return a2;
+    else if constexpr (K == 3) return a3;
+    else if constexpr (K == 4) return a4;
+    else if constexpr (K == 5) return a5;
+    else if constexpr (K == 6) return a6;
+    else return a7;
+}
+
 // The K loop of a cold tile: nst = K / 32 stages in eight slots; slot s holds
-// the B rows of chunk c = s mod 8, ring[s] that chunk's two A fragments.
+// the B rows (X array s) and the A rows (Y array s) of chunk c = s mod 8.
 // Chunks are fetched in pairs (2m, 2m + 1): the two 64-byte halves of every
 // 128-byte line of a row go out back to back, so the memory sees whole lines
 // rather than halves a stage apart.  At an even stage j: the pair (j, j + 1)
@@ -282,34 +306,23 @@ struct GemmCold {
 // receive the pair (j + 6, j + 7); odd stages only compute.
 template <class GC>
 __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t* X1, uint8_t* X2, uint8_t* X3,
-                                            uint8_t* X4, uint8_t* X5, uint8_t* X6, uint8_t* X7) {
+                                            uint8_t* X4, uint8_t* X5, uint8_t* X6, uint8_t* X7, uint8_t* Y0,
+                                            uint8_t* Y1, uint8_t* Y2, uint8_t* Y3, uint8_t* Y4, uint8_t* Y5,
+                                            uint8_t* Y6, uint8_t* Y7) {
     constexpr int NCP = GC::NCP, NI = GC::NI, NCB = GC::NCB;
-    constexpr bool HAS_A = GC::NCP > GC::NCB;
-    bf16x8_t ring[8][2];
     const int last = nst - 1;
     auto kb = [&](int c) { return (size_t)(c < last ? c : last) * SROW; };
-    auto slot = [&](auto kc) -> uint8_t* {
-        constexpr int K = decltype(kc)::value;
-        if constexpr (K == 0) return X0;
-        else if constexpr (K == 1) return X1;
-        else if constexpr (K == 2) return X2;
-        else if constexpr (K == 3) return X3;
-        else if constexpr (K == 4) return X4;
-        else if constexpr (K == 5) return X5;
-        else if constexpr (K == 6) return X6;
-        else return X7;
-    };
-    // chunks c, c + 1 into slots K, K + 1 (K even): A fragments, then the B
-    // rows, each row's two halves back to back
+    auto slot = [&](auto kc) { return pick8<decltype(kc)::value>(X0, X1, X2, X3, X4, X5, X6, X7); };
+    auto aslot = [&](auto kc) { return pick8<decltype(kc)::value>(Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7); };
+    // chunks c, c + 1 into slots K, K + 1 (K even): A rows, then the B rows,
+    // each row's two halves back to back
     auto issue_pair = [&](auto kc, int c) {
         constexpr int K = decltype(kc)::value;
         static_assert(K % 2 == 0, "pairs start at even slots");
         const size_t o0 = kb(c), o1 = kb(c + 1);
-        if constexpr (HAS_A) {
-            ring[K][0] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o0);
-            ring[K][1] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o0 + 32);
-            ring[K + 1][0] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o1);
-            ring[K + 1][1] = *reinterpret_cast<const bf16x8_t*>(g.asrc + o1 + 32);
+        if constexpr (GC::ACOPIES == 1) {
+            copy16(g.asrc + o0, aslot(kc) + g.adst);
+            copy16(g.asrc + o1, aslot(ic<K + 1>()) + g.adst);
         }
 #pragma unroll
         for (int q = 0; q < NCB; ++q) {
@@ -325,19 +338,22 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
             barrier_nofence();
             issue_pair(ic<(K + 6) % 8>(), j + 6);
         }
-        if constexpr (HAS_A) {
+        if constexpr (GC::BLOCKS == 1) {
             const uint8_t* S = slot(kc);
-            bf16x8_t b[2][NI];
+            const uint8_t* SA = aslot(kc);
+            bf16x8_t af[2], b[2][NI];
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < 2; ++s) {
+                af[s] = *reinterpret_cast<const bf16x8_t*>(SA + (s ? (g.fa ^ 32) : g.fa));
 #pragma unroll
                 for (int jj = 0; jj < NI; ++jj)
                     b[s][jj] = *reinterpret_cast<const bf16x8_t*>(S + (s ? (g.fo[jj] ^ 32) : g.fo[jj]));
+            }
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int jj = 0; jj < NI; ++jj)
-                    g.acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[s][jj], ring[K][s], g.acc[jj], 0, 0, 0);
+                    g.acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[s][jj], af[s], g.acc[jj], 0, 0, 0);
         }
     };
     issue_pair(ic<0>(), 0);
@@ -397,6 +413,7 @@ struct GateUpTile {
     const TileRows& tr;
     const int* src_row;
     uint8_t *X0, *X1, *X2, *X3, *X4, *X5, *X6, *X7;
+    uint8_t *Y0, *Y1, *Y2, *Y3, *Y4, *Y5, *Y6, *Y7;
     int F, n0, wave, lane;
 
     template <int AI, int NCAA>
@@ -461,9 +478,9 @@ struct GateUpTile {
     }
 
     // a tile of at most COLD_ROWS rows (see k_loop_cold)
-    template <int AI>
+    template <int AI, int NA>
     __device__ __forceinline__ void run_cold() {
-        using G = GemmCold<GEO, AI>;
+        using G = GemmCold<GEO, AI, NA>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
         const int K = a.d;
@@ -486,21 +503,24 @@ struct GateUpTile {
             g.src[qb] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K + cch);
         }
         const int mh = wave % MW, nh = wave / MW;
-        {   // A fragment rows: block mh, row lane & 31, K half lane / 32 (rows past the tile read token 0)
-            const int t = src_row[block_row<MW>(0, mh) + (lane & 31)];
-            g.asrc = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K) + 16 * (lane >> 5);
+        if constexpr (NA == 1) {  // A rows 16 nh .. 16 nh + 15 (rows past the tile read token 0)
+            const int t = src_row[16 * nh + (lane >> 2)];
+            g.asrc = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
+            g.adst = 16 * nh * SROW;
         }
         int brow[NI];
 #pragma unroll
         for (int j = 0; j < NI; ++j) brow[j] = (j < NI / 2 ? 0 : 128) + nh * (128 / NW) + 32 * (j % (NI / 2));
+        // fragment lanes: row lane & 31, logical chunk lane / 32 (K16 step 0)
         const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
+        g.fa = (lane & 31) * SROW + slot0 * 16;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
             g.acc[j] = f32x16_t{};
         }
 
-        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
+        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7);
 
         if constexpr (AI == 1) {
             const int row = block_row<MW>(0, mh) + (lane & 31);
@@ -533,6 +553,15 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t X5[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X6[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X7[XS];
+    // cold tiles' A rows, one K32 stage each
+    __shared__ __attribute__((aligned(1024))) uint8_t Y0[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y1[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y2[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y3[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y4[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y5[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y6[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y7[YS];
     __shared__ int src_row[BM];
     int tile, ntile;
     if (!work_item<4>(tile_count(a), tile, ntile)) return;
@@ -557,11 +586,14 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
         src_row[r] = t;
     }
     __syncthreads();
-    GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, F, n0, wave, lane};
+    GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, F, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
     if (tr.nrows <= COLD_ROWS) {
-        if (ai) body.template run_cold<1>();
-        else body.template run_cold<0>();
+        // wavefronts of row 0 compute the block; two of the others copy its A rows
+        static_assert(MW >= 2 && WV / MW >= 2, "a cold tile needs two wavefronts with no row block");
+        if (ai) body.template run_cold<1, 0>();
+        else if (wave / MW < 2) body.template run_cold<0, 1>();
+        else body.template run_cold<0, 0>();
     } else {
         dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
@@ -578,6 +610,7 @@ struct DownTile {
     const int* dst_row;
     const float* wrow;
     uint8_t *X0, *X1, *X2, *X3, *X4, *X5, *X6, *X7;
+    uint8_t *Y0, *Y1, *Y2, *Y3, *Y4, *Y5, *Y6, *Y7;
     int n0, wave, lane;
 
     template <int AI, int NCAA>
@@ -640,9 +673,9 @@ struct DownTile {
     }
 
     // a tile of at most COLD_ROWS rows (see k_loop_cold)
-    template <int AI>
+    template <int AI, int NA>
     __device__ __forceinline__ void run_cold() {
-        using G = GemmCold<GEO, AI>;
+        using G = GemmCold<GEO, AI, NA>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
         const int K = shared ? a.Fs : a.F;
@@ -662,22 +695,25 @@ struct DownTile {
             g.src[qb] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K + cch);
         }
         const int mh = wave % MW, nh = wave / MW;
-        {   // A fragment rows: block mh, row lane & 31, K half lane / 32 (rows past the tile: never stored)
-            const int row = block_row<MW>(0, mh) + (lane & 31);
+        if constexpr (NA == 1) {  // A rows 16 nh .. 16 nh + 15 (rows past the tile read row 0; never stored)
+            const int row = 16 * nh + (lane >> 2);
             const int rr = row < tr.nrows ? row : 0;
-            g.asrc = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh) + 16 * (lane >> 5);
+            g.asrc = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
+            g.adst = 16 * nh * SROW;
         }
         int brow[NI];
 #pragma unroll
         for (int j = 0; j < NI; ++j) brow[j] = nh * (SBN / NW) + 32 * j;
+        // fragment lanes: row lane & 31, logical chunk lane / 32 (K16 step 0)
         const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
+        g.fa = (lane & 31) * SROW + slot0 * 16;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
             g.acc[j] = f32x16_t{};
         }
 
-        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
+        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7);
 
         if constexpr (AI == 1) {
             const int row = block_row<MW>(0, mh) + (lane & 31);
@@ -714,6 +750,15 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t X5[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X6[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X7[XS];
+    // cold tiles' A rows, one K32 stage each
+    __shared__ __attribute__((aligned(1024))) uint8_t Y0[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y1[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y2[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y3[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y4[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y5[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y6[YS];
+    __shared__ __attribute__((aligned(1024))) uint8_t Y7[YS];
     __shared__ int dst_row[BM];
     __shared__ float wrow[BM];
     int tile, ntile;
@@ -743,11 +788,14 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
         wrow[r] = w;
     }
     __syncthreads();
-    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, n0, wave, lane};
+    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
     if (tr.nrows <= COLD_ROWS) {
-        if (ai) body.template run_cold<1>();
-        else body.template run_cold<0>();
+        // wavefronts of row 0 compute the block; two of the others copy its A rows
+        static_assert(MW >= 2 && WV / MW >= 2, "a cold tile needs two wavefronts with no row block");
+        if (ai) body.template run_cold<1, 0>();
+        else if (wave / MW < 2) body.template run_cold<0, 1>();
+        else body.template run_cold<0, 0>();
     } else {
         dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
