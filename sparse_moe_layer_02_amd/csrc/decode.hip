@@ -388,32 +388,17 @@ __global__ __launch_bounds__(DD_THREADS) void decode_down_kernel(FfnArgs a) {
 //
 // Latency: the slot headers come in with one lane-parallel load (lane s holds
 // slot s) and are broadcast with v_readlane; the h rows of all slots are
-// copied into LDS through the global->LDS path (no VGPRs); then the weight
-// row pieces of a whole batch of slots are loaded at once, unconditionally
-// (slots past the last valid one repeat it), so the compiler's wait counts
-// are exact and each slot is reduced as soon as its own pieces have landed.
+// staged into LDS (four 16-byte loads per thread, all in flight together,
+// then stored after the headers are read); then the weight row pieces of a
+// whole batch of slots are loaded at once, unconditionally (slots past the
+// last valid one repeat it), so the compiler's wait counts are exact and
+// each slot is reduced as soon as its own pieces have landed.
 // Used when F = F_s is 1-4 chunks of 64 lanes x 16 bytes, the table has at
 // most 64 slots and h fits the staging buffer; decode_down_kernel otherwise.
 // ---------------------------------------------------------------------------
 constexpr int DR_WAVES = 16;  // rows of y per workgroup
 constexpr int DR_THREADS = DR_WAVES * WAVE;
 constexpr int DR_H_BYTES = 64 * 1024;  // LDS staging buffer for h
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst
-// wave-uniform).
-__device__ __forceinline__ void copy16_lds(const uint8_t* src, uint8_t* dst) {
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(dst), 16, 0, 0);
-}
-
-// s_waitcnt for at most N vector-memory operations outstanding (vmcnt in bits
-// 3:0 and 15:14; expcnt and lgkmcnt at their maxima do not wait).
-template <int N>
-__device__ __forceinline__ void wait_vm_le() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Slot headers held across the wavefront: lane s has slot s.
 struct SlotLanes {
