@@ -250,26 +250,33 @@ __device__ __forceinline__ void dispatch(int ai, int ncaa, B& body) {
 // stream, so what bounds them is how many weight bytes a CU keeps in flight:
 // with the hot tiles' four K32 stages (A and B rows in each) three stages are
 // in flight, about 22 GB/s per CU.  A cold tile uses the same eight LDS arrays
-// as eight B-only K32 stages, seven of them in flight.  Its 32 A rows per
-// stage go to eight small arrays of their own (2 KB each), copied by two of
-// the wavefronts that hold no row block (one 16-row copy each per chunk):
-// the A rows then cross the load path once per workgroup, in copies of 16
-// rows, rather than once per computing wavefront in fragment loads that each
-// touch 32 rows (about 3% of the cold tiles' time at d = 6144).
+// as eight B-only K32 stages, seven of them in flight.  Its A rows (up to 64)
+// go to eight small arrays of their own (4 KB each), one 16-row copy per
+// chunk issued by each of two or four wavefronts: the A rows then cross the
+// load path once per workgroup, in copies of 16 rows, rather than once per
+// computing wavefront in fragment loads that each touch 32 rows (about 3% of
+// the cold tiles' time at d = 6144).  Tiles of up to 32 rows are one row
+// block, computed by the first wavefront row while two wavefronts of the
+// second copy its A rows; tiles of 33-64 rows give each wavefront row one
+// block, and the first four wavefronts copy the A rows.
 // ---------------------------------------------------------------------------
 #ifndef COLD_ROWS_MAX
 #define COLD_ROWS_MAX 32
 #endif
-constexpr int COLD_ROWS = COLD_ROWS_MAX;
-static_assert(COLD_ROWS <= 32, "a cold tile is one 32-row block");
-constexpr int YS = 32 * SROW;  // bytes of one cold A array: one stage's 32 A rows (2 KB)
+#ifndef COLD_WIDE_MAX
+#define COLD_WIDE_MAX 64
+#endif
+constexpr int COLD_ROWS = COLD_ROWS_MAX;  // one row block
+constexpr int COLD_WIDE = COLD_WIDE_MAX;  // two row blocks
+static_assert(COLD_ROWS <= 32 && COLD_WIDE <= 64, "a cold tile is at most two 32-row blocks");
+constexpr int YS = 64 * SROW;  // bytes of one cold A array: one stage's A rows (4 KB)
 
 // AI: row blocks this wavefront computes (0 or 1); NA: 16-row A copies it
-// issues per stage (0 or 1; only wavefronts with no row block copy A rows).
+// issues per stage (0 or 1).
 template <class GEO, int AI, int NA>
 struct GemmCold {
     static_assert(AI == 0 || AI == 1, "a cold tile gives a wavefront at most one row block");
-    static_assert(NA == 0 || (NA == 1 && AI == 0), "A rows are copied by wavefronts that compute nothing");
+    static_assert(NA == 0 || NA == 1, "at most one A copy per wavefront and stage");
     static constexpr int BLOCKS = AI, ACOPIES = NA;
     static constexpr int NI = GEO::NI, NCB = GEO::NCP - GEO::NCA;  // B-row copies per wavefront per stage
     static constexpr int NCP = NA + NCB;                           // copies per wavefront per stage
@@ -477,9 +484,10 @@ struct GateUpTile {
         }
     }
 
-    // a tile of at most COLD_ROWS rows (see k_loop_cold)
+    // a tile of at most COLD_WIDE rows (see k_loop_cold); ac: the A rows this
+    // wavefront copies when NA = 1 (rows 16 ac .. 16 ac + 15)
     template <int AI, int NA>
-    __device__ __forceinline__ void run_cold() {
+    __device__ __forceinline__ void run_cold(int ac) {
         using G = GemmCold<GEO, AI, NA>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
@@ -503,17 +511,18 @@ struct GateUpTile {
             g.src[qb] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K + cch);
         }
         const int mh = wave % MW, nh = wave / MW;
-        if constexpr (NA == 1) {  // A rows 16 nh .. 16 nh + 15 (rows past the tile read token 0)
-            const int t = src_row[16 * nh + (lane >> 2)];
+        if constexpr (NA == 1) {  // rows past the tile read token 0
+            const int t = src_row[16 * ac + (lane >> 2)];
             g.asrc = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
-            g.adst = 16 * nh * SROW;
+            g.adst = 16 * ac * SROW;
         }
         int brow[NI];
 #pragma unroll
         for (int j = 0; j < NI; ++j) brow[j] = (j < NI / 2 ? 0 : 128) + nh * (128 / NW) + 32 * (j % (NI / 2));
-        // fragment lanes: row lane & 31, logical chunk lane / 32 (K16 step 0)
+        // fragment lanes: row lane & 31 (of block mh for A), logical chunk
+        // lane / 32 (K16 step 0)
         const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
-        g.fa = (lane & 31) * SROW + slot0 * 16;
+        g.fa = (block_row<MW>(0, mh) + (lane & 31)) * SROW + slot0 * 16;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
@@ -562,7 +571,11 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t Y5[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y6[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y7[YS];
-    __shared__ int src_row[BM];
+    // the tile's source tokens share Y7: the hot loop never uses the Y
+    // arrays, and the cold loop reads them only before its first copy into Y7
+    // (issued after the first stage's barrier)
+    static_assert(BM * sizeof(int) <= YS, "row table fits one A array");
+    int* src_row = reinterpret_cast<int*>(Y7);
     int tile, ntile;
     if (!work_item<4>(tile_count(a), tile, ntile)) return;
     TileRows tr;
@@ -588,12 +601,16 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     __syncthreads();
     GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, F, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
+    static_assert(MW == 2 && WV >= 4, "cold tiles: one row block per wavefront row, four A-row copies");
     if (tr.nrows <= COLD_ROWS) {
         // wavefronts of row 0 compute the block; two of the others copy its A rows
-        static_assert(MW >= 2 && WV / MW >= 2, "a cold tile needs two wavefronts with no row block");
-        if (ai) body.template run_cold<1, 0>();
-        else if (wave / MW < 2) body.template run_cold<0, 1>();
-        else body.template run_cold<0, 0>();
+        if (ai) body.template run_cold<1, 0>(0);
+        else if (wave / MW < 2) body.template run_cold<0, 1>(wave / MW);
+        else body.template run_cold<0, 0>(0);
+    } else if (tr.nrows <= COLD_WIDE) {
+        // each wavefront row computes one block; the first four wavefronts copy the A rows
+        if (wave < 4) body.template run_cold<1, 1>(wave);
+        else body.template run_cold<1, 0>(0);
     } else {
         dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
@@ -672,9 +689,10 @@ struct DownTile {
         }
     }
 
-    // a tile of at most COLD_ROWS rows (see k_loop_cold)
+    // a tile of at most COLD_WIDE rows (see k_loop_cold); ac: the A rows this
+    // wavefront copies when NA = 1 (rows 16 ac .. 16 ac + 15)
     template <int AI, int NA>
-    __device__ __forceinline__ void run_cold() {
+    __device__ __forceinline__ void run_cold(int ac) {
         using G = GemmCold<GEO, AI, NA>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
@@ -695,18 +713,24 @@ struct DownTile {
             g.src[qb] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K + cch);
         }
         const int mh = wave % MW, nh = wave / MW;
-        if constexpr (NA == 1) {  // A rows 16 nh .. 16 nh + 15 (rows past the tile read row 0; never stored)
-            const int row = 16 * nh + (lane >> 2);
+        if constexpr (NA == 1) {  // rows past the tile read row 0 (never stored)
+            const int row = 16 * ac + (lane >> 2);
             const int rr = row < tr.nrows ? row : 0;
             g.asrc = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
-            g.adst = 16 * nh * SROW;
+            g.adst = 16 * ac * SROW;
         }
+        // this lane's output row and weight, read before the K loop: the
+        // LDS that holds them is reused by the A-row copies
+        const int orow_i = block_row<MW>(0, mh) + (lane & 31);
+        const int drow = AI == 1 && orow_i < tr.nrows ? dst_row[orow_i] : -1;
+        const float dw = AI == 1 && orow_i < tr.nrows ? wrow[orow_i] : 0.0f;
         int brow[NI];
 #pragma unroll
         for (int j = 0; j < NI; ++j) brow[j] = nh * (SBN / NW) + 32 * j;
-        // fragment lanes: row lane & 31, logical chunk lane / 32 (K16 step 0)
+        // fragment lanes: row lane & 31 (of block mh for A), logical chunk
+        // lane / 32 (K16 step 0)
         const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
-        g.fa = (lane & 31) * SROW + slot0 * 16;
+        g.fa = (block_row<MW>(0, mh) + (lane & 31)) * SROW + slot0 * 16;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
@@ -716,10 +740,9 @@ struct DownTile {
         k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7);
 
         if constexpr (AI == 1) {
-            const int row = block_row<MW>(0, mh) + (lane & 31);
-            if (row < tr.nrows && dst_row[row] >= 0) {
-                float* orow = (shared ? a.shared_out : a.slot_out) + (size_t)dst_row[row] * N + n0;
-                const float w = wrow[row];
+            if (drow >= 0) {
+                float* orow = (shared ? a.shared_out : a.slot_out) + (size_t)drow * N + n0;
+                const float w = dw;
 #pragma unroll
                 for (int j = 0; j < NI; ++j) {
                     if (n0 + brow[j] >= N) continue;
@@ -759,8 +782,10 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t Y5[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y6[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y7[YS];
-    __shared__ int dst_row[BM];
-    __shared__ float wrow[BM];
+    // the tile's destinations and weights share Y7 (see gateup_dma_kernel)
+    static_assert(BM * (sizeof(int) + sizeof(float)) <= YS, "row tables fit one A array");
+    int* dst_row = reinterpret_cast<int*>(Y7);
+    float* wrow = reinterpret_cast<float*>(Y7 + BM * sizeof(int));
     int tile, ntile;
     if (!work_item<4>(tile_count(a), tile, ntile)) return;
     TileRows tr;
@@ -790,12 +815,16 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     __syncthreads();
     DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
+    static_assert(MW == 2 && WV >= 4, "cold tiles: one row block per wavefront row, four A-row copies");
     if (tr.nrows <= COLD_ROWS) {
         // wavefronts of row 0 compute the block; two of the others copy its A rows
-        static_assert(MW >= 2 && WV / MW >= 2, "a cold tile needs two wavefronts with no row block");
-        if (ai) body.template run_cold<1, 0>();
-        else if (wave / MW < 2) body.template run_cold<0, 1>();
-        else body.template run_cold<0, 0>();
+        if (ai) body.template run_cold<1, 0>(0);
+        else if (wave / MW < 2) body.template run_cold<0, 1>(wave / MW);
+        else body.template run_cold<0, 0>(0);
+    } else if (tr.nrows <= COLD_WIDE) {
+        // each wavefront row computes one block; the first four wavefronts copy the A rows
+        if (wave < 4) body.template run_cold<1, 1>(wave);
+        else body.template run_cold<1, 0>(0);
     } else {
         dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
