@@ -218,7 +218,12 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
 // additions differs from the definition's, far below the fp32 rounding of the
 // result).  K is staged raw through two LDS stages of 64 columns: the next
 // chunk's global loads are in flight while the current one is consumed, and
-// one barrier per chunk separates the stages.
+// one barrier per chunk separates the stages.  Inside a chunk the K order is
+// free (the products are exact), so each 16-column group is split so that the
+// lane with K slot lk takes columns 4 lk .. 4 lk + 3 of the group over four
+// instructions: one 8-byte (x, bf16) and two 16-byte (Wr) LDS reads feed
+// eight MFMAs.  Row pitches of 4 mod 64 words put the sixteen rows a read
+// serves on distinct banks.
 //
 // Operand layout of the 16x16x4 f64 instruction (checked on the device): lane l
 // supplies A[l % 16][l / 16] and B[l / 16][l % 16]; its four results are
@@ -232,9 +237,9 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict
                                                           int E, float* __restrict__ logits) {
     constexpr int TM = 64, TE = 64, KC = 64, NT = 512;
     constexpr int XW = AF == MOE_DT_BF16 ? KC / 2 : KC;  // 32-bit words of one staged x row
-    constexpr int XP = XW + 1, WP = KC + 1;              // row pitches in words (odd: rows on distinct banks)
-    __shared__ uint32_t xs[2][TM * XP];                  // raw x (bf16 pairs or fp32), two stages
-    __shared__ float ws[2][TE * WP];                     // raw Wr, two stages
+    constexpr int XP = XW + 4, WP = KC + 4;              // row pitches in words (4 mod 64, 16-byte rows)
+    __shared__ __attribute__((aligned(16))) uint32_t xs[2][TM * XP];  // raw x (bf16 pairs or fp32), two stages
+    __shared__ __attribute__((aligned(16))) float ws[2][TE * WP];     // raw Wr, two stages
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
     // staging items of 16 bytes: x rows hold XW / 4 of them, Wr rows KC / 4
@@ -266,25 +271,29 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict
 #pragma unroll
         for (int it = 0; it < XI; ++it) {
             const int q = tid + NT * it, r = q / (XW / 4), c = (q % (XW / 4)) * 4;
-            if (q < XQ) {
-                uint32_t* dst = &xs[stg][r * XP + c];
-                dst[0] = rx[it].x; dst[1] = rx[it].y; dst[2] = rx[it].z; dst[3] = rx[it].w;
-            }
+            if (q < XQ) *reinterpret_cast<uint4*>(&xs[stg][r * XP + c]) = rx[it];
         }
 #pragma unroll
         for (int it = 0; it < WI; ++it) {
             const int q = tid + NT * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
-            float* dst = &ws[stg][r * WP + c];
-            dst[0] = rw[it].x; dst[1] = rw[it].y; dst[2] = rw[it].z; dst[3] = rw[it].w;
+            *reinterpret_cast<float4*>(&ws[stg][r * WP + c]) = rw[it];
         }
     };
-    // x[m][k] of a stage, widened to fp64 (exact)
-    auto xval = [&](int stg, int m, int kk) -> double {
-        if (AF == MOE_DT_BF16) {
-            const uint32_t pair = xs[stg][m * XP + (kk >> 1)];
-            return (double)((kk & 1) ? bf16_hi(pair) : bf16_lo(pair));
+    // x[m][k0 .. k0 + 3] of a stage, widened to fp64 (exact)
+    auto xvals = [&](int stg, int m, int k0, double (&v)[4]) {
+        if constexpr (AF == MOE_DT_BF16) {
+            const uint2 p = *reinterpret_cast<const uint2*>(&xs[stg][m * XP + (k0 >> 1)]);
+            v[0] = (double)bf16_lo(p.x);
+            v[1] = (double)bf16_hi(p.x);
+            v[2] = (double)bf16_lo(p.y);
+            v[3] = (double)bf16_hi(p.y);
+        } else {
+            const uint4 p = *reinterpret_cast<const uint4*>(&xs[stg][m * XP + k0]);
+            v[0] = (double)__uint_as_float(p.x);
+            v[1] = (double)__uint_as_float(p.y);
+            v[2] = (double)__uint_as_float(p.z);
+            v[3] = (double)__uint_as_float(p.w);
         }
-        return (double)__uint_as_float(xs[stg][m * XP + kk]);
     };
 
     // wavefront w: tokens (w / 2) * 16 .. +15, experts (w % 2) * 32 .. +31 of the tile
@@ -302,13 +311,21 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict
         const int stg = ch & 1;
         if (ch + 1 < nch) gload((ch + 1) * KC);  // in flight during this chunk's products
 #pragma unroll
-        for (int ks = 0; ks < KC; ks += 4) {
-            const double a = xval(stg, wm + lr, ks + lk);
-            double b[2];
+        for (int kg = 0; kg < KC; kg += 16) {  // K slot lk of instruction s: column kg + 4 lk + s
+            double av[4];
+            xvals(stg, wm + lr, kg + 4 * lk, av);
+            float4 wv[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = (double)ws[stg][(wn + 16 * j + lr) * WP + ks + lk];
+            for (int j = 0; j < 2; ++j)
+                wv[j] = *reinterpret_cast<const float4*>(&ws[stg][(wn + 16 * j + lr) * WP + kg + 4 * lk]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[j], acc[j], 0, 0, 0);
+            for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float bw = s4 == 0 ? wv[j].x : s4 == 1 ? wv[j].y : s4 == 2 ? wv[j].z : wv[j].w;
+                    acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s4], (double)bw, acc[j], 0, 0, 0);
+                }
+            }
         }
         // the other stage was last read in the previous chunk, before the barrier below it
         if (ch + 1 < nch) lstore(stg ^ 1);

@@ -357,9 +357,12 @@ def test_split_entry_points(torch_cuda, orc):
                                   dict(T=2100, d=192, E=250, k=6, F=64, act="f32", w="f32",
                                        score="sqrt_softplus", scale=1.5, bias="none"),
                                   dict(T=1000, d=320, E=72, k=4, F=64, act="bf16", w="bf16"),
-                                  dict(T=1100, d=128, E=64, k=8, F=64, act="f32", w="f32")],
+                                  dict(T=1100, d=128, E=64, k=8, F=64, act="f32", w="f32"),
+                                  dict(T=4100, d=128, E=250, k=8, F=64, act="bf16", w="bf16"),
+                                  dict(T=4200, d=192, E=255, k=6, F=64, act="f32", w="f32",
+                                       score="sqrt_softplus", scale=1.5, bias="none")],
                          ids=["bf16_T4100_E192", "f32_T2100_E250", "split_bf16_T1000_E72_d320",
-                              "split_f32_T1100_E64_d128"])
+                              "split_f32_T1100_E64_d128", "bf16_T4100_E250", "f32_T4200_E255_d192"])
 def test_router_matrix_cores(torch_cuda, orc, spec):
     """Router shapes on the fp64 matrix-core kernels (at least 128 tiles of
     64 x 64, or of 16 x 32 with K split over four groups of wavefronts, five
