@@ -390,6 +390,35 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
 
 }  // namespace
 
+// Cold tiles (see k_loop_cold): the wavefronts of the rows that hold a row
+// block compute it (row mh owns block mh, so a tile of up to 32 rows is
+// computed by wavefront row 0, one of up to 64 rows by rows 0 and 1), and the
+// tile's A rows are copied in 16-row pieces (2 or 4 of them per stage) by
+// wavefronts of the next row that holds no block, or, with two wavefront
+// rows and two blocks, by the first four wavefronts.
+template <int MW, int WV, class B>
+__device__ __forceinline__ void cold_dispatch(B& body, int nrows, int wave) {
+    constexpr int NW = WV / MW;
+    const int mh = wave % MW, nh = wave / MW;
+    const int nb = nrows <= COLD_ROWS ? 1 : 2;  // row blocks
+    if constexpr (MW == 2) {
+        static_assert(WV >= 4, "four A-row copies");
+        if (nb == 1) {
+            if (mh == 0) body.template run_cold<1, 0>(0);
+            else if (nh < 2) body.template run_cold<0, 1>(nh);
+            else body.template run_cold<0, 0>(0);
+        } else {
+            if (wave < 4) body.template run_cold<1, 1>(wave);
+            else body.template run_cold<1, 0>(0);
+        }
+    } else {
+        static_assert(MW >= 3 && NW >= 4, "a wavefront row with no block copies the A rows");
+        if (mh < nb) body.template run_cold<1, 0>(0);
+        else if (mh == nb && nh < 2 * nb) body.template run_cold<0, 1>(nh);
+        else body.template run_cold<0, 0>(0);
+    }
+}
+
 // Epilogue layout.  With the weight fragment as the MFMA's first operand, the
 // 32 x 32 block's lane l holds tile row (l & 31) of its row block and the 16
 // columns 8 * (v / 4) + 4 * (l / 32) + v % 4, v = 0..15 of its column block:
@@ -601,16 +630,8 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     __syncthreads();
     GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, F, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
-    static_assert(MW == 2 && WV >= 4, "cold tiles: one row block per wavefront row, four A-row copies");
-    if (tr.nrows <= COLD_ROWS) {
-        // wavefronts of row 0 compute the block; two of the others copy its A rows
-        if (ai) body.template run_cold<1, 0>(0);
-        else if (wave / MW < 2) body.template run_cold<0, 1>(wave / MW);
-        else body.template run_cold<0, 0>(0);
-    } else if (tr.nrows <= COLD_WIDE) {
-        // each wavefront row computes one block; the first four wavefronts copy the A rows
-        if (wave < 4) body.template run_cold<1, 1>(wave);
-        else body.template run_cold<1, 0>(0);
+    if (tr.nrows <= COLD_WIDE) {
+        cold_dispatch<MW, WV>(body, tr.nrows, wave);
     } else {
         dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
@@ -815,23 +836,19 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     __syncthreads();
     DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
-    static_assert(MW == 2 && WV >= 4, "cold tiles: one row block per wavefront row, four A-row copies");
-    if (tr.nrows <= COLD_ROWS) {
-        // wavefronts of row 0 compute the block; two of the others copy its A rows
-        if (ai) body.template run_cold<1, 0>(0);
-        else if (wave / MW < 2) body.template run_cold<0, 1>(wave / MW);
-        else body.template run_cold<0, 0>(0);
-    } else if (tr.nrows <= COLD_WIDE) {
-        // each wavefront row computes one block; the first four wavefronts copy the A rows
-        if (wave < 4) body.template run_cold<1, 1>(wave);
-        else body.template run_cold<1, 0>(0);
+    if (tr.nrows <= COLD_WIDE) {
+        cold_dispatch<MW, WV>(body, tr.nrows, wave);
     } else {
         dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
 }
 
 // wavefront grid of the kernels launched: DMA_MW x (DMA_WV / DMA_MW)
-constexpr int DMA_MW = 2, DMA_WV = 8;
+#ifndef DMA_MW_V
+#define DMA_MW_V 2
+#define DMA_WV_V 8
+#endif
+constexpr int DMA_MW = DMA_MW_V, DMA_WV = DMA_WV_V;
 
 hipError_t launch_gateup_dma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
