@@ -18,11 +18,13 @@
 // written at M0 + 16 * lane), which costs no VGPRs and no LDS write
 // instructions.
 //
-// Pipeline.  K advances in stages of 32.  Four stages live in four separate
-// LDS arrays (separate objects, so the compiler can tell that reading one
-// stage does not wait for the copies into the others).  Chunk j + 4 is copied
-// into the stage of chunk j as soon as every wavefront has finished reading
-// it, so each copy has three stages of MFMA work to land.  Inside a stage the
+// Pipeline.  K advances in stages of 32.  The A rows of four stages live in
+// four separate LDS arrays (separate objects, so the compiler can tell that
+// reading one stage does not wait for the copies into the others); chunk
+// j + 4 is copied into the array of chunk j as soon as every wavefront has
+// finished reading it, so each copy has three stages of MFMA work to land.
+// The B (weight) rows go in pairs of stages (K64, whole 128-byte lines per
+// row, see k_loop) through two pair arrays, two stages to land.  Inside a stage the
 // two K16 steps alternate: while the MFMAs of one step run, the fragments of
 // the next step are read; the copies of the next chunk and the first
 // fragments of the next stage are issued between the MFMAs of the second step
@@ -39,11 +41,12 @@
 // costs about its weight stream (3.1 MB at d = 6144) instead of a full
 // 256-row product.
 //
-// LDS layout of a stage: rows of 64 bytes (32 bf16 of K), A rows first, then
-// 256 B rows.  The four 16-byte chunks of row r sit at slot c ^ f(r),
-// f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1): the sixteen lanes that a 128-bit LDS
-// read serves per cycle (sixteen consecutive rows, one chunk) hit sixteen
-// different 16-byte bank groups (measured: no bank-conflict cycles).
+// LDS layout of an A stage: rows of 64 bytes (32 bf16 of K).  The four
+// 16-byte chunks of row r sit at slot c ^ f(r), f(r) = ((r >> 1) & 3) ^
+// ((r >> 3) & 1): the sixteen lanes that a 128-bit LDS read serves per cycle
+// (sixteen consecutive rows, one chunk) hit sixteen different 16-byte bank
+// groups (measured: no bank-conflict cycles).  B pairs: rows of 128 bytes,
+// the same property with g(r) = (r >> 1) & 7 over eight chunks.
 #include "common.h"
 #include "dma_dev.h"
 #include "gemm_dev.h"
@@ -70,7 +73,7 @@ __device__ constexpr int spread(int t) {
 // so a tile with few rows leaves every SIMD the same share of matrix work.
 template <int BM_, int MW, int WV>
 struct Geo {
-    static constexpr int BM = BM_, NW = WV / MW;
+    static constexpr int BM = BM_, NW = WV / MW, NWV = WV;
     static constexpr int MI = BM / (32 * MW);      // 32-row blocks per wavefront
     static constexpr int NI = SBN / (32 * NW);    // 32-column blocks per wavefront
     static constexpr int ROWS = BM + SBN;         // LDS rows per stage
@@ -84,32 +87,51 @@ struct Geo {
 template <int MW>
 __device__ __forceinline__ int block_row(int i, int mh) { return 32 * (MW * i + mh); }
 
+// B rows of a pair of K32 stages (K64) in the hot loop: 256 rows of 128 bytes
+// in two arrays of 128 rows.  A copy of 64 lanes x 16 bytes then covers eight
+// whole 128-byte lines (eight rows) rather than sixteen half lines: the copy
+// path of a CU costs per instruction and per line, and whole lines take it
+// measurably less.  The eight 16-byte chunks of row r sit at slot
+// c ^ g(r), g(r) = (r >> 1) & 7: sixteen consecutive rows read at one chunk
+// hit sixteen different 16-byte bank groups.
+constexpr int PROW = 2 * SROW;  // LDS bytes per row of a B pair
+__device__ __forceinline__ int pair_swz(int r) { return (r >> 1) & 7; }
+
 // One tile's operand sources (copy lane addresses, fragment offsets) and its
 // accumulators, for a wavefront that computes AI of its MI row blocks (the
 // blocks that hold rows of the tile; AI = 0: copies only) and issues NCAA of
-// the NCA A-row copies of a stage (those that reach rows of the tile).
+// the NCA A-row copies of a stage (those that reach rows of the tile), and
+// NCB B-row copies per pair of stages.
 template <class GEO, int AI, int NCAA>
 struct Gemm {
-    static constexpr int NI = GEO::NI, NCB = GEO::NCP - GEO::NCA;
-    static constexpr int NCPA = NCAA + NCB;           // copies issued per stage
+    static constexpr int NI = GEO::NI, NCA_ = NCAA, NCAA_COPIES = NCAA;
+    static constexpr int NCB = SBN / 8 / GEO::NWV;    // B copies per wavefront per pair (eight rows each)
+    static_assert(NCB * 8 * GEO::NWV == SBN && NCB % 2 == 0, "B copies fill both halves of a pair");
+    static_assert(NI == 2 && GEO::NW == 4, "a wavefront's two B blocks lie in the two halves of a pair");
+    static constexpr int NCPA = NCAA + NCB;           // A copies, then B copies
     static constexpr int NF = AI > 0 ? AI + NI : 0;   // fragments per K16 step
     static constexpr int NM = AI * NI;                // MFMAs per K16 step
     static constexpr int AIS = AI > 0 ? AI : 1, NFS = NF > 0 ? NF : 1;
     const uint8_t* src[NCPA];  // per-lane source of each copy at K = 0
-    int dst[NCPA];             // wave-uniform LDS byte offset of each copy in a stage
-    int fo[NFS];               // per-lane LDS byte offset of each fragment (K16 step 0)
+    int dst[NCPA];             // wave-uniform LDS byte offset (A: in an A array; B: in its half of a pair)
+    int fo[NFS];               // per-lane LDS byte offset of each fragment (first K16 step)
     f32x16_t acc[AIS][NI];
 
-    // A rows of a stage live in one LDS array, its B rows in another: the
-    // first NCAA copies and the A fragments go to SA, the rest to SB (dst and
-    // fo are offsets inside their own array)
-    __device__ __forceinline__ void copy(uint8_t* SA, uint8_t* SB, int ci, size_t kb) const {
-        copy16(src[ci] + kb, (ci < NCAA ? SA : SB) + dst[ci]);
+    // A copy ci (< NCAA) of the chunk at byte offset kb into the A array SA
+    __device__ __forceinline__ void copy_a(uint8_t* SA, int ci, size_t kb) const { copy16(src[ci] + kb, SA + dst[ci]); }
+    // B copy ci (>= NCAA) of the pair at byte offset pb: the first NCB / 2
+    // fill rows 0..127 (Blo), the rest rows 128..255 (Bhi)
+    __device__ __forceinline__ void copy_b(uint8_t* Blo, uint8_t* Bhi, int ci, size_t pb) const {
+        copy16(src[ci] + pb, (ci - NCAA < NCB / 2 ? Blo : Bhi) + dst[ci]);
     }
-    // step 1 reads logical chunk c + 2 of the same row: slot ^ 2
-    __device__ __forceinline__ bf16x8_t frag(const uint8_t* SA, const uint8_t* SB, int fi, int ks) const {
-        const uint8_t* S = (fi == 0 || fi > NI) ? SA : SB;
-        return *reinterpret_cast<const bf16x8_t*>(S + (ks ? (fo[fi] ^ 32) : fo[fi]));
+    // fragment fi: A (fi = 0 or > NI) at K16 step ks of its stage (step 1
+    // reads logical chunk c + 2: slot ^ 2); B block j = fi - 1 at K16 step sp
+    // (0..3) of its pair (logical chunk c + 2 sp: slot ^ 2 sp); block j < NI/2
+    // lies in Blo, the other in Bhi
+    __device__ __forceinline__ bf16x8_t frag(const uint8_t* SA, const uint8_t* Blo, const uint8_t* Bhi, int fi,
+                                             int ks, int sp) const {
+        if (fi == 0 || fi > NI) return *reinterpret_cast<const bf16x8_t*>(SA + (ks ? (fo[fi] ^ 32) : fo[fi]));
+        return *reinterpret_cast<const bf16x8_t*>((fi - 1 < NI / 2 ? Blo : Bhi) + (fo[fi] ^ (32 * sp)));
     }
     // MFMA t of a K16 step: block (i, j) = (t / NI, t % NI); fragments are
     // ordered A0, B0..B(NI-1), A1.. so that the first MFMAs wait least.  The
@@ -123,76 +145,117 @@ struct Gemm {
     }
 };
 
-// The K loop shared by both kernels.  nst = K / 32 stages; chunk c of the
-// operands is at byte offset c * 64 of every row.
+// The K loop shared by both kernels.  nst = K / 32 stages (even: K is a
+// multiple of 64).  A rows: chunk c (K32) at byte offset c * 64 of a row, in
+// four A arrays, one per stage; chunk j + 4 is copied into the array of chunk
+// j as soon as every wavefront has read it (three stages to land).  B rows:
+// pair p (K64) at byte offset p * 128 of a row, in two pair arrays; pair
+// p + 2 is copied into the arrays of pair p at its second stage's barrier,
+// after every wavefront has read it (two stages to land).  Each stage has one
+// barrier, between its two K16 steps: by then every fragment of the stage has
+// been read (the second step's during the first), and the next stage's
+// operands must have landed (the next stage's first fragments are read during
+// the second step).  Vector-memory counts complete in issue order; a stage
+// issues its A copy first, then (odd stages) its B pair, so at the barrier of
+// an odd stage only the last even stage's A copy may still be in flight, and
+// at an even stage the last odd stage's A copy and B pair and the A copy
+// before.
 template <class GM>
-__device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* A0, uint8_t* B0, uint8_t* A1, uint8_t* B1,
-                                       uint8_t* A2, uint8_t* B2, uint8_t* A3, uint8_t* B3) {
-    constexpr int NCP = GM::NCPA, NF = GM::NF, NM = GM::NM, NFS = GM::NFS;
+__device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* A0, uint8_t* A1, uint8_t* A2, uint8_t* A3,
+                                       uint8_t* B0lo, uint8_t* B0hi, uint8_t* B1lo, uint8_t* B1hi) {
+    constexpr int NCAA = GM::NCA_, NCB = GM::NCB, NF = GM::NF, NM = GM::NM, NFS = GM::NFS;
     bf16x8_t P[NFS], Q[NFS];
-    const int last = nst - 1;
+    const int last = nst - 1, lastp = nst / 2 - 1;
     auto kb = [&](int c) { return (size_t)(c < last ? c : last) * SROW; };
+    auto pb = [&](int p) { return (size_t)(p < lastp ? p : lastp) * PROW; };
+    auto arr = [&](auto kc) -> uint8_t* {
+        constexpr int K = decltype(kc)::value % 4;
+        if constexpr (K == 0) return A0;
+        else if constexpr (K == 1) return A1;
+        else if constexpr (K == 2) return A2;
+        else return A3;
+    };
     // Fragment reads go with the first three quarters of a step's MFMAs, so
     // they have landed when the step ends; the copies go with the last three
     // quarters.
     constexpr int RD = (NM * 3 + 3) / 4, CP = NM / 4;
 
-    // one stage: (SA, SB) holds chunk j, (NA, NB) is the stage of chunk j + 1
-    auto stage = [&](uint8_t* SA, uint8_t* SB, uint8_t* NA, uint8_t* NB, int j) {
+    // stage J of four (chunk j): A array J, B pair array J / 2, K32 half J & 1
+    auto stage = [&](auto kc, int j) {
+        constexpr int J = decltype(kc)::value;
+        constexpr bool ODD = (J & 1) != 0;
+        constexpr int NCS = NCAA + (ODD ? NCB : 0);  // copies issued this stage
+        uint8_t* SA = arr(kc);
+        uint8_t* NA = arr(ic<J + 1>());
+        uint8_t* Blo = J < 2 ? B0lo : B1lo;
+        uint8_t* Bhi = J < 2 ? B0hi : B1hi;
+        uint8_t* NBlo = (J + 1) % 4 < 2 ? B0lo : B1lo;
+        uint8_t* NBhi = (J + 1) % 4 < 2 ? B0hi : B1hi;
         // step 0 MFMAs (fragments P) with step 1's fragment reads (Q)
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
             g.mfma(P, t);
 #pragma unroll
-            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q) Q[q] = g.frag(SA, SB, q, 1);
+            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q)
+                Q[q] = g.frag(SA, Blo, Bhi, q, 1, 2 * (J & 1) + 1);
             pin();
         }
-        // every read of S done, chunk j + 1 landed (two later chunks may be in flight)
+        // every read of this stage done; chunk j + 1 (A and B) landed
         wait_lgkm0();
-        wait_vm<2 * NCP>();
+        wait_vm<ODD ? NCAA : 2 * NCAA + NCB>();
         barrier_nofence();
-        // step 1 MFMAs (Q) with the copy of chunk j + 4 into S and the first
+        // step 1 MFMAs (Q) with the copies (A chunk j + 4 into SA; odd
+        // stages: B pair (j + 3) / 2 into this pair's arrays) and the first
         // fragment reads of the next stage (P)
-        const size_t k4 = kb(j + 4);
+        const size_t k4 = kb(j + 4), p2 = pb((j + 3) / 2);
+        auto issue = [&](int q) {
+            if (q < NCAA) g.copy_a(SA, q, k4);
+            else g.copy_b(Blo, Bhi, q, p2);
+        };
         if constexpr (NM == 0) {
 #pragma unroll
-            for (int q = 0; q < NCP; ++q) g.copy(SA, SB, q, k4);
+            for (int q = 0; q < NCS; ++q) issue(q);
         }
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
             g.mfma(Q, t);
 #pragma unroll
-            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q) P[q] = g.frag(NA, NB, q, 0);
+            for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q)
+                P[q] = g.frag(NA, NBlo, NBhi, q, 0, 2 * ((J + 1) & 1));
 #pragma unroll
-            for (int q = spread<NCP, CP, NM>(t); q < spread<NCP, CP, NM>(t + 1); ++q) g.copy(SA, SB, q, k4);
+            for (int q = spread<NCS, CP, NM>(t); q < spread<NCS, CP, NM>(t + 1); ++q) issue(q);
             pin();
         }
     };
 
-    // prologue: chunks 0..3 into stages 0..3, wait for chunk 0
+    // prologue, in the steady state's issue order: A chunks 0, 1, B pair 0,
+    // A chunks 2, 3, B pair 1; then wait for chunk 0 (A chunk 0, B pair 0)
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(A0, B0, q, kb(0));
+    for (int q = 0; q < NCAA; ++q) g.copy_a(A0, q, kb(0));
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(A1, B1, q, kb(1));
+    for (int q = 0; q < NCAA; ++q) g.copy_a(A1, q, kb(1));
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(A2, B2, q, kb(2));
+    for (int q = NCAA; q < NCAA + NCB; ++q) g.copy_b(B0lo, B0hi, q, pb(0));
 #pragma unroll
-    for (int q = 0; q < NCP; ++q) g.copy(A3, B3, q, kb(3));
-    wait_vm<3 * NCP>();
+    for (int q = 0; q < NCAA; ++q) g.copy_a(A2, q, kb(2));
+#pragma unroll
+    for (int q = 0; q < NCAA; ++q) g.copy_a(A3, q, kb(3));
+#pragma unroll
+    for (int q = NCAA; q < NCAA + NCB; ++q) g.copy_b(B1lo, B1hi, q, pb(1));
+    wait_vm<2 * NCAA + NCB>();
     barrier_nofence();
 #pragma unroll
-    for (int q = 0; q < NF; ++q) P[q] = g.frag(A0, B0, q, 0);
+    for (int q = 0; q < NF; ++q) P[q] = g.frag(A0, B0lo, B0hi, q, 0, 0);
 
     int j = 0;
     for (; j + 4 <= nst; j += 4) {
-        stage(A0, B0, A1, B1, j);
-        stage(A1, B1, A2, B2, j + 1);
-        stage(A2, B2, A3, B3, j + 2);
-        stage(A3, B3, A0, B0, j + 3);
+        stage(ic<0>(), j);
+        stage(ic<1>(), j + 1);
+        stage(ic<2>(), j + 2);
+        stage(ic<3>(), j + 3);
     }
-    if (j < nst) stage(A0, B0, A1, B1, j);
-    if (j + 1 < nst) stage(A1, B1, A2, B2, j + 1);
-    if (j + 2 < nst) stage(A2, B2, A3, B3, j + 2);
+    if (j < nst) stage(ic<0>(), j);  // (nst is even: zero or two stages left)
+    if (j + 1 < nst) stage(ic<1>(), j + 1);
     // no copy may still be writing LDS when the workgroup ends
     wait_vm<0>();
 }
@@ -200,13 +263,10 @@ __device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* A0, uint8_t* B0,
 // Element offset of a copy lane's 16-byte chunk within a row (bf16).
 __device__ __forceinline__ int copy_col(int lane) { return copy_chunk(lane) * 8; }
 
-// Active copy index qa (0 .. NCPA-1) -> copy index of the full stage: the
-// first NCAA A-row copies, then every B-row copy.
-template <class GM, class GEO>
-__device__ __forceinline__ int copy_index(int qa) { return qa < GM::NCPA - GM::NCB ? qa : qa - (GM::NCPA - GM::NCB) + GEO::NCA; }
 
 // Per-lane fragment offsets: wavefront (mh, nh) reads A rows
-// block_row(i, mh) + (lane & 31) and B rows brow[j] + (lane & 31).
+// block_row(i, mh) + (lane & 31) and B rows brow[j] + (lane & 31) (B block j
+// < NI/2 lies in rows 0..127 of a pair, the other in rows 128..255).
 template <class GEO, class GM, int MW>
 __device__ __forceinline__ void frag_offsets(GM& g, int mh, const int (&brow)[GEO::NI], int lane) {
     if constexpr (GM::NF > 0) {
@@ -215,8 +275,10 @@ __device__ __forceinline__ void frag_offsets(GM& g, int mh, const int (&brow)[GE
         const int base = r * SROW + slot0 * 16;
 #pragma unroll
         for (int i = 0; i < GM::AIS; ++i) g.fo[GM::fa_idx(i)] = block_row<MW>(i, mh) * SROW + base;
+        // B: row brow + r of a pair (in its half), logical chunk lane / 32
+        const int bslot = (lane >> 5) ^ pair_swz(r);
 #pragma unroll
-        for (int j = 0; j < GEO::NI; ++j) g.fo[GM::fb_idx(j)] = brow[j] * SROW + base;
+        for (int j = 0; j < GEO::NI; ++j) g.fo[GM::fb_idx(j)] = ((brow[j] & 127) + r) * PROW + bslot * 16;
     }
 }
 
@@ -467,21 +529,21 @@ struct GateUpTile {
         const uint16_t* ubase = static_cast<const uint16_t*>(Wu.q) + ((size_t)ge * F + n0) * K;
         const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
 #pragma unroll
-        for (int qa = 0; qa < G::NCPA; ++qa) {
-            const int q = copy_index<G, GEO>(qa);
-            g.dst[qa] = (q * WV + wave) * 1024 - (q < GEO::NCA ? 0 : BM * SROW);
-            const int row = copy_row(q, WV, wave, lane);
-            if (q < GEO::NCA) {
-                // rows past the tile read token 0; their results are never stored
-                const int t = src_row[row];
-                g.src[qa] = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
-            } else {
-                const int br = row - BM;  // 0..255: gate rows, then up rows
-                const int n = br & 127;
-                const int rr = n0 + n < F ? n : 0;  // columns past F read row 0 and are never stored
-                const uint16_t* b = br < 128 ? gbase : ubase;
-                g.src[qa] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K + cch);
-            }
+        for (int qa = 0; qa < G::NCAA_COPIES; ++qa) {  // A: 16 rows x 64 bytes per copy
+            g.dst[qa] = (qa * WV + wave) * 1024;
+            // rows past the tile read token 0; their results are never stored
+            const int t = src_row[copy_row(qa, WV, wave, lane)];
+            g.src[qa] = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
+        }
+#pragma unroll
+        for (int b = 0; b < G::NCB; ++b) {  // B: 8 rows x 128 bytes per copy, rows 0..255 = gate, then up
+            const int r0 = (b * WV + wave) * 8, br = r0 + (lane >> 3);
+            g.dst[G::NCAA_COPIES + b] = (r0 & 127) * PROW;
+            const int n = br & 127;
+            const int rr = n0 + n < F ? n : 0;  // columns past F read row 0 and are never stored
+            const uint16_t* bb = br < 128 ? gbase : ubase;
+            g.src[G::NCAA_COPIES + b] =
+                reinterpret_cast<const uint8_t*>(bb + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
         }
         // wavefront (mh, nh): gate columns nh * 128/NW + 32 j' and the same up
         // columns (blocks j < NI/2 are gate, j >= NI/2 up)
@@ -495,7 +557,7 @@ struct GateUpTile {
 #pragma unroll
             for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
 
-        k_loop(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
+        k_loop(g, K / SK, X0, X2, X4, X6, X1, X3, X5, X7);
 
         // epilogue: lane holds row (lane & 31) of each row block (see run_col)
         uint16_t* h = static_cast<uint16_t*>(a.h);
@@ -665,30 +727,33 @@ struct DownTile {
         const uint16_t* dbase = static_cast<const uint16_t*>(D.q) + ((size_t)ge * N + n0) * K;
         const uint16_t* hbase = static_cast<const uint16_t*>(a.h) + (size_t)tr.rbeg * a.ldh;
 #pragma unroll
-        for (int qa = 0; qa < G::NCPA; ++qa) {
-            const int q = copy_index<G, GEO>(qa);
-            g.dst[qa] = (q * WV + wave) * 1024 - (q < GEO::NCA ? 0 : BM * SROW);
-            const int row = copy_row(q, WV, wave, lane);
-            if (q < GEO::NCA) {
-                const int rr = row < tr.nrows ? row : 0;  // rows past the tile: never stored
-                g.src[qa] = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
-            } else {
-                const int br = row - BM;
-                const int rr = n0 + br < N ? br : 0;
-                g.src[qa] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K + cch);
-            }
+        for (int qa = 0; qa < G::NCAA_COPIES; ++qa) {  // A: 16 rows x 64 bytes per copy
+            g.dst[qa] = (qa * WV + wave) * 1024;
+            const int row = copy_row(qa, WV, wave, lane);
+            const int rr = row < tr.nrows ? row : 0;  // rows past the tile: never stored
+            g.src[qa] = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
         }
+#pragma unroll
+        for (int b = 0; b < G::NCB; ++b) {  // B: 8 rows x 128 bytes per copy
+            const int r0 = (b * WV + wave) * 8, br = r0 + (lane >> 3);
+            g.dst[G::NCAA_COPIES + b] = (r0 & 127) * PROW;
+            const int rr = n0 + br < N ? br : 0;
+            g.src[G::NCAA_COPIES + b] =
+                reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
+        }
+        // wavefront (mh, nh): output columns nh * 32 + 128 j (one block in
+        // each half of a B pair)
         const int mh = wave % MW, nh = wave / MW;
         int brow[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) brow[j] = nh * (SBN / NW) + 32 * j;
+        for (int j = 0; j < NI; ++j) brow[j] = 128 * j + nh * (128 / NW);
         frag_offsets<GEO, G, MW>(g, mh, brow, lane);
 #pragma unroll
         for (int i = 0; i < G::AIS; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
 
-        k_loop(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7);
+        k_loop(g, K / SK, X0, X2, X4, X6, X1, X3, X5, X7);
 
         // epilogue: lane holds row (lane & 31) of each row block (see run_col)
         float* out = shared ? a.shared_out : a.slot_out;
