@@ -340,14 +340,15 @@ struct GemmCold {
     static_assert(AI == 0 || AI == 1, "a cold tile gives a wavefront at most one row block");
     static_assert(NA == 0 || NA == 1, "at most one A copy per wavefront and stage");
     static constexpr int BLOCKS = AI, ACOPIES = NA;
-    static constexpr int NI = GEO::NI, NCB = GEO::NCP - GEO::NCA;  // B-row copies per wavefront per stage
-    static constexpr int NCP = NA + NCB;                           // copies per wavefront per stage
+    static constexpr int NI = GEO::NI, NCB = SBN / 8 / GEO::NWV;  // B-row copies per wavefront per pair (8 rows)
+    static_assert(NI == 2 && GEO::NW == 4 && NCB % 2 == 0, "a wavefront's two B blocks lie in the two halves of a pair");
+    static constexpr int NCPP = 2 * NA + NCB;                      // copies per wavefront per pair of stages
     const uint8_t* asrc;   // NA: this lane's A-row copy source at K = 0
     int adst;              // NA: wave-uniform offset of the copy in an A array
     int fa;                // AI: A fragment offset in an A array (K16 step 0)
     const uint8_t* src[NCB];
-    int dst[NCB];          // offsets in a B array
-    int fo[NI];            // B fragment offsets (K16 step 0)
+    int dst[NCB];          // offsets in a half of a B pair
+    int fo[NI];            // B fragment offsets (first K16 step of a pair)
     f32x16_t acc[NI];
 };
 
@@ -366,10 +367,11 @@ __device__ __forceinline__ uint8_t* pick8(uint8_t* a0, uint8_t* a1, uint8_t* a2,
 }
 
 // The K loop of a cold tile: nst = K / 32 stages in eight slots; slot s holds
-// the B rows (X array s) and the A rows (Y array s) of chunk c = s mod 8.
-// Chunks are fetched in pairs (2m, 2m + 1): the two 64-byte halves of every
-// 128-byte line of a row go out back to back, so the memory sees whole lines
-// rather than halves a stage apart.  At an even stage j: the pair (j, j + 1)
+// the A rows (Y array s) of chunk c = s mod 8, and slots 2m, 2m + 1 hold the
+// B rows of that pair of chunks (K64: 128-byte rows, rows 0..127 in X array
+// 2m and 128..255 in X array 2m + 1, laid out as the hot loop's B pairs).
+// Chunks are fetched in pairs (2m, 2m + 1): each B copy covers eight whole
+// 128-byte lines (see the hot loop's B pairs).  At an even stage j: the pair (j, j + 1)
 // has landed (the pairs of chunks j + 2 .. j + 5 may still be in flight) and
 // every wavefront has finished reading slots j - 2 and j - 1, which then
 // receive the pair (j + 6, j + 7); odd stages only compute.
@@ -378,37 +380,36 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
                                             uint8_t* X4, uint8_t* X5, uint8_t* X6, uint8_t* X7, uint8_t* Y0,
                                             uint8_t* Y1, uint8_t* Y2, uint8_t* Y3, uint8_t* Y4, uint8_t* Y5,
                                             uint8_t* Y6, uint8_t* Y7) {
-    constexpr int NCP = GC::NCP, NI = GC::NI, NCB = GC::NCB;
+    constexpr int NCPP = GC::NCPP, NI = GC::NI, NCB = GC::NCB;
     const int last = nst - 1;
     auto kb = [&](int c) { return (size_t)(c < last ? c : last) * SROW; };
+    auto pb = [&](int c) { return (size_t)((c < last ? c : last) / 2) * PROW; };
     auto slot = [&](auto kc) { return pick8<decltype(kc)::value>(X0, X1, X2, X3, X4, X5, X6, X7); };
     auto aslot = [&](auto kc) { return pick8<decltype(kc)::value>(Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7); };
-    // chunks c, c + 1 into slots K, K + 1 (K even): A rows, then the B rows,
-    // each row's two halves back to back
+    // chunks c, c + 1 into slots K, K + 1 (K even, c even): A rows, then the
+    // B pair (whole 128-byte lines)
     auto issue_pair = [&](auto kc, int c) {
         constexpr int K = decltype(kc)::value;
         static_assert(K % 2 == 0, "pairs start at even slots");
-        const size_t o0 = kb(c), o1 = kb(c + 1);
         if constexpr (GC::ACOPIES == 1) {
-            copy16(g.asrc + o0, aslot(kc) + g.adst);
-            copy16(g.asrc + o1, aslot(ic<K + 1>()) + g.adst);
+            copy16(g.asrc + kb(c), aslot(kc) + g.adst);
+            copy16(g.asrc + kb(c + 1), aslot(ic<K + 1>()) + g.adst);
         }
+        const size_t p0 = pb(c);
 #pragma unroll
-        for (int q = 0; q < NCB; ++q) {
-            copy16(g.src[q] + o0, slot(kc) + g.dst[q]);
-            copy16(g.src[q] + o1, slot(ic<K + 1>()) + g.dst[q]);
-        }
+        for (int q = 0; q < NCB; ++q) copy16(g.src[q] + p0, (q < NCB / 2 ? slot(kc) : slot(ic<K + 1>())) + g.dst[q]);
     };
     auto stage = [&](auto kc, int j) {
         constexpr int K = decltype(kc)::value;
         if constexpr (K % 2 == 0) {
             wait_lgkm0();
-            wait_vm<4 * NCP>();
+            wait_vm<2 * NCPP>();
             barrier_nofence();
             issue_pair(ic<(K + 6) % 8>(), j + 6);
         }
         if constexpr (GC::BLOCKS == 1) {
-            const uint8_t* S = slot(kc);
+            const uint8_t* Blo = slot(ic<K & ~1>());
+            const uint8_t* Bhi = slot(ic<K | 1>());
             const uint8_t* SA = aslot(kc);
             bf16x8_t af[2], b[2][NI];
 #pragma unroll
@@ -416,7 +417,8 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
                 af[s] = *reinterpret_cast<const bf16x8_t*>(SA + (s ? (g.fa ^ 32) : g.fa));
 #pragma unroll
                 for (int jj = 0; jj < NI; ++jj)
-                    b[s][jj] = *reinterpret_cast<const bf16x8_t*>(S + (s ? (g.fo[jj] ^ 32) : g.fo[jj]));
+                    b[s][jj] = *reinterpret_cast<const bf16x8_t*>((jj < NI / 2 ? Blo : Bhi) +
+                                                                  (g.fo[jj] ^ (32 * (2 * (K & 1) + s))));
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -592,14 +594,13 @@ struct GateUpTile {
         const uint16_t* ubase = static_cast<const uint16_t*>(Wu.q) + ((size_t)ge * F + n0) * K;
         const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
 #pragma unroll
-        for (int qb = 0; qb < G::NCB; ++qb) {
-            const int q = GEO::NCA + qb;
-            g.dst[qb] = (q * WV + wave) * 1024 - BM * SROW;
-            const int br = copy_row(q, WV, wave, lane) - BM;  // 0..255: gate rows, then up rows
+        for (int qb = 0; qb < G::NCB; ++qb) {  // B: 8 rows x 128 bytes per copy, rows 0..255 = gate, then up
+            const int r0 = (qb * WV + wave) * 8, br = r0 + (lane >> 3);
+            g.dst[qb] = (r0 & 127) * PROW;
             const int n = br & 127;
             const int rr = n0 + n < F ? n : 0;  // columns past F read row 0 and are never stored
             const uint16_t* b = br < 128 ? gbase : ubase;
-            g.src[qb] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K + cch);
+            g.src[qb] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
         }
         const int mh = wave % MW, nh = wave / MW;
         if constexpr (NA == 1) {  // rows past the tile read token 0
@@ -614,9 +615,10 @@ struct GateUpTile {
         // lane / 32 (K16 step 0)
         const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
         g.fa = (block_row<MW>(0, mh) + (lane & 31)) * SROW + slot0 * 16;
+        const int bslot = (lane >> 5) ^ pair_swz(lane & 31);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
+            g.fo[j] = ((brow[j] & 127) + (lane & 31)) * PROW + bslot * 16;
             g.acc[j] = f32x16_t{};
         }
 
@@ -791,12 +793,11 @@ struct DownTile {
         const uint16_t* dbase = static_cast<const uint16_t*>(D.q) + ((size_t)ge * N + n0) * K;
         const uint16_t* hbase = static_cast<const uint16_t*>(a.h) + (size_t)tr.rbeg * a.ldh;
 #pragma unroll
-        for (int qb = 0; qb < G::NCB; ++qb) {
-            const int q = GEO::NCA + qb;
-            g.dst[qb] = (q * WV + wave) * 1024 - BM * SROW;
-            const int br = copy_row(q, WV, wave, lane) - BM;
+        for (int qb = 0; qb < G::NCB; ++qb) {  // B: 8 rows x 128 bytes per copy
+            const int r0 = (qb * WV + wave) * 8, br = r0 + (lane >> 3);
+            g.dst[qb] = (r0 & 127) * PROW;
             const int rr = n0 + br < N ? br : 0;
-            g.src[qb] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K + cch);
+            g.src[qb] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
         }
         const int mh = wave % MW, nh = wave / MW;
         if constexpr (NA == 1) {  // rows past the tile read row 0 (never stored)
@@ -812,14 +813,15 @@ struct DownTile {
         const float dw = AI == 1 && orow_i < tr.nrows ? wrow[orow_i] : 0.0f;
         int brow[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) brow[j] = nh * (SBN / NW) + 32 * j;
+        for (int j = 0; j < NI; ++j) brow[j] = 128 * j + nh * (128 / NW);
         // fragment lanes: row lane & 31 (of block mh for A), logical chunk
         // lane / 32 (K16 step 0)
         const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
         g.fa = (block_row<MW>(0, mh) + (lane & 31)) * SROW + slot0 * 16;
+        const int bslot = (lane >> 5) ^ pair_swz(lane & 31);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            g.fo[j] = (brow[j] + (lane & 31)) * SROW + slot0 * 16;
+            g.fo[j] = ((brow[j] & 127) + (lane & 31)) * PROW + bslot * 16;
             g.acc[j] = f32x16_t{};
         }
 
