@@ -17,8 +17,8 @@
 //
 // Pass: at most 32 rows (a 64-row tile of the list takes two) x 256 weight rows.  Gate/up: 128 gate columns and the
 // same 128 up columns; wavefront w owns gate columns 16w .. 16w + 15 and the
-// same up columns as one 32 x 32 MFMA block (B rows: those 16 gate rows, then
-// those 16 up rows).  Down: wavefront w owns output columns 32w .. 32w + 31.
+// same up columns as one 32 x 32 MFMA block (B rows 32w .. 32w + 31: those
+// 16 gate rows, then those 16 up rows).  Down: wavefront w owns output columns 32w .. 32w + 31.
 // A (the tile's bf16 rows of x or h, 128 bytes per row and stage) is copied
 // into LDS beside the weight rows by wavefronts 0-3, one 1 KB copy each, and
 // read by all eight.
@@ -41,6 +41,7 @@ constexpr int QSK = 64;                  // K per stage: 64 int8 = 64 bytes of e
 constexpr int QBN = 256;                 // weight rows per tile
 constexpr int QXS = QBN * QSK;           // bytes of one stage's weight rows (16 KB)
 constexpr int QNCB = QXS / (1024 * QWV); // 1 KB weight copies per wavefront per stage (2)
+constexpr int QNCP = 2 * QNCB;           // ... per pair of stages (8 rows x 128 bytes each)
 constexpr int QROWS = 32;                // rows of a tile these kernels take
 constexpr int QAS = QROWS * QSK * 2;     // bytes of one stage's A rows (4 KB: 32 rows x 64 bf16)
 constexpr int QAW = QAS / 1024;          // wavefronts that copy A rows (one 1 KB copy each)
@@ -66,11 +67,12 @@ __device__ __forceinline__ bf16x8_t widen8(uint32_t lo, uint32_t hi) {
 struct QTile {
     const uint8_t* asrc;     // A bytes this copy lane fetches at K = 0 (wavefronts < QAW)
     int adst;                // wave-uniform offset of that copy in an A stage
-    const uint8_t* src[QNCB];// weight-row bytes each copy lane fetches at K = 0
-    int dst[QNCB];           // wave-uniform offset of each copy in a stage
+    const uint8_t* src[QNCP];// weight-row bytes each copy lane fetches at K = 0
+    int dst[QNCP];           // wave-uniform offset of each copy in its half of a pair
     const uint4* scp;        // the lane's weight row's block scales, eight (four stages) per 16 bytes
-    int fo;                  // LDS offset of the lane's weight fragment (row, half h) in a stage
+    int fo;                  // LDS offset of the lane's weight fragment (row, half h) in its half of a pair
     int fsw;                 // that row's chunk swizzle
+    bool fhi;                // the lane's weight row lies in rows 128..255 of a pair
     int ao;                  // LDS offset of the lane's A row (lane & 31) in an A stage
     f32x16_t acc;
 };
@@ -81,13 +83,20 @@ struct QTile {
 __device__ __forceinline__ int a_copy_row(int q, int lane) { return 8 * q + (lane >> 3); }
 __device__ __forceinline__ int a_copy_chunk(int lane) { return (lane & 7) ^ ((lane >> 3) & 7); }
 
+// Weight rows of a pair of stages (K128: 128 bytes of each row, whole cache
+// lines) in two arrays of 128 rows: a copy of 64 lanes x 16 bytes covers
+// eight whole lines rather than sixteen half lines, which the copy path of a
+// CU takes measurably faster.  The eight 16-byte chunks of row r sit at slot
+// c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int q8_pair_swz(int r) { return (r >> 1) & 7; }
+
 // The K loop: nst = K / 64 stages (a multiple of 4) in eight slots; slot s
-// holds the weight rows (X) and A rows (Y) of chunk c = s mod 8.  The lane's
+// holds the A rows (Y) of chunk c = s mod 8, slots 2m, 2m + 1 the weight rows
+// of that pair of chunks (rows 0..127 in X[2m], 128..255 in X[2m + 1]).  The lane's
 // block scales come 16 bytes (four chunks) per load: sc[0] serves slots 0-3
 // and is reloaded at stage 4 for the next round, sc[1] serves slots 4-7 and
 // is reloaded at stage 0 of its round; each load goes out after every use of
-// the values it replaces.  Chunks are fetched in pairs (2m, 2m + 1): the two
-// 64-byte halves of every 128-byte line of a weight row go out back to back.
+// the values it replaces.  Chunks are fetched in pairs (2m, 2m + 1).
 // At an even stage j the pair (j, j + 1) has landed (the pairs of chunks
 // j + 2 .. j + 5 may still be in flight) and every wavefront has finished
 // reading slots j - 2 and j - 1, which then receive the pair (j + 6, j + 7).
@@ -107,11 +116,9 @@ __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const 
             copy16(g.asrc + (size_t)c0 * 128, Y[K] + g.adst);
             copy16(g.asrc + (size_t)c1 * 128, Y[K + 1] + g.adst);
         }
+        const size_t p0 = (size_t)(c0 & ~1) * QSK;  // the pair's 128 bytes of each weight row
 #pragma unroll
-        for (int q = 0; q < QNCB; ++q) {
-            copy16(g.src[q] + (size_t)c0 * QSK, X[K] + g.dst[q]);
-            copy16(g.src[q] + (size_t)c1 * QSK, X[K + 1] + g.dst[q]);
-        }
+        for (int q = 0; q < QNCP; ++q) copy16(g.src[q] + p0, (q < QNCP / 2 ? X[K] : X[K + 1]) + g.dst[q]);
     };
     auto stage = [&](auto kk, int j) {
         constexpr int K = decltype(kk)::value;
@@ -126,13 +133,13 @@ __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const 
             if constexpr (K == 4) sc[0] = g.scp[kc(j + 4) >> 2];
             issue_pair(ic<(K + 6) % 8>(), j + 6);
         }
-        const uint8_t* S = X[K];
+        const uint8_t* S = g.fhi ? X[K | 1] : X[K & ~1];
         const uint8_t* A = Y[K];
         uint2 wq[4];
         bf16x8_t fa[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            wq[s] = *reinterpret_cast<const uint2*>(S + g.fo + ((s ^ g.fsw) << 4));
+            wq[s] = *reinterpret_cast<const uint2*>(S + g.fo + (((4 * (K & 1) + s) ^ g.fsw) << 4));
             fa[s] = *reinterpret_cast<const bf16x8_t*>(A + g.ao + (((2 * s + (threadIdx.x >> 5 & 1)) ^ (threadIdx.x & 7)) << 4));
         }
 #pragma unroll
@@ -174,26 +181,24 @@ __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const 
     wait_vm<0>();
 }
 
-// Copy and fragment set-up shared by both kernels.  wrow(sr) is the global
-// address of stage row sr's weight bytes at K = 0, srow(br) the scale row of
-// fragment row br, arow(r) the global address of A row r (r < 32) at K = 0.
-template <class WR, class SR, class AR>
-__device__ __forceinline__ void q8_dma_setup(QTile& g, int wave, int lane, int br, WR wrow, SR srow, AR arow) {
+// Copy and fragment set-up shared by both kernels (the passes fill in the
+// copy sources g.src, g.asrc and the scale row g.scp): br is the lane's
+// fragment row (0..255) in a pair of stages.
+__device__ __forceinline__ void q8_dma_setup(QTile& g, int wave, int lane, int br) {
 #pragma unroll
-    for (int q = 0; q < QNCB; ++q) {
-        const int sr = copy_row(q, QWV, wave, lane);
-        g.src[q] = wrow(sr) + copy_chunk(lane) * 16;
-        g.dst[q] = (q * QWV + wave) * 1024;
-    }
-    const int aq = wave < QAW ? wave : 0;
-    g.asrc = arow(a_copy_row(aq, lane)) + a_copy_chunk(lane) * 16;
-    g.adst = aq * 1024;
-    g.fsw = slot_swz(br);
-    g.fo = br * QSK + 8 * (lane >> 5);
+    for (int q = 0; q < QNCP; ++q) g.dst[q] = (((q * QWV + wave) * 8) & 127) * 128;
+    g.adst = (wave < QAW ? wave : 0) * 1024;
+    g.fsw = q8_pair_swz(br);
+    g.fhi = br >= 128;
+    g.fo = (br & 127) * 128 + 8 * (lane >> 5);
     g.ao = (lane & 31) * 128;
-    g.scp = srow(br);
     g.acc = f32x16_t{};
 }
+// Weight copy q (8 rows x 128 bytes; copies 0 .. QNCP/2 - 1 fill rows 0..127
+// of a pair): the stage row of this copy lane, and its byte offset in that
+// row's 128 bytes.
+__device__ __forceinline__ int q8_copy_row(int q, int wave, int lane) { return (q * QWV + wave) * 8 + (lane >> 3); }
+__device__ __forceinline__ int q8_copy_byte(int sr, int lane) { return 16 * ((lane & 7) ^ q8_pair_swz(sr)); }
 
 // Eight weight stages of 16 KB and eight A stages of 4 KB: the whole 160 KB.
 #define Q8_DMA_LDS                                                                 \
@@ -227,13 +232,31 @@ __device__ __forceinline__ void gateup_q8_dma_pass(const FfnArgs& a, const TileR
     const bool shared = tr.g == a.E;
     const int K = a.d, KB = K / 32;
     const int r32 = lane & 31;
-    const MatRef& G = shared ? a.s_gate : a.gate;
-    const MatRef& U = shared ? a.s_up : a.up;
+    const uint8_t* gq = static_cast<const uint8_t*>(shared ? a.s_gate.q : a.gate.q);
+    const uint8_t* uq = static_cast<const uint8_t*>(shared ? a.s_up.q : a.up.q);
+    const uint16_t* gsc = shared ? a.s_gate.scale : a.gate.scale;
+    const uint16_t* usc = shared ? a.s_up.scale : a.up.scale;
     const size_t e0 = (size_t)(shared ? 0 : tr.g) * F;
-    // stage rows 0..127: gate rows n0 + r, 128..255: up rows n0 + r - 128 (rows past F read row n0)
-    auto grow = [&](int sr) -> size_t { const int n = n0 + (sr & 127); return e0 + (n < F ? n : n0); };
-    // A row r: the token of tile row r (rows past the tile read token 0; their results are never stored)
-    auto arow = [&](int r) -> const uint8_t* {
+    QTile g;
+    const int br = 32 * wave + r32;
+    q8_dma_setup(g, wave, lane, br);
+    // stage rows 32 m .. 32 m + 15: gate rows n0 + 16 m + (0..15), 32 m + 16 ..
+    // 32 m + 31: the same up rows, so each wavefront's 32 fragment rows lie in
+    // one half of a pair (rows past F read row n0)
+#pragma unroll
+    for (int q = 0; q < QNCP; ++q) {
+        const int sr = q8_copy_row(q, wave, lane);
+        const int n = n0 + 16 * (sr >> 5) + (sr & 15);
+        const size_t row = e0 + (n < F ? n : n0);
+        g.src[q] = ((sr & 31) < 16 ? gq : uq) + row * K + q8_copy_byte(sr, lane);
+    }
+    {
+        const int n = n0 + 16 * wave + (r32 & 15);
+        const size_t row = e0 + (n < F ? n : n0);
+        g.scp = reinterpret_cast<const uint4*>((r32 < 16 ? gsc : usc) + row * KB);
+    }
+    {   // A row r: the token of tile row r (rows past the tile read token 0; their results are never stored)
+        const int r = a_copy_row(wave < QAW ? wave : 0, lane);
         int t = 0;
         if (r < tr.nrows) {
             if (shared) {
@@ -243,15 +266,9 @@ __device__ __forceinline__ void gateup_q8_dma_pass(const FfnArgs& a, const TileR
                 t = (f >= 0 && f < a.T * a.k) ? f / a.k : 0;
             }
         }
-        return reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.x) + (size_t)t * K);
-    };
-    QTile g;
-    const int br = (r32 < 16 ? 0 : 128) + 16 * wave + (r32 & 15);
-    q8_dma_setup(
-        g, wave, lane, br,
-        [&](int sr) { return static_cast<const uint8_t*>(sr < 128 ? G.q : U.q) + grow(sr) * K; },
-        [&](int b) { return reinterpret_cast<const uint4*>((b < 128 ? G.scale : U.scale) + grow(b) * KB); },
-        arow);
+        g.asrc = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.x) + (size_t)t * K) +
+                 a_copy_chunk(lane) * 16;
+    }
     q8_run(g, K / QSK, wave, X, Y);
 
     // lane l (l & 31 < 16) holds gate column n0 + 16w + (l & 15) of rows
@@ -274,18 +291,25 @@ __device__ __forceinline__ void down_q8_dma_pass(const FfnArgs& a, const TileRow
     const int N = a.d;
     const int K = shared ? a.Fs : a.F, KB = K / 32;
     const int r32 = lane & 31;
-    const MatRef& D = shared ? a.s_down : a.down;
+    const uint8_t* dq = static_cast<const uint8_t*>(shared ? a.s_down.q : a.down.q);
+    const uint16_t* dsc = shared ? a.s_down.scale : a.down.scale;
     const size_t e0 = (size_t)(shared ? 0 : tr.g) * N;
-    auto drow = [&](int sr) -> size_t { const int n = n0 + sr; return e0 + (n < N ? n : n0); };
     QTile g;
     const int br = 32 * wave + r32;
-    q8_dma_setup(
-        g, wave, lane, br, [&](int sr) { return static_cast<const uint8_t*>(D.q) + drow(sr) * K; },
-        [&](int b) { return reinterpret_cast<const uint4*>(D.scale + drow(b) * KB); },
-        [&](int r) {  // rows past the tile: never stored
-            return reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.h) +
-                                                    (size_t)(tr.rbeg + (r < tr.nrows ? r : 0)) * a.ldh);
-        });
+    q8_dma_setup(g, wave, lane, br);
+#pragma unroll
+    for (int q = 0; q < QNCP; ++q) {  // stage row sr: output column n0 + sr (rows past N read row n0)
+        const int sr = q8_copy_row(q, wave, lane);
+        const size_t row = e0 + (n0 + sr < N ? n0 + sr : n0);
+        g.src[q] = dq + row * K + q8_copy_byte(sr, lane);
+    }
+    g.scp = reinterpret_cast<const uint4*>(dsc + (e0 + (n0 + br < N ? n0 + br : n0)) * KB);
+    {   // A row r (rows past the tile read row 0; never stored)
+        const int r = a_copy_row(wave < QAW ? wave : 0, lane);
+        g.asrc = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.h) +
+                                                  (size_t)(tr.rbeg + (r < tr.nrows ? r : 0)) * a.ldh) +
+                 a_copy_chunk(lane) * 16;
+    }
     q8_run(g, K / QSK, wave, X, Y);
 
     const int col = n0 + br;
