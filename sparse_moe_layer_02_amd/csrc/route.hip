@@ -18,6 +18,7 @@
 // kernel splits the sum across a workgroup (fixed order) for latency; its fp64
 // sum rounds to the same fp32 value except in vanishingly rare cases.
 #include "common.h"
+#include "dma_dev.h"
 #include "kernels.h"
 #include "route_dev.h"
 
@@ -216,14 +217,15 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
 // Wr rows, widened to fp64 as they are read from LDS; every product is exact
 // in fp64 and the unit accumulates in fp64, so only the order of the fp64
 // additions differs from the definition's, far below the fp32 rounding of the
-// result).  K is staged raw through two LDS stages of 64 columns: the next
-// chunk's global loads are in flight while the current one is consumed, and
-// one barrier per chunk separates the stages.  Inside a chunk the K order is
-// free (the products are exact), so each 16-column group is split so that the
-// lane with K slot lk takes columns 4 lk .. 4 lk + 3 of the group over four
+// result).  K is staged raw through three LDS stages of 64 columns, copied
+// straight from global memory into LDS (1 KB per copy instruction: whole
+// 128- or 256-byte rows), chunk c + 2 issued into the stage of chunk c - 1
+// behind one barrier per chunk.  Inside a chunk the K order is free (the
+// products are exact), so each 16-column group is split so that the lane
+// with K slot lk takes columns 4 lk .. 4 lk + 3 of the group over four
 // instructions: one 8-byte (x, bf16) and two 16-byte (Wr) LDS reads feed
-// eight MFMAs.  Row pitches of 4 mod 64 words put the sixteen rows a read
-// serves on distinct banks.
+// eight MFMAs.  The 16-byte chunks of a staged row are XOR-swizzled so the
+// sixteen rows a read serves hit distinct banks.
 //
 // Operand layout of the 16x16x4 f64 instruction (checked on the device): lane l
 // supplies A[l % 16][l / 16] and B[l / 16][l % 16]; its four results are
@@ -235,64 +237,57 @@ template <int AF>
 __global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict__ x,
                                                           const float* __restrict__ wr, int T, int d,
                                                           int E, float* __restrict__ logits) {
-    constexpr int TM = 64, TE = 64, KC = 64, NT = 512;
-    constexpr int XW = AF == MOE_DT_BF16 ? KC / 2 : KC;  // 32-bit words of one staged x row
-    constexpr int XP = XW + 4, WP = KC + 4;              // row pitches in words (4 mod 64, 16-byte rows)
-    __shared__ __attribute__((aligned(16))) uint32_t xs[2][TM * XP];  // raw x (bf16 pairs or fp32), two stages
-    __shared__ __attribute__((aligned(16))) float ws[2][TE * WP];     // raw Wr, two stages
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    constexpr int TM = 64, TE = 64, KC = 64, NW = 8;
+    constexpr int XRB = KC * (AF == MOE_DT_BF16 ? 2 : 4);  // bytes of one staged x row (128 or 256)
+    constexpr int XS = TM * XRB, WS = TE * KC * 4;          // bytes of a stage's x and Wr rows
+    constexpr int XCP = XS / 1024, NCP = (XS + WS) / 1024;  // 1 KB copies per stage (x, all)
+    constexpr int NQ = NCP / NW, XQ = XCP / NW;             // per wavefront (all, x)
+    static_assert(NQ * NW == NCP && XQ * NW == XCP, "copy geometry");
+    constexpr int XCH = XRB / 16;                           // 16-byte chunks per x row
+    // three stages of raw x and raw Wr rows (separate objects: reading one
+    // stage does not wait for the copies into the others)
+    __shared__ __attribute__((aligned(1024))) uint8_t xs0[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs1[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs2[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t ws0[WS];
+    __shared__ __attribute__((aligned(1024))) uint8_t ws1[WS];
+    __shared__ __attribute__((aligned(1024))) uint8_t ws2[WS];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
     const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TE;
-    // staging items of 16 bytes: x rows hold XW / 4 of them, Wr rows KC / 4
-    constexpr int XQ = TM * XW / 4, WQ = TE * KC / 4;
-    constexpr int XI = (XQ + NT - 1) / NT, WI = WQ / NT;
-    static_assert(WQ % NT == 0 && XI <= 2, "staging shape");
-    uint4 rx[XI];
-    float4 rw[WI];
-    auto gload = [&](int k0) {
+    // chunk c of row r sits at slot c ^ sw(r): x rows of 128 bytes sw = (r >> 1) & 7,
+    // rows of 256 bytes sw = r & 15 (the sixteen rows one read serves hit distinct banks)
+    auto xswz = [](int r) { return XCH == 8 ? (r >> 1) & 7 : r & 15; };
+    // copy q of this wavefront: 1 KB = 1024 / row bytes rows, lane l at slot l % chunks
+    // (rows past T or E read the last row; their results are never stored)
+    const uint8_t* src[NQ];
+    int dst[NQ];
 #pragma unroll
-        for (int it = 0; it < XI; ++it) {
-            const int q = tid + NT * it, r = q / (XW / 4), c = (q % (XW / 4)) * 4;  // c in words
-            rx[it] = make_uint4(0, 0, 0, 0);
-            if (q < XQ && t0 + r < T) {
-                const uint32_t* row = AF == MOE_DT_BF16
-                    ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + (size_t)(t0 + r) * d + k0)
-                    : reinterpret_cast<const uint32_t*>(static_cast<const float*>(x) + (size_t)(t0 + r) * d + k0);
-                rx[it] = *reinterpret_cast<const uint4*>(row + c);
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < WI; ++it) {
-            const int q = tid + NT * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
-            rw[it] = e0 + r < E ? *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * d + k0 + c)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    auto lstore = [&](int stg) {
-#pragma unroll
-        for (int it = 0; it < XI; ++it) {
-            const int q = tid + NT * it, r = q / (XW / 4), c = (q % (XW / 4)) * 4;
-            if (q < XQ) *reinterpret_cast<uint4*>(&xs[stg][r * XP + c]) = rx[it];
-        }
-#pragma unroll
-        for (int it = 0; it < WI; ++it) {
-            const int q = tid + NT * it, r = q / (KC / 4), c = (q % (KC / 4)) * 4;
-            *reinterpret_cast<float4*>(&ws[stg][r * WP + c]) = rw[it];
-        }
-    };
-    // x[m][k0 .. k0 + 3] of a stage, widened to fp64 (exact)
-    auto xvals = [&](int stg, int m, int k0, double (&v)[4]) {
-        if constexpr (AF == MOE_DT_BF16) {
-            const uint2 p = *reinterpret_cast<const uint2*>(&xs[stg][m * XP + (k0 >> 1)]);
-            v[0] = (double)bf16_lo(p.x);
-            v[1] = (double)bf16_hi(p.x);
-            v[2] = (double)bf16_lo(p.y);
-            v[3] = (double)bf16_hi(p.y);
+    for (int q = 0; q < NQ; ++q) {
+        const int id = q * NW + wave;
+        if (q < XQ) {
+            const int r = id * (1024 / XRB) + lane / XCH, slot = lane % XCH;
+            const int row = min(t0 + r, T - 1);
+            src[q] = static_cast<const uint8_t*>(x) + (size_t)row * d * (XRB / KC) + 16 * (slot ^ xswz(r));
+            dst[q] = id * 1024;
         } else {
-            const uint4 p = *reinterpret_cast<const uint4*>(&xs[stg][m * XP + k0]);
-            v[0] = (double)__uint_as_float(p.x);
-            v[1] = (double)__uint_as_float(p.y);
-            v[2] = (double)__uint_as_float(p.z);
-            v[3] = (double)__uint_as_float(p.w);
+            const int id2 = id - XCP;
+            const int r = id2 * 4 + lane / 16, slot = lane % 16;
+            const int row = min(e0 + r, E - 1);
+            src[q] = reinterpret_cast<const uint8_t*>(wr + (size_t)row * d) + 16 * (slot ^ (r & 15));
+            dst[q] = id2 * 1024;
+        }
+    }
+    const int nch = d / KC;
+    auto issue = [&](auto sc, int ch) {
+        constexpr int S = decltype(sc)::value;
+        uint8_t* X = S == 0 ? xs0 : S == 1 ? xs1 : xs2;
+        uint8_t* W = S == 0 ? ws0 : S == 1 ? ws1 : ws2;
+        const int c = ch < nch ? ch : nch - 1;  // chunks past the end re-read the last (unused)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            if (q < XQ) copy16(src[q] + (size_t)c * XRB, X + dst[q]);
+            else copy16(src[q] + (size_t)c * 256, W + dst[q]);
         }
     };
 
@@ -302,22 +297,41 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict
     f64x4 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
-
-    const int nch = d / KC;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int ch = 0; ch < nch; ++ch) {
-        const int stg = ch & 1;
-        if (ch + 1 < nch) gload((ch + 1) * KC);  // in flight during this chunk's products
+    const int xm = wm + lr;
+    // chunk ch in stage S: wait for it (chunk ch + 1 may still be in flight),
+    // barrier (every wavefront has also finished the stage of chunk ch - 1),
+    // issue chunk ch + 2 into that stage, then the products
+    auto chunk = [&](auto sc, int ch) {
+        constexpr int S = decltype(sc)::value;
+        const uint8_t* X = S == 0 ? xs0 : S == 1 ? xs1 : xs2;
+        const uint8_t* W = S == 0 ? ws0 : S == 1 ? ws1 : ws2;
+        wait_vm<NQ>();
+        barrier_nofence();
+        issue(ic<(S + 2) % 3>(), ch + 2);
 #pragma unroll
         for (int kg = 0; kg < KC; kg += 16) {  // K slot lk of instruction s: column kg + 4 lk + s
             double av[4];
-            xvals(stg, wm + lr, kg + 4 * lk, av);
+            if constexpr (AF == MOE_DT_BF16) {
+                const int c = kg / 8 + lk / 2;
+                const uint2 p = *reinterpret_cast<const uint2*>(X + xm * XRB + 16 * (c ^ xswz(xm)) + 8 * (lk & 1));
+                av[0] = (double)bf16_lo(p.x);
+                av[1] = (double)bf16_hi(p.x);
+                av[2] = (double)bf16_lo(p.y);
+                av[3] = (double)bf16_hi(p.y);
+            } else {
+                const int c = kg / 4 + lk;
+                const float4 p = *reinterpret_cast<const float4*>(X + xm * XRB + 16 * (c ^ xswz(xm)));
+                av[0] = (double)p.x;
+                av[1] = (double)p.y;
+                av[2] = (double)p.z;
+                av[3] = (double)p.w;
+            }
             float4 wv[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                wv[j] = *reinterpret_cast<const float4*>(&ws[stg][(wn + 16 * j + lr) * WP + kg + 4 * lk]);
+            for (int j = 0; j < 2; ++j) {
+                const int n = wn + 16 * j + lr;
+                wv[j] = *reinterpret_cast<const float4*>(W + n * 256 + 16 * ((kg / 4 + lk) ^ (n & 15)));
+            }
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
@@ -327,10 +341,19 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const void* __restrict
                 }
             }
         }
-        // the other stage was last read in the previous chunk, before the barrier below it
-        if (ch + 1 < nch) lstore(stg ^ 1);
-        __syncthreads();
+        wait_lgkm0();  // this stage's reads done before the next barrier releases its refill
+    };
+    issue(ic<0>(), 0);
+    issue(ic<1>(), 1);
+    int ch = 0;
+    for (; ch + 3 <= nch; ch += 3) {
+        chunk(ic<0>(), ch);
+        chunk(ic<1>(), ch + 1);
+        chunk(ic<2>(), ch + 2);
     }
+    if (ch < nch) chunk(ic<0>(), ch);
+    if (ch + 1 < nch) chunk(ic<1>(), ch + 1);
+    wait_vm<0>();  // no copy may still be writing LDS when the workgroup ends
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = e0 + wn + 16 * j + lr;
