@@ -491,6 +491,32 @@ __device__ __forceinline__ void cold_dispatch(B& body, int nrows, int wave) {
 // together write 16 or 32 contiguous bytes per run pair.
 __device__ __forceinline__ int run_col(int q, int lane) { return 8 * q + 4 * (lane >> 5); }
 
+// A wavefront's 32 x 32 fp32 block stored as whole 128-byte row segments:
+// lane l holds row l & 31 in runs of four columns (run_col), so a direct
+// store instruction would write 32 rows x 32 bytes.  The block goes through
+// the wavefront's own 4 KB of LDS (16-byte chunk c of row r at slot
+// c ^ ((r >> 1) & 7): no bank conflicts either way), scaled by the lane row's
+// w, then each lane stores 16 bytes of row 8 p + l / 8 (p = 0..3): eight whole
+// rows per instruction.  dst(R) is row R's output address for the block, or
+// null (row not stored).
+template <class D>
+__device__ __forceinline__ void store_block_rows(uint8_t* wl, const f32x16_t& v, float w, int lane, D dst) {
+    const int r = lane & 31;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int slot = (2 * q + (lane >> 5)) ^ ((r >> 1) & 7);
+        *reinterpret_cast<float4*>(wl + r * 128 + slot * 16) =
+            make_float4(w * v[4 * q], w * v[4 * q + 1], w * v[4 * q + 2], w * v[4 * q + 3]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int R = 8 * p + (lane >> 3), c = lane & 7;
+        const float4 val = *reinterpret_cast<const float4*>(wl + R * 128 + ((c ^ ((R >> 1) & 7)) * 16));
+        float* o = dst(R);
+        if (o) *reinterpret_cast<float4*>(o + 4 * c) = val;
+    }
+}
+
 // h = bf16(silu(g) * u) of four adjacent columns as one 8-byte store.
 __device__ __forceinline__ void store_h4(uint16_t* dst, const f32x16_t& g, const f32x16_t& u, int q) {
     uint32_t w[2];
@@ -757,22 +783,25 @@ struct DownTile {
 
         k_loop(g, K / SK, X0, X2, X4, X6, X1, X3, X5, X7);
 
-        // epilogue: lane holds row (lane & 31) of each row block (see run_col)
+        // epilogue through LDS (store_block_rows): every wavefront has left
+        // the K loop's LDS stages before any is reused
+        wait_lgkm0();
+        barrier_nofence();
         float* out = shared ? a.shared_out : a.slot_out;
+        uint8_t* wl = (wave < 4 ? X0 : X2) + (wave & 3) * 4096;
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
-            const int row = block_row<MW>(i, mh) + (lane & 31);
-            if (row >= tr.nrows || dst_row[row] < 0) continue;
-            float* orow = out + (size_t)dst_row[row] * N + n0;
-            const float w = wrow[row];
+            const int rb = block_row<MW>(i, mh);
+            const int row = rb + (lane & 31);
+            const float w = row < tr.nrows ? wrow[row] : 0.0f;
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 if (n0 + brow[j] >= N) continue;  // (d is a multiple of 64: whole blocks)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<float4*>(orow + brow[j] + run_col(q, lane)) =
-                        make_float4(w * g.acc[i][j][4 * q], w * g.acc[i][j][4 * q + 1], w * g.acc[i][j][4 * q + 2],
-                                    w * g.acc[i][j][4 * q + 3]);
+                store_block_rows(wl, g.acc[i][j], w, lane, [&](int R) -> float* {
+                    const int rr = rb + R;
+                    if (rr >= tr.nrows || dst_row[rr] < 0) return nullptr;
+                    return out + (size_t)dst_row[rr] * N + n0 + brow[j];
+                });
             }
         }
     }
