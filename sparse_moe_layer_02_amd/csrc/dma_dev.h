@@ -40,15 +40,12 @@ __device__ __forceinline__ void copy16(const uint8_t* src, uint8_t* dst) {
 template <int K>
 using ic = std::integral_constant<int, K>;
 
-// LDS rows of 64 bytes: the four 16-byte chunks of row r sit at slot c ^ f(r),
-// f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1), so that sixteen consecutive rows
-// read at one chunk hit sixteen different 16-byte bank groups.
-__device__ __forceinline__ int slot_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
-
-// Copy lanes: lane l of copy q of wavefront w fills stage row
-// r = (q * WV + w) * 16 + l / 4, slot l & 3, which holds logical chunk
-// (l & 3) ^ f(r); f(r) = ((l >> 3) & 3) ^ ((l >> 5) & 1) since r = l / 4 mod 16.
-__device__ __forceinline__ int copy_row(int q, int wv, int wave, int lane) { return (q * wv + wave) * 16 + (lane >> 2); }
-__device__ __forceinline__ int copy_chunk(int lane) { return (lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1); }
+// LDS rows of 128 bytes (a copy instruction of 64 lanes x 16 bytes then
+// covers eight whole cache lines): the eight 16-byte chunks of row r sit at
+// slot c ^ g(r), g(r) = (r >> 1) & 7, so that sixteen consecutive rows read at
+// one chunk hit sixteen different 16-byte bank groups.  Copy lane l of a copy
+// of rows r0 .. r0 + 7 (r0 a multiple of 8) fills row r0 + l / 8, slot l & 7,
+// which holds logical chunk (l & 7) ^ g(r0 + l / 8).
+__device__ __forceinline__ int pair_swz(int r) { return (r >> 1) & 7; }
 
 }  // namespace moe

@@ -18,13 +18,12 @@
 // written at M0 + 16 * lane), which costs no VGPRs and no LDS write
 // instructions.
 //
-// Pipeline.  K advances in stages of 32.  The A rows of four stages live in
-// four separate LDS arrays (separate objects, so the compiler can tell that
-// reading one stage does not wait for the copies into the others); chunk
-// j + 4 is copied into the array of chunk j as soon as every wavefront has
-// finished reading it, so each copy has three stages of MFMA work to land.
-// The B (weight) rows go in pairs of stages (K64, whole 128-byte lines per
-// row, see k_loop) through two pair arrays, two stages to land.  Inside a stage the
+// Pipeline.  K advances in stages of 32, the operands in pairs of stages
+// (K64: 128-byte rows, so each copy instruction covers eight whole cache
+// lines) through separate LDS arrays (separate objects, so the compiler can
+// tell that reading one pair does not wait for the copies into the others):
+// three A pair arrays, each A pair copied three stages before it is read, and
+// two B (weight) pair arrays, two stages ahead (see k_loop).  Inside a stage the
 // two K16 steps alternate: while the MFMAs of one step run, the fragments of
 // the next step are read; the copies of the next chunk and the first
 // fragments of the next stage are issued between the MFMAs of the second step
@@ -41,12 +40,10 @@
 // costs about its weight stream (3.1 MB at d = 6144) instead of a full
 // 256-row product.
 //
-// LDS layout of an A stage: rows of 64 bytes (32 bf16 of K).  The four
-// 16-byte chunks of row r sit at slot c ^ f(r), f(r) = ((r >> 1) & 3) ^
-// ((r >> 3) & 1): the sixteen lanes that a 128-bit LDS read serves per cycle
-// (sixteen consecutive rows, one chunk) hit sixteen different 16-byte bank
-// groups (measured: no bank-conflict cycles).  B pairs: rows of 128 bytes,
-// the same property with g(r) = (r >> 1) & 7 over eight chunks.
+// LDS layout of a pair: rows of 128 bytes (64 bf16 of K).  The eight 16-byte
+// chunks of row r sit at slot c ^ g(r), g(r) = (r >> 1) & 7: the sixteen
+// lanes that a 128-bit LDS read serves per cycle (sixteen consecutive rows,
+// one chunk) hit sixteen different 16-byte bank groups.
 #include "common.h"
 #include "dma_dev.h"
 #include "gemm_dev.h"
@@ -76,61 +73,60 @@ struct Geo {
     static constexpr int BM = BM_, NW = WV / MW, NWV = WV;
     static constexpr int MI = BM / (32 * MW);      // 32-row blocks per wavefront
     static constexpr int NI = SBN / (32 * NW);    // 32-column blocks per wavefront
-    static constexpr int ROWS = BM + SBN;         // LDS rows per stage
-    static constexpr int STAGE = ROWS * SROW;     // bytes per stage
-    static constexpr int NCP = ROWS / (16 * WV);  // copies per wavefront per stage (16 rows each)
-    static constexpr int NCA = BM / (16 * WV);    // ... of which A rows
-    static_assert(MI >= 1 && NI >= 1 && NCA >= 1 && NCP * 16 * WV == ROWS && NCA * 16 * WV == BM, "geometry");
+    static constexpr int NCA8 = BM / (8 * WV);    // A copies per wavefront per pair of stages (8 rows x 128 bytes)
+    static_assert(MI >= 1 && NI >= 1 && NCA8 >= 1 && NCA8 * 8 * WV == BM, "geometry");
 };
 
 // First row of row block i of wavefront row mh.
 template <int MW>
 __device__ __forceinline__ int block_row(int i, int mh) { return 32 * (MW * i + mh); }
 
-// B rows of a pair of K32 stages (K64) in the hot loop: 256 rows of 128 bytes
-// in two arrays of 128 rows.  A copy of 64 lanes x 16 bytes then covers eight
-// whole 128-byte lines (eight rows) rather than sixteen half lines: the copy
-// path of a CU costs per instruction and per line, and whole lines take it
-// measurably less.  The eight 16-byte chunks of row r sit at slot
-// c ^ g(r), g(r) = (r >> 1) & 7: sixteen consecutive rows read at one chunk
-// hit sixteen different 16-byte bank groups.
-constexpr int PROW = 2 * SROW;  // LDS bytes per row of a B pair
-__device__ __forceinline__ int pair_swz(int r) { return (r >> 1) & 7; }
+// Rows of a pair of K32 stages (K64): 128 bytes, so a copy of 64 lanes x 16
+// bytes covers eight whole 128-byte lines (eight rows) rather than sixteen
+// half lines: the copy path of a CU costs per instruction and per line, and
+// whole lines take it measurably less (chunk swizzle: pair_swz).
+constexpr int PROW = 2 * SROW;  // LDS bytes per row of a pair
 
 // One tile's operand sources (copy lane addresses, fragment offsets) and its
 // accumulators, for a wavefront that computes AI of its MI row blocks (the
 // blocks that hold rows of the tile; AI = 0: copies only) and issues NCAA of
-// the NCA A-row copies of a stage (those that reach rows of the tile), and
-// NCB B-row copies per pair of stages.
+// the NCA8 A-row copies of a pair of stages (those that reach rows of the
+// tile) and NCB B-row copies per pair.  A and B rows both travel in pairs of
+// K32 stages (K64: 128-byte rows, eight whole lines per copy).  An A pair
+// array is four quarters of 64 rows (copy q fills quarter q; row block i,
+// rows 32 (2 i + mh), lies in quarter i), a B pair array two halves of 128
+// rows (block j < NI / 2 in the first).
 template <class GEO, int AI, int NCAA>
 struct Gemm {
-    static constexpr int NI = GEO::NI, NCA_ = NCAA, NCAA_COPIES = NCAA;
+    static constexpr int NI = GEO::NI, NCA_ = NCAA;
     static constexpr int NCB = SBN / 8 / GEO::NWV;    // B copies per wavefront per pair (eight rows each)
     static_assert(NCB * 8 * GEO::NWV == SBN && NCB % 2 == 0, "B copies fill both halves of a pair");
-    static_assert(NI == 2 && GEO::NW == 4, "a wavefront's two B blocks lie in the two halves of a pair");
-    static constexpr int NCPA = NCAA + NCB;           // A copies, then B copies
+    static_assert(NI == 2 && GEO::NW == 4 && GEO::MI == 4, "pair layout: two B blocks, four A quarters");
+    static_assert(GEO::NCA8 == 4, "one A copy per quarter and wavefront");
+    static constexpr int NCPA = NCAA + NCB;           // A copies, then B copies (per pair of stages)
     static constexpr int NF = AI > 0 ? AI + NI : 0;   // fragments per K16 step
     static constexpr int NM = AI * NI;                // MFMAs per K16 step
     static constexpr int AIS = AI > 0 ? AI : 1, NFS = NF > 0 ? NF : 1;
     const uint8_t* src[NCPA];  // per-lane source of each copy at K = 0
-    int dst[NCPA];             // wave-uniform LDS byte offset (A: in an A array; B: in its half of a pair)
-    int fo[NFS];               // per-lane LDS byte offset of each fragment (first K16 step)
+    int dst[NCPA];             // wave-uniform LDS byte offset (in its quarter / half of a pair)
+    int fo[NFS];               // per-lane LDS byte offset of each fragment (first K16 step of a pair)
     f32x16_t acc[AIS][NI];
 
-    // A copy ci (< NCAA) of the chunk at byte offset kb into the A array SA
-    __device__ __forceinline__ void copy_a(uint8_t* SA, int ci, size_t kb) const { copy16(src[ci] + kb, SA + dst[ci]); }
-    // B copy ci (>= NCAA) of the pair at byte offset pb: the first NCB / 2
-    // fill rows 0..127 (Blo), the rest rows 128..255 (Bhi)
+    // A copy ci (< NCAA) of the pair at byte offset pb into quarter ci
+    __device__ __forceinline__ void copy_a(uint8_t* const (&AQ)[4], int ci, size_t pb) const {
+        copy16(src[ci] + pb, AQ[ci] + dst[ci]);
+    }
+    // B copy ci (>= NCAA): the first NCB / 2 fill rows 0..127 (Blo), the rest rows 128..255
     __device__ __forceinline__ void copy_b(uint8_t* Blo, uint8_t* Bhi, int ci, size_t pb) const {
         copy16(src[ci] + pb, (ci - NCAA < NCB / 2 ? Blo : Bhi) + dst[ci]);
     }
-    // fragment fi: A (fi = 0 or > NI) at K16 step ks of its stage (step 1
-    // reads logical chunk c + 2: slot ^ 2); B block j = fi - 1 at K16 step sp
-    // (0..3) of its pair (logical chunk c + 2 sp: slot ^ 2 sp); block j < NI/2
-    // lies in Blo, the other in Bhi
-    __device__ __forceinline__ bf16x8_t frag(const uint8_t* SA, const uint8_t* Blo, const uint8_t* Bhi, int fi,
-                                             int ks, int sp) const {
-        if (fi == 0 || fi > NI) return *reinterpret_cast<const bf16x8_t*>(SA + (ks ? (fo[fi] ^ 32) : fo[fi]));
+    // fragment fi at K16 step sp (0..3) of its pair (logical chunk c + 2 sp: slot ^ 2 sp)
+    __device__ __forceinline__ bf16x8_t frag(uint8_t* const (&AQ)[4], const uint8_t* Blo, const uint8_t* Bhi, int fi,
+                                             int sp) const {
+        if (fi == 0 || fi > NI) {
+            const int i = fi == 0 ? 0 : fi - NI;
+            return *reinterpret_cast<const bf16x8_t*>(AQ[i] + (fo[fi] ^ (32 * sp)));
+        }
         return *reinterpret_cast<const bf16x8_t*>((fi - 1 < NI / 2 ? Blo : Bhi) + (fo[fi] ^ (32 * sp)));
     }
     // MFMA t of a K16 step: block (i, j) = (t / NI, t % NI); fragments are
@@ -146,71 +142,65 @@ struct Gemm {
 };
 
 // The K loop shared by both kernels.  nst = K / 32 stages (even: K is a
-// multiple of 64).  A rows: chunk c (K32) at byte offset c * 64 of a row, in
-// four A arrays, one per stage; chunk j + 4 is copied into the array of chunk
-// j as soon as every wavefront has read it (three stages to land).  B rows:
-// pair p (K64) at byte offset p * 128 of a row, in two pair arrays; pair
-// p + 2 is copied into the arrays of pair p at its second stage's barrier,
-// after every wavefront has read it (two stages to land).  Each stage has one
-// barrier, between its two K16 steps: by then every fragment of the stage has
-// been read (the second step's during the first), and the next stage's
-// operands must have landed (the next stage's first fragments are read during
-// the second step).  Vector-memory counts complete in issue order; a stage
-// issues its A copy first, then (odd stages) its B pair, so at the barrier of
-// an odd stage only the last even stage's A copy may still be in flight, and
-// at an even stage the last odd stage's A copy and B pair and the A copy
-// before.
+// multiple of 64), in pairs p = (2p, 2p + 1).  A pair p lives in A pair array
+// p mod 3, B pair p in B pair array p mod 2.  A pair p + 2 goes out at the
+// barrier of stage 2p (every wavefront has then finished pair p - 1, whose
+// arrays it takes), three stages before it is read; B pair p + 2 at the
+// barrier of stage 2p + 1, into the arrays of pair p, two stages before.  Each stage has
+// one barrier, between its two K16 steps: by then every fragment of the
+// stage has been read (the second step's during the first), and the next
+// stage's operands must have landed (its first fragments are read during the
+// second step).  Vector-memory counts complete in issue order: at an odd
+// stage's barrier only the A pair issued at the even stage before may still
+// be in flight; even stages need nothing new.
 template <class GM>
-__device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* A0, uint8_t* A1, uint8_t* A2, uint8_t* A3,
-                                       uint8_t* B0lo, uint8_t* B0hi, uint8_t* B1lo, uint8_t* B1hi) {
+__device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* const (&A0)[4], uint8_t* const (&A1)[4],
+                                       uint8_t* const (&A2)[4], uint8_t* B0lo, uint8_t* B0hi, uint8_t* B1lo,
+                                       uint8_t* B1hi) {
     constexpr int NCAA = GM::NCA_, NCB = GM::NCB, NF = GM::NF, NM = GM::NM, NFS = GM::NFS;
     bf16x8_t P[NFS], Q[NFS];
-    const int last = nst - 1, lastp = nst / 2 - 1;
-    auto kb = [&](int c) { return (size_t)(c < last ? c : last) * SROW; };
+    const int lastp = nst / 2 - 1;
     auto pb = [&](int p) { return (size_t)(p < lastp ? p : lastp) * PROW; };
-    auto arr = [&](auto kc) -> uint8_t* {
-        constexpr int K = decltype(kc)::value % 4;
-        if constexpr (K == 0) return A0;
-        else if constexpr (K == 1) return A1;
-        else if constexpr (K == 2) return A2;
-        else return A3;
-    };
     // Fragment reads go with the first three quarters of a step's MFMAs, so
     // they have landed when the step ends; the copies go with the last three
     // quarters.
     constexpr int RD = (NM * 3 + 3) / 4, CP = NM / 4;
 
-    // stage J of four (chunk j): A array J, B pair array J / 2, K32 half J & 1
+    // stage J of twelve (chunk j): A pair array (J / 2) mod 3, B pair array
+    // (J / 2) mod 2, K32 half J & 1 of the pair
     auto stage = [&](auto kc, int j) {
         constexpr int J = decltype(kc)::value;
         constexpr bool ODD = (J & 1) != 0;
-        constexpr int NCS = NCAA + (ODD ? NCB : 0);  // copies issued this stage
-        uint8_t* SA = arr(kc);
-        uint8_t* NA = arr(ic<J + 1>());
-        uint8_t* Blo = J < 2 ? B0lo : B1lo;
-        uint8_t* Bhi = J < 2 ? B0hi : B1hi;
-        uint8_t* NBlo = (J + 1) % 4 < 2 ? B0lo : B1lo;
-        uint8_t* NBhi = (J + 1) % 4 < 2 ? B0hi : B1hi;
+        constexpr int PA = (J / 2) % 3, PB = (J / 2) % 2;
+        constexpr int NJ = (J + 1) % 12, NPA = (NJ / 2) % 3, NPB = (NJ / 2) % 2;
+        constexpr int NCS = ODD ? NCB : NCAA;  // copies issued this stage
+        uint8_t* const (&AQ)[4] = PA == 0 ? A0 : PA == 1 ? A1 : A2;
+        uint8_t* const (&NAQ)[4] = NPA == 0 ? A0 : NPA == 1 ? A1 : A2;
+        uint8_t* Blo = PB == 0 ? B0lo : B1lo;
+        uint8_t* Bhi = PB == 0 ? B0hi : B1hi;
+        uint8_t* NBlo = NPB == 0 ? B0lo : B1lo;
+        uint8_t* NBhi = NPB == 0 ? B0hi : B1hi;
         // step 0 MFMAs (fragments P) with step 1's fragment reads (Q)
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
             g.mfma(P, t);
 #pragma unroll
             for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q)
-                Q[q] = g.frag(SA, Blo, Bhi, q, 1, 2 * (J & 1) + 1);
+                Q[q] = g.frag(AQ, Blo, Bhi, q, 2 * (J & 1) + 1);
             pin();
         }
-        // every read of this stage done; chunk j + 1 (A and B) landed
+        // every read of this stage done; chunk j + 1 landed
         wait_lgkm0();
-        wait_vm<ODD ? NCAA : 2 * NCAA + NCB>();
+        wait_vm<ODD ? NCAA : NCAA + NCB>();
         barrier_nofence();
-        // step 1 MFMAs (Q) with the copies (A chunk j + 4 into SA; odd
-        // stages: B pair (j + 3) / 2 into this pair's arrays) and the first
-        // fragment reads of the next stage (P)
-        const size_t k4 = kb(j + 4), p2 = pb((j + 3) / 2);
+        // step 1 MFMAs (Q) with the copies (even stages: A pair j / 2 + 2 into
+        // the arrays of pair j / 2 - 1; odd stages: B pair (j + 3) / 2 into
+        // this pair's B arrays) and the first fragment reads of the next stage
+        const size_t pa = pb(j / 2 + 2), pbb = pb((j + 3) / 2);
+        uint8_t* const (&FAQ)[4] = PA == 0 ? A2 : PA == 1 ? A0 : A1;  // arrays of pair j / 2 - 1 (= j / 2 + 2 mod 3)
         auto issue = [&](int q) {
-            if (q < NCAA) g.copy_a(SA, q, k4);
-            else g.copy_b(Blo, Bhi, q, p2);
+            if constexpr (ODD) g.copy_b(Blo, Bhi, NCAA + q, pbb);
+            else g.copy_a(FAQ, q, pa);
         };
         if constexpr (NM == 0) {
 #pragma unroll
@@ -221,62 +211,76 @@ __device__ __forceinline__ void k_loop(GM& g, int nst, uint8_t* A0, uint8_t* A1,
             g.mfma(Q, t);
 #pragma unroll
             for (int q = spread<NF, 0, RD>(t); q < spread<NF, 0, RD>(t + 1); ++q)
-                P[q] = g.frag(NA, NBlo, NBhi, q, 0, 2 * ((J + 1) & 1));
+                P[q] = g.frag(NAQ, NBlo, NBhi, q, 2 * ((J + 1) & 1));
 #pragma unroll
             for (int q = spread<NCS, CP, NM>(t); q < spread<NCS, CP, NM>(t + 1); ++q) issue(q);
             pin();
         }
     };
 
-    // prologue, in the steady state's issue order: A chunks 0, 1, B pair 0,
-    // A chunks 2, 3, B pair 1; then wait for chunk 0 (A chunk 0, B pair 0)
+    // prologue, in the steady state's issue order: A pair 0, B pair 0, A pair
+    // 1, B pair 1; then wait for pair 0
 #pragma unroll
-    for (int q = 0; q < NCAA; ++q) g.copy_a(A0, q, kb(0));
-#pragma unroll
-    for (int q = 0; q < NCAA; ++q) g.copy_a(A1, q, kb(1));
+    for (int q = 0; q < NCAA; ++q) g.copy_a(A0, q, pb(0));
 #pragma unroll
     for (int q = NCAA; q < NCAA + NCB; ++q) g.copy_b(B0lo, B0hi, q, pb(0));
 #pragma unroll
-    for (int q = 0; q < NCAA; ++q) g.copy_a(A2, q, kb(2));
-#pragma unroll
-    for (int q = 0; q < NCAA; ++q) g.copy_a(A3, q, kb(3));
+    for (int q = 0; q < NCAA; ++q) g.copy_a(A1, q, pb(1));
 #pragma unroll
     for (int q = NCAA; q < NCAA + NCB; ++q) g.copy_b(B1lo, B1hi, q, pb(1));
-    wait_vm<2 * NCAA + NCB>();
+    wait_vm<NCAA + NCB>();
     barrier_nofence();
 #pragma unroll
-    for (int q = 0; q < NF; ++q) P[q] = g.frag(A0, B0lo, B0hi, q, 0, 0);
+    for (int q = 0; q < NF; ++q) P[q] = g.frag(A0, B0lo, B0hi, q, 0);
 
     int j = 0;
-    for (; j + 4 <= nst; j += 4) {
+    for (; j + 12 <= nst; j += 12) {
         stage(ic<0>(), j);
         stage(ic<1>(), j + 1);
         stage(ic<2>(), j + 2);
         stage(ic<3>(), j + 3);
+        stage(ic<4>(), j + 4);
+        stage(ic<5>(), j + 5);
+        stage(ic<6>(), j + 6);
+        stage(ic<7>(), j + 7);
+        stage(ic<8>(), j + 8);
+        stage(ic<9>(), j + 9);
+        stage(ic<10>(), j + 10);
+        stage(ic<11>(), j + 11);
     }
-    if (j < nst) stage(ic<0>(), j);  // (nst is even: zero or two stages left)
+    // (nst is even: an even number of stages left, at most ten)
+    if (j < nst) stage(ic<0>(), j);
     if (j + 1 < nst) stage(ic<1>(), j + 1);
+    if (j + 2 < nst) stage(ic<2>(), j + 2);
+    if (j + 3 < nst) stage(ic<3>(), j + 3);
+    if (j + 4 < nst) stage(ic<4>(), j + 4);
+    if (j + 5 < nst) stage(ic<5>(), j + 5);
+    if (j + 6 < nst) stage(ic<6>(), j + 6);
+    if (j + 7 < nst) stage(ic<7>(), j + 7);
+    if (j + 8 < nst) stage(ic<8>(), j + 8);
+    if (j + 9 < nst) stage(ic<9>(), j + 9);
     // no copy may still be writing LDS when the workgroup ends
     wait_vm<0>();
 }
 
-// Element offset of a copy lane's 16-byte chunk within a row (bf16).
-__device__ __forceinline__ int copy_col(int lane) { return copy_chunk(lane) * 8; }
 
 
 // Per-lane fragment offsets: wavefront (mh, nh) reads A rows
-// block_row(i, mh) + (lane & 31) and B rows brow[j] + (lane & 31) (B block j
-// < NI/2 lies in rows 0..127 of a pair, the other in rows 128..255).
+// block_row(i, mh) + (lane & 31) (quarter i of an A pair) and B rows brow[j] +
+// (lane & 31) (B block j < NI/2 lies in rows 0..127 of a pair, the other in
+// rows 128..255).
 template <class GEO, class GM, int MW>
 __device__ __forceinline__ void frag_offsets(GM& g, int mh, const int (&brow)[GEO::NI], int lane) {
     if constexpr (GM::NF > 0) {
         const int r = lane & 31;
         const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);  // chunk lane / 32 of row lane & 31
         const int base = r * SROW + slot0 * 16;
-#pragma unroll
-        for (int i = 0; i < GM::AIS; ++i) g.fo[GM::fa_idx(i)] = block_row<MW>(i, mh) * SROW + base;
-        // B: row brow + r of a pair (in its half), logical chunk lane / 32
+        (void)base;
+        // row r of a 32-row block of a pair (A: in its quarter, B: in its
+        // half), logical chunk lane / 32
         const int bslot = (lane >> 5) ^ pair_swz(r);
+#pragma unroll
+        for (int i = 0; i < GM::AIS; ++i) g.fo[GM::fa_idx(i)] = ((block_row<MW>(i, mh) & 63) + r) * PROW + bslot * 16;
 #pragma unroll
         for (int j = 0; j < GEO::NI; ++j) g.fo[GM::fb_idx(j)] = ((brow[j] & 127) + r) * PROW + bslot * 16;
     }
@@ -292,18 +296,20 @@ __device__ __forceinline__ int active_blocks(int nrows, int mh) {
 template <class GEO, int WV>
 __device__ __forceinline__ int active_a_copies(int nrows) {
     const int rows = (nrows + 31) / 32 * 32;
-    return min(GEO::NCA, max(1, (rows + 16 * WV - 1) / (16 * WV)));
+    return min(GEO::NCA8, max(1, (rows + 8 * WV - 1) / (8 * WV)));
 }
 
-// Calls body.template run<AI, NCAA>() for the runtime pair (ai, ncaa).
-template <class GEO, int AI, int NCAA, class B>
-__device__ __forceinline__ void dispatch(int ai, int ncaa, B& body) {
-    if (ai == AI && ncaa == NCAA) {
-        body.template run<AI, NCAA>();
+// Calls body.template run<AI, NCAA>() for the runtime pair (ai, ncaa); with
+// two wavefront rows ai is ncaa or ncaa - 1 (copy q covers rows 64 q ..
+// 64 q + 63, wavefront row mh blocks mh, mh + 2, ...).
+template <class GEO, int NCAA, class B>
+__device__ __forceinline__ void dispatch_pairs(int ai, int ncaa, B& body) {
+    if (ncaa == NCAA) {
+        if (ai == NCAA) body.template run<NCAA, NCAA>();
+        else body.template run<NCAA - 1, NCAA>();
         return;
     }
-    if constexpr (NCAA < GEO::NCA) dispatch<GEO, AI, NCAA + 1>(ai, ncaa, body);
-    else if constexpr (AI < GEO::MI) dispatch<GEO, AI + 1, 1>(ai, ncaa, body);
+    if constexpr (NCAA < GEO::NCA8) dispatch_pairs<GEO, NCAA + 1>(ai, ncaa, body);
 }
 
 // ---------------------------------------------------------------------------
@@ -331,21 +337,21 @@ __device__ __forceinline__ void dispatch(int ai, int ncaa, B& body) {
 constexpr int COLD_ROWS = COLD_ROWS_MAX;  // one row block
 constexpr int COLD_WIDE = COLD_WIDE_MAX;  // two row blocks
 static_assert(COLD_ROWS <= 32 && COLD_WIDE <= 64, "a cold tile is at most two 32-row blocks");
-constexpr int YS = 64 * SROW;  // bytes of one cold A array: one stage's A rows (4 KB)
+constexpr int YS = 64 * PROW;  // bytes of one A pair array of a cold tile: 64 rows x 128 bytes (8 KB)
 
-// AI: row blocks this wavefront computes (0 or 1); NA: 16-row A copies it
-// issues per stage (0 or 1).
+// AI: row blocks this wavefront computes (0 or 1); NA: 8-row A copies it
+// issues per pair of stages (0 or 1).
 template <class GEO, int AI, int NA>
 struct GemmCold {
     static_assert(AI == 0 || AI == 1, "a cold tile gives a wavefront at most one row block");
-    static_assert(NA == 0 || NA == 1, "at most one A copy per wavefront and stage");
+    static_assert(NA == 0 || NA == 1, "at most one A copy per wavefront and pair");
     static constexpr int BLOCKS = AI, ACOPIES = NA;
     static constexpr int NI = GEO::NI, NCB = SBN / 8 / GEO::NWV;  // B-row copies per wavefront per pair (8 rows)
     static_assert(NI == 2 && GEO::NW == 4 && NCB % 2 == 0, "a wavefront's two B blocks lie in the two halves of a pair");
-    static constexpr int NCPP = 2 * NA + NCB;                      // copies per wavefront per pair of stages
+    static constexpr int NCPP = NA + NCB;                          // copies per wavefront per pair of stages
     const uint8_t* asrc;   // NA: this lane's A-row copy source at K = 0
     int adst;              // NA: wave-uniform offset of the copy in an A array
-    int fa;                // AI: A fragment offset in an A array (K16 step 0)
+    int fa;                // AI: A fragment offset in an A pair array (first K16 step)
     const uint8_t* src[NCB];
     int dst[NCB];          // offsets in a half of a B pair
     int fo[NI];            // B fragment offsets (first K16 step of a pair)
@@ -366,10 +372,10 @@ __device__ __forceinline__ uint8_t* pick8(uint8_t* a0, uint8_t* a1, uint8_t* a2,
     else return a7;
 }
 
-// The K loop of a cold tile: nst = K / 32 stages in eight slots; slot s holds
-// the A rows (Y array s) of chunk c = s mod 8, and slots 2m, 2m + 1 hold the
-// B rows of that pair of chunks (K64: 128-byte rows, rows 0..127 in X array
-// 2m and 128..255 in X array 2m + 1, laid out as the hot loop's B pairs).
+// The K loop of a cold tile: nst = K / 32 stages in eight slots; slots 2m,
+// 2m + 1 hold a pair of chunks (K64: 128-byte rows, laid out as the hot
+// loop's pairs): the B rows in X arrays 2m (rows 0..127) and 2m + 1 (rows
+// 128..255), the A rows in Y array m.
 // Chunks are fetched in pairs (2m, 2m + 1): each B copy covers eight whole
 // 128-byte lines (see the hot loop's B pairs).  At an even stage j: the pair (j, j + 1)
 // has landed (the pairs of chunks j + 2 .. j + 5 may still be in flight) and
@@ -378,24 +384,22 @@ __device__ __forceinline__ uint8_t* pick8(uint8_t* a0, uint8_t* a1, uint8_t* a2,
 template <class GC>
 __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t* X1, uint8_t* X2, uint8_t* X3,
                                             uint8_t* X4, uint8_t* X5, uint8_t* X6, uint8_t* X7, uint8_t* Y0,
-                                            uint8_t* Y1, uint8_t* Y2, uint8_t* Y3, uint8_t* Y4, uint8_t* Y5,
-                                            uint8_t* Y6, uint8_t* Y7) {
+                                            uint8_t* Y1, uint8_t* Y2, uint8_t* Y3) {
     constexpr int NCPP = GC::NCPP, NI = GC::NI, NCB = GC::NCB;
     const int last = nst - 1;
-    auto kb = [&](int c) { return (size_t)(c < last ? c : last) * SROW; };
     auto pb = [&](int c) { return (size_t)((c < last ? c : last) / 2) * PROW; };
     auto slot = [&](auto kc) { return pick8<decltype(kc)::value>(X0, X1, X2, X3, X4, X5, X6, X7); };
-    auto aslot = [&](auto kc) { return pick8<decltype(kc)::value>(Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7); };
+    auto aslot = [&](auto kc) {  // the A pair array of slot K
+        constexpr int M = decltype(kc)::value / 2;
+        return M == 0 ? Y0 : M == 1 ? Y1 : M == 2 ? Y2 : Y3;
+    };
     // chunks c, c + 1 into slots K, K + 1 (K even, c even): A rows, then the
     // B pair (whole 128-byte lines)
     auto issue_pair = [&](auto kc, int c) {
         constexpr int K = decltype(kc)::value;
         static_assert(K % 2 == 0, "pairs start at even slots");
-        if constexpr (GC::ACOPIES == 1) {
-            copy16(g.asrc + kb(c), aslot(kc) + g.adst);
-            copy16(g.asrc + kb(c + 1), aslot(ic<K + 1>()) + g.adst);
-        }
         const size_t p0 = pb(c);
+        if constexpr (GC::ACOPIES == 1) copy16(g.asrc + p0, aslot(kc) + g.adst);
 #pragma unroll
         for (int q = 0; q < NCB; ++q) copy16(g.src[q] + p0, (q < NCB / 2 ? slot(kc) : slot(ic<K + 1>())) + g.dst[q]);
     };
@@ -414,7 +418,7 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
             bf16x8_t af[2], b[2][NI];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                af[s] = *reinterpret_cast<const bf16x8_t*>(SA + (s ? (g.fa ^ 32) : g.fa));
+                af[s] = *reinterpret_cast<const bf16x8_t*>(SA + (g.fa ^ (32 * (2 * (K & 1) + s))));
 #pragma unroll
                 for (int jj = 0; jj < NI; ++jj)
                     b[s][jj] = *reinterpret_cast<const bf16x8_t*>((jj < NI / 2 ? Blo : Bhi) +
@@ -454,32 +458,20 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
 
 }  // namespace
 
-// Cold tiles (see k_loop_cold): the wavefronts of the rows that hold a row
-// block compute it (row mh owns block mh, so a tile of up to 32 rows is
-// computed by wavefront row 0, one of up to 64 rows by rows 0 and 1), and the
-// tile's A rows are copied in 16-row pieces (2 or 4 of them per stage) by
-// wavefronts of the next row that holds no block, or, with two wavefront
-// rows and two blocks, by the first four wavefronts.
+// Cold tiles (see k_loop_cold): wavefront row mh computes row block mh (a
+// tile of up to 32 rows is computed by wavefront row 0, one of up to 64 rows
+// by rows 0 and 1), and the tile's A rows go in copies of 8 rows x 128 bytes
+// per pair of stages: 4 of them by the wavefronts of row 1 (tiles of up to
+// 32 rows) or 8 by all eight wavefronts.
 template <int MW, int WV, class B>
 __device__ __forceinline__ void cold_dispatch(B& body, int nrows, int wave) {
-    constexpr int NW = WV / MW;
+    static_assert(MW == 2 && WV == 8, "two wavefront rows of four");
     const int mh = wave % MW, nh = wave / MW;
-    const int nb = nrows <= COLD_ROWS ? 1 : 2;  // row blocks
-    if constexpr (MW == 2) {
-        static_assert(WV >= 4, "four A-row copies");
-        if (nb == 1) {
-            if (mh == 0) body.template run_cold<1, 0>(0);
-            else if (nh < 2) body.template run_cold<0, 1>(nh);
-            else body.template run_cold<0, 0>(0);
-        } else {
-            if (wave < 4) body.template run_cold<1, 1>(wave);
-            else body.template run_cold<1, 0>(0);
-        }
+    if (nrows <= COLD_ROWS) {
+        if (mh == 0) body.template run_cold<1, 0>(0);
+        else body.template run_cold<0, 1>(nh);
     } else {
-        static_assert(MW >= 3 && NW >= 4, "a wavefront row with no block copies the A rows");
-        if (mh < nb) body.template run_cold<1, 0>(0);
-        else if (mh == nb && nh < 2 * nb) body.template run_cold<0, 1>(nh);
-        else body.template run_cold<0, 0>(0);
+        body.template run_cold<1, 1>(wave);
     }
 }
 
@@ -539,7 +531,7 @@ struct GateUpTile {
     const TileRows& tr;
     const int* src_row;
     uint8_t *X0, *X1, *X2, *X3, *X4, *X5, *X6, *X7;
-    uint8_t *Y0, *Y1, *Y2, *Y3, *Y4, *Y5, *Y6, *Y7;
+    uint8_t *Y0, *Y1, *Y2, *Y3;
     int F, n0, wave, lane;
 
     template <int AI, int NCAA>
@@ -549,7 +541,6 @@ struct GateUpTile {
         const bool shared = tr.g == a.E;
         const int K = a.d;
         G g;
-        const int cch = copy_col(lane);
         const MatRef& Wg = shared ? a.s_gate : a.gate;
         const MatRef& Wu = shared ? a.s_up : a.up;
         const int ge = shared ? 0 : tr.g;
@@ -557,20 +548,22 @@ struct GateUpTile {
         const uint16_t* ubase = static_cast<const uint16_t*>(Wu.q) + ((size_t)ge * F + n0) * K;
         const uint16_t* xbase = static_cast<const uint16_t*>(a.x);
 #pragma unroll
-        for (int qa = 0; qa < G::NCAA_COPIES; ++qa) {  // A: 16 rows x 64 bytes per copy
-            g.dst[qa] = (qa * WV + wave) * 1024;
+        for (int qa = 0; qa < NCAA; ++qa) {  // A: 8 rows x 128 bytes per copy, rows 64 qa + 8 wave ..
+            const int ar = 64 * qa + 8 * wave + (lane >> 3);
+            g.dst[qa] = wave * 1024;
             // rows past the tile read token 0; their results are never stored
-            const int t = src_row[copy_row(qa, WV, wave, lane)];
-            g.src[qa] = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
+            const int t = src_row[ar];
+            g.src[qa] = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K) +
+                        16 * ((lane & 7) ^ pair_swz(ar));
         }
 #pragma unroll
         for (int b = 0; b < G::NCB; ++b) {  // B: 8 rows x 128 bytes per copy, rows 0..255 = gate, then up
             const int r0 = (b * WV + wave) * 8, br = r0 + (lane >> 3);
-            g.dst[G::NCAA_COPIES + b] = (r0 & 127) * PROW;
+            g.dst[NCAA + b] = (r0 & 127) * PROW;
             const int n = br & 127;
             const int rr = n0 + n < F ? n : 0;  // columns past F read row 0 and are never stored
             const uint16_t* bb = br < 128 ? gbase : ubase;
-            g.src[G::NCAA_COPIES + b] =
+            g.src[NCAA + b] =
                 reinterpret_cast<const uint8_t*>(bb + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
         }
         // wavefront (mh, nh): gate columns nh * 128/NW + 32 j' and the same up
@@ -585,7 +578,10 @@ struct GateUpTile {
 #pragma unroll
             for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
 
-        k_loop(g, K / SK, X0, X2, X4, X6, X1, X3, X5, X7);
+        uint8_t* const AQ0[4] = {X0, X0 + 8192, X2, X2 + 8192};
+        uint8_t* const AQ1[4] = {X4, X4 + 8192, X6, X6 + 8192};
+        uint8_t* const AQ2[4] = {Y0, Y1, Y2, Y3};
+        k_loop(g, K / SK, AQ0, AQ1, AQ2, X1, X3, X5, X7);
 
         // epilogue: lane holds row (lane & 31) of each row block (see run_col)
         uint16_t* h = static_cast<uint16_t*>(a.h);
@@ -612,7 +608,6 @@ struct GateUpTile {
         const bool shared = tr.g == a.E;
         const int K = a.d;
         G g;
-        const int cch = copy_col(lane);
         const MatRef& Wg = shared ? a.s_gate : a.gate;
         const MatRef& Wu = shared ? a.s_up : a.up;
         const int ge = shared ? 0 : tr.g;
@@ -629,26 +624,27 @@ struct GateUpTile {
             g.src[qb] = reinterpret_cast<const uint8_t*>(b + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
         }
         const int mh = wave % MW, nh = wave / MW;
-        if constexpr (NA == 1) {  // rows past the tile read token 0
-            const int t = src_row[16 * ac + (lane >> 2)];
-            g.asrc = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K + cch);
-            g.adst = 16 * ac * SROW;
+        if constexpr (NA == 1) {  // A rows 8 ac .. 8 ac + 7 (rows past the tile read token 0)
+            const int ar = 8 * ac + (lane >> 3);
+            const int t = src_row[ar];
+            g.asrc = reinterpret_cast<const uint8_t*>(xbase + (size_t)(t >= 0 ? t : 0) * K) +
+                     16 * ((lane & 7) ^ pair_swz(ar));
+            g.adst = ac * 1024;
         }
         int brow[NI];
 #pragma unroll
         for (int j = 0; j < NI; ++j) brow[j] = (j < NI / 2 ? 0 : 128) + nh * (128 / NW) + 32 * (j % (NI / 2));
         // fragment lanes: row lane & 31 (of block mh for A), logical chunk
-        // lane / 32 (K16 step 0)
-        const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
-        g.fa = (block_row<MW>(0, mh) + (lane & 31)) * SROW + slot0 * 16;
+        // lane / 32 (first K16 step of a pair)
         const int bslot = (lane >> 5) ^ pair_swz(lane & 31);
+        g.fa = (block_row<MW>(0, mh) + (lane & 31)) * PROW + bslot * 16;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             g.fo[j] = ((brow[j] & 127) + (lane & 31)) * PROW + bslot * 16;
             g.acc[j] = f32x16_t{};
         }
 
-        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7);
+        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3);
 
         if constexpr (AI == 1) {
             const int row = block_row<MW>(0, mh) + (lane & 31);
@@ -681,20 +677,17 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t X5[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X6[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X7[XS];
-    // cold tiles' A rows, one K32 stage each
+    // four 8 KB arrays: the hot loop's third A pair array (64 rows each), or a
+    // cold tile's four A pair arrays
     __shared__ __attribute__((aligned(1024))) uint8_t Y0[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y1[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y2[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y3[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y4[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y5[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y6[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y7[YS];
-    // the tile's source tokens share Y7: the hot loop never uses the Y
-    // arrays, and the cold loop reads them only before its first copy into Y7
+    // the tile's source tokens share Y3: both loops read them before their
+    // first copy into Y3, which goes out after the first barrier of the loop
     // (issued after the first stage's barrier)
     static_assert(BM * sizeof(int) <= YS, "row table fits one A array");
-    int* src_row = reinterpret_cast<int*>(Y7);
+    int* src_row = reinterpret_cast<int*>(Y3);
     int tile, ntile;
     if (!work_item<4>(tile_count(a), tile, ntile)) return;
     TileRows tr;
@@ -718,12 +711,12 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
         src_row[r] = t;
     }
     __syncthreads();
-    GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, F, n0, wave, lane};
+    GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, F, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
     if (tr.nrows <= COLD_WIDE) {
         cold_dispatch<MW, WV>(body, tr.nrows, wave);
     } else {
-        dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
+        dispatch_pairs<GEO, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
 }
 
@@ -738,7 +731,7 @@ struct DownTile {
     const int* dst_row;
     const float* wrow;
     uint8_t *X0, *X1, *X2, *X3, *X4, *X5, *X6, *X7;
-    uint8_t *Y0, *Y1, *Y2, *Y3, *Y4, *Y5, *Y6, *Y7;
+    uint8_t *Y0, *Y1, *Y2, *Y3;
     int n0, wave, lane;
 
     template <int AI, int NCAA>
@@ -749,24 +742,23 @@ struct DownTile {
         const int K = shared ? a.Fs : a.F;
         const int N = a.d;
         G g;
-        const int cch = copy_col(lane);
         const MatRef& D = shared ? a.s_down : a.down;
         const int ge = shared ? 0 : tr.g;
         const uint16_t* dbase = static_cast<const uint16_t*>(D.q) + ((size_t)ge * N + n0) * K;
         const uint16_t* hbase = static_cast<const uint16_t*>(a.h) + (size_t)tr.rbeg * a.ldh;
 #pragma unroll
-        for (int qa = 0; qa < G::NCAA_COPIES; ++qa) {  // A: 16 rows x 64 bytes per copy
-            g.dst[qa] = (qa * WV + wave) * 1024;
-            const int row = copy_row(qa, WV, wave, lane);
-            const int rr = row < tr.nrows ? row : 0;  // rows past the tile: never stored
-            g.src[qa] = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
+        for (int qa = 0; qa < NCAA; ++qa) {  // A: 8 rows x 128 bytes per copy, rows 64 qa + 8 wave ..
+            const int ar = 64 * qa + 8 * wave + (lane >> 3);
+            g.dst[qa] = wave * 1024;
+            const int rr = ar < tr.nrows ? ar : 0;  // rows past the tile: never stored
+            g.src[qa] = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh) + 16 * ((lane & 7) ^ pair_swz(ar));
         }
 #pragma unroll
         for (int b = 0; b < G::NCB; ++b) {  // B: 8 rows x 128 bytes per copy
             const int r0 = (b * WV + wave) * 8, br = r0 + (lane >> 3);
-            g.dst[G::NCAA_COPIES + b] = (r0 & 127) * PROW;
+            g.dst[NCAA + b] = (r0 & 127) * PROW;
             const int rr = n0 + br < N ? br : 0;
-            g.src[G::NCAA_COPIES + b] =
+            g.src[NCAA + b] =
                 reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
         }
         // wavefront (mh, nh): output columns nh * 32 + 128 j (one block in
@@ -781,26 +773,36 @@ struct DownTile {
 #pragma unroll
             for (int j = 0; j < NI; ++j) g.acc[i][j] = f32x16_t{};
 
-        k_loop(g, K / SK, X0, X2, X4, X6, X1, X3, X5, X7);
+        // the lane's rows' destinations and weights (their LDS table is
+        // overwritten by the K loop's third A pair array)
+        int drow[G::AIS];
+        float dw[G::AIS];
+#pragma unroll
+        for (int i = 0; i < AI; ++i) {
+            const int row = block_row<MW>(i, mh) + (lane & 31);
+            drow[i] = row < tr.nrows ? dst_row[row] : -1;
+            dw[i] = row < tr.nrows ? wrow[row] : 0.0f;
+        }
+        uint8_t* const AQ0[4] = {X0, X0 + 8192, X2, X2 + 8192};
+        uint8_t* const AQ1[4] = {X4, X4 + 8192, X6, X6 + 8192};
+        uint8_t* const AQ2[4] = {Y0, Y1, Y2, Y3};
+        k_loop(g, K / SK, AQ0, AQ1, AQ2, X1, X3, X5, X7);
 
         // epilogue through LDS (store_block_rows): every wavefront has left
-        // the K loop's LDS stages before any is reused
+        // the K loop's LDS stages before any is reused; row R's destination
+        // comes from lane R
         wait_lgkm0();
         barrier_nofence();
         float* out = shared ? a.shared_out : a.slot_out;
         uint8_t* wl = (wave < 4 ? X0 : X2) + (wave & 3) * 4096;
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
-            const int rb = block_row<MW>(i, mh);
-            const int row = rb + (lane & 31);
-            const float w = row < tr.nrows ? wrow[row] : 0.0f;
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 if (n0 + brow[j] >= N) continue;  // (d is a multiple of 64: whole blocks)
-                store_block_rows(wl, g.acc[i][j], w, lane, [&](int R) -> float* {
-                    const int rr = rb + R;
-                    if (rr >= tr.nrows || dst_row[rr] < 0) return nullptr;
-                    return out + (size_t)dst_row[rr] * N + n0 + brow[j];
+                store_block_rows(wl, g.acc[i][j], dw[i], lane, [&](int R) -> float* {
+                    const int dr = __shfl(drow[i], R);
+                    return dr >= 0 ? out + (size_t)dr * N + n0 + brow[j] : nullptr;
                 });
             }
         }
@@ -816,7 +818,6 @@ struct DownTile {
         const int K = shared ? a.Fs : a.F;
         const int N = a.d;
         G g;
-        const int cch = copy_col(lane);
         const MatRef& D = shared ? a.s_down : a.down;
         const int ge = shared ? 0 : tr.g;
         const uint16_t* dbase = static_cast<const uint16_t*>(D.q) + ((size_t)ge * N + n0) * K;
@@ -829,11 +830,11 @@ struct DownTile {
             g.src[qb] = reinterpret_cast<const uint8_t*>(dbase + (size_t)rr * K) + 16 * ((lane & 7) ^ pair_swz(br));
         }
         const int mh = wave % MW, nh = wave / MW;
-        if constexpr (NA == 1) {  // rows past the tile read row 0 (never stored)
-            const int row = 16 * ac + (lane >> 2);
-            const int rr = row < tr.nrows ? row : 0;
-            g.asrc = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh + cch);
-            g.adst = 16 * ac * SROW;
+        if constexpr (NA == 1) {  // A rows 8 ac .. 8 ac + 7 (rows past the tile read row 0; never stored)
+            const int ar = 8 * ac + (lane >> 3);
+            const int rr = ar < tr.nrows ? ar : 0;
+            g.asrc = reinterpret_cast<const uint8_t*>(hbase + (size_t)rr * a.ldh) + 16 * ((lane & 7) ^ pair_swz(ar));
+            g.adst = ac * 1024;
         }
         // this lane's output row and weight, read before the K loop: the
         // LDS that holds them is reused by the A-row copies
@@ -844,17 +845,16 @@ struct DownTile {
 #pragma unroll
         for (int j = 0; j < NI; ++j) brow[j] = 128 * j + nh * (128 / NW);
         // fragment lanes: row lane & 31 (of block mh for A), logical chunk
-        // lane / 32 (K16 step 0)
-        const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);
-        g.fa = (block_row<MW>(0, mh) + (lane & 31)) * SROW + slot0 * 16;
+        // lane / 32 (first K16 step of a pair)
         const int bslot = (lane >> 5) ^ pair_swz(lane & 31);
+        g.fa = (block_row<MW>(0, mh) + (lane & 31)) * PROW + bslot * 16;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             g.fo[j] = ((brow[j] & 127) + (lane & 31)) * PROW + bslot * 16;
             g.acc[j] = f32x16_t{};
         }
 
-        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7);
+        k_loop_cold(g, K / SK, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3);
 
         if constexpr (AI == 1) {
             if (drow >= 0) {
@@ -890,19 +890,17 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t X5[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X6[XS];
     __shared__ __attribute__((aligned(1024))) uint8_t X7[XS];
-    // cold tiles' A rows, one K32 stage each
+    // four 8 KB arrays: the hot loop's third A pair array (64 rows each), or a
+    // cold tile's four A pair arrays
     __shared__ __attribute__((aligned(1024))) uint8_t Y0[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y1[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y2[YS];
     __shared__ __attribute__((aligned(1024))) uint8_t Y3[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y4[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y5[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y6[YS];
-    __shared__ __attribute__((aligned(1024))) uint8_t Y7[YS];
-    // the tile's destinations and weights share Y7 (see gateup_dma_kernel)
+    // the tile's destinations and weights share Y3 (see gateup_dma_kernel):
+    // each lane reads its rows' into registers before the K loop
     static_assert(BM * (sizeof(int) + sizeof(float)) <= YS, "row tables fit one A array");
-    int* dst_row = reinterpret_cast<int*>(Y7);
-    float* wrow = reinterpret_cast<float*>(Y7 + BM * sizeof(int));
+    int* dst_row = reinterpret_cast<int*>(Y3);
+    float* wrow = reinterpret_cast<float*>(Y3 + BM * sizeof(int));
     int tile, ntile;
     if (!work_item<4>(tile_count(a), tile, ntile)) return;
     TileRows tr;
@@ -930,12 +928,12 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
         wrow[r] = w;
     }
     __syncthreads();
-    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7, n0, wave, lane};
+    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
     if (tr.nrows <= COLD_WIDE) {
         cold_dispatch<MW, WV>(body, tr.nrows, wave);
     } else {
-        dispatch<GEO, 0, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
+        dispatch_pairs<GEO, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
     }
 }
 

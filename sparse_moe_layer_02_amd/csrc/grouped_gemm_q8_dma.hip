@@ -86,9 +86,7 @@ __device__ __forceinline__ int a_copy_chunk(int lane) { return (lane & 7) ^ ((la
 // Weight rows of a pair of stages (K128: 128 bytes of each row, whole cache
 // lines) in two arrays of 128 rows: a copy of 64 lanes x 16 bytes covers
 // eight whole lines rather than sixteen half lines, which the copy path of a
-// CU takes measurably faster.  The eight 16-byte chunks of row r sit at slot
-// c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int q8_pair_swz(int r) { return (r >> 1) & 7; }
+// CU takes measurably faster (chunk swizzle: pair_swz).
 
 // The K loop: nst = K / 64 stages (a multiple of 4) in eight slots; slot s
 // holds the A rows (Y) of chunk c = s mod 8, slots 2m, 2m + 1 the weight rows
@@ -188,7 +186,7 @@ __device__ __forceinline__ void q8_dma_setup(QTile& g, int wave, int lane, int b
 #pragma unroll
     for (int q = 0; q < QNCP; ++q) g.dst[q] = (((q * QWV + wave) * 8) & 127) * 128;
     g.adst = (wave < QAW ? wave : 0) * 1024;
-    g.fsw = q8_pair_swz(br);
+    g.fsw = pair_swz(br);
     g.fhi = br >= 128;
     g.fo = (br & 127) * 128 + 8 * (lane >> 5);
     g.ao = (lane & 31) * 128;
@@ -198,7 +196,7 @@ __device__ __forceinline__ void q8_dma_setup(QTile& g, int wave, int lane, int b
 // of a pair): the stage row of this copy lane, and its byte offset in that
 // row's 128 bytes.
 __device__ __forceinline__ int q8_copy_row(int q, int wave, int lane) { return (q * QWV + wave) * 8 + (lane >> 3); }
-__device__ __forceinline__ int q8_copy_byte(int sr, int lane) { return 16 * ((lane & 7) ^ q8_pair_swz(sr)); }
+__device__ __forceinline__ int q8_copy_byte(int sr, int lane) { return 16 * ((lane & 7) ^ pair_swz(sr)); }
 
 // Eight weight stages of 16 KB and eight A stages of 4 KB: the whole 160 KB.
 #define Q8_DMA_LDS                                                                 \
