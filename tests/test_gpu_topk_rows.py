@@ -5,8 +5,8 @@ equal the scores at those indices bit for bit (NaN payloads and the sign of
 zero included).  Cases span every launch shape (512 threads with 1..32 keys
 each, 1024 threads with 32 or 64), a ragged tail in the last chunk, the
 degenerate rows of the selection order (all equal, NaN, signed zeros,
-infinities, subnormals, heavy ties at the cut) and the full-size indexer
-workloads.
+infinities, subnormals, heavy ties at the cut), one row per branch of the
+sampled pass (topk_branch_rows) and the full-size indexer workloads.
 """
 import ctypes
 import sys
@@ -138,3 +138,13 @@ def test_topk_rows_clustered(dev, orc, n, k):
     rows[2, -3 * k:] = np.float32(5.0)                     # 3k equal scores at the end: ties at the cut
     rows[3, ::97] += 8.0                                   # spread thinly over every wavefront
     check(dev, orc, rows, k, "clustered_n%d_k%d" % (n, k))
+
+
+@pytest.mark.parametrize("name", ["all candidates equal", "bin whole", "one-wavefront pick",
+                                  "radix on candidates", "full radix"])
+def test_topk_rows_branches(dev, orc, name):
+    """One row per branch of the sampled pass (rows built in topk_branch_rows,
+    whose host-side check confirms the branch each takes), against the oracle."""
+    from topk_branch_rows import branch_rows
+    row, k = branch_rows()[name]
+    check(dev, orc, row[None, :].copy(), k, "branch " + name)
