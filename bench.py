@@ -81,6 +81,12 @@ TOPK_WORKLOADS = {
     "i2": dict(copies=8, steps=200, warmup=20),
     "i3": dict(copies=64, steps=400, warmup=40),
 }
+# The expert GEMMs of c5's hottest experts alone: c5's own routing (the
+# library's router on c5's tokens) with every assignment outside the HOT_E
+# most-loaded experts dropped, then the grouped gate/up and down over what is
+# left (no shared expert).  HOT_E = 10 is 3.9% of the 256 experts, the share the
+# skew is calibrated on.
+HOT_WORKLOADS = {"c5hot": dict(base="c5", hot=10, steps=20, warmup=5)}
 
 
 def describe(cfg):
@@ -500,7 +506,8 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(TOPK_WORKLOADS),
+    ap.add_argument("--workload", default=None,
+                    choices=sorted(WORKLOADS) + sorted(TOPK_WORKLOADS) + sorted(HOT_WORKLOADS),
                     help="one workload alone; default: c5 as the headline with the c2 decode layer beside it")
     ap.add_argument("--no-decode", action="store_true", help="default run: leave out the c2 decode section")
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated across steps")
@@ -554,6 +561,9 @@ def main():
 
     if args.workload in TOPK_WORKLOADS:
         return bench_topk_rows(args)
+    if args.workload in HOT_WORKLOADS:
+        print(json.dumps(measure_hot(args)), flush=True)
+        return
     if args.workload is not None:
         out = measure_layer(args, args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
         print(json.dumps(out), flush=True)
@@ -569,6 +579,79 @@ def main():
                 "expert_union_mean", "stages_us", "cpu_baseline")
         out["decode"] = {key: dec[key] for key in keep if key in dec}
     print(json.dumps(out), flush=True)
+
+
+def measure_hot(args):
+    """The grouped gate/up and down GEMMs over the rows c5 routes to its
+    hottest experts (moe_route, then moe_permute of the masked assignments,
+    then moe_expert_ffn timed alone): matrix-core TFLOP/s of those expert
+    groups.  The kernels are the 256-row-tile ones c5 itself runs."""
+    import numpy as np
+    import torch
+    from synth import configs
+    import sparse_moe_layer_02_amd as moe
+
+    spec = HOT_WORKLOADS[args.workload]
+    steps = args.steps or spec["steps"]
+    warmup = spec["warmup"] if args.warmup is None else args.warmup
+    cfg = configs.get(spec["base"])
+    T, E, k, d, F = cfg["T"], cfg["E"], cfg["k"], cfg["d"], cfg["F"]
+    torch.cuda.init()
+    moe.load()
+    hip = Hip()
+    L = gen_weights_host(dict(cfg, n_shared=0))
+    for key in ("s_gate", "s_up", "s_down"):
+        L[key] = None
+    W = upload_copies(L, 1, torch)[0]
+    x = configs.gen_x(cfg)
+    x_dev = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+    c = moe.config_from(dict(cfg, n_shared=0))
+    ws = moe.workspace(c)
+    stream = torch.cuda.current_stream().cuda_stream
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(c, x_dev, W["w_router"], W["bias"], None, idx, tw, ws, stream=stream)
+    counts = torch.bincount(idx.flatten().long(), minlength=E)
+    hot = torch.topk(counts, spec["hot"]).indices
+    idx_h = torch.where(torch.isin(idx, hot.to(torch.int32)), idx, torch.full_like(idx, -1))
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    moe.moe_permute(c, idx_h, offsets, perm, inv, ws, stream=stream)
+    slot_out = torch.empty((T * k, d), dtype=torch.float32, device="cuda")
+    Wm = moe.make_weights(W)
+    rows = int(counts[hot].sum().item())
+    hot_rows = sorted((int(v) for v in counts[hot].tolist()), reverse=True)
+
+    def ffn():
+        moe.moe_expert_ffn(c, x_dev, Wm, offsets, perm, tw, slot_out, None, ws, stream=stream)
+
+    for _ in range(warmup):
+        ffn()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(steps):
+        ffn()
+    hip.record(e1, stream)
+    hip.sync(e1)
+    ms = hip.ms(e0, e1) / steps
+    flops = 2.0 * rows * d * 3 * F
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "matrix-core TFLOP/s of the grouped expert GEMMs on c5's hottest experts",
+        "value": round(tfs, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16",
+        "dtype_note": DTYPE_NOTE["bf16"],
+        "data": "synthetic (seeded counter-based generator; random-init weights of the layer's shape)",
+        "config": {"workload": "%s: the grouped gate/up and down GEMMs over the rows of c5's %d most-loaded "
+                               "experts (c5's own routing), no shared expert" % (args.workload, spec["hot"]),
+                   "T": T, "d_model": d, "n_expert": E, "top_k": k, "d_ff": F, "hot_experts": spec["hot"],
+                   "hot_rows": rows, "hot_share": round(rows / float(T * k), 4), "rows_per_hot_expert": hot_rows},
+        "mfma_frac": round(tfs / BF16_PEAK_TFS, 4),
+        "flops_per_step": flops,
+        "note": "gate/up and down launches together; profiles/ splits them by kernel",
+    }
 
 
 def measure_layer(args, wname, steps, warmup, with_cpu):
