@@ -118,6 +118,15 @@ class Hip:
         assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
         return e
 
+    def stage_event(self):
+        """A timing event for the dispatch timestamps of a stage's kernels,
+        without the system-scope fence a default event performs when it
+        completes (that fence writes back the caches after the kernel and
+        holds the next dispatch by several microseconds)."""
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) == 0
+        return e
+
     def sync_event(self):
         """An event that only orders streams (the work after it reads no data
         that the work before it writes): no timing and no system-scope fence,
@@ -782,10 +791,13 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
     stage_names = moe.binding.DECODE_STAGES if decode else moe.binding.STAGES
     stage_ids = [moe.binding.STAGES.index(n) for n in stage_names]
     n_ev = moe.binding.STAGE_EVENTS
-    ev = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    live = graph is None and (args.stage_times == "live" or (args.stage_times == "auto" and not decode))
+    # live stage events ride on the timed steps: without the system-scope
+    # fence, so they do not hold the next dispatch; a second eager pass keeps
+    # default events (their kernel times agree with rocprofv3's trace)
+    ev = [[hip.stage_event() if live else hip.event() for _ in range(n_ev)] for _ in range(steps)]
     ev_arr = [(ctypes.c_void_p * n_ev)(*[e.value for e in row]) for row in ev]
     idx_log = torch.empty((steps, T, cfg["k"]), dtype=torch.int32, device="cuda")
-    live = graph is None and (args.stage_times == "live" or (args.stage_times == "auto" and not decode))
     e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
