@@ -533,8 +533,9 @@ def parse_args(argv=None):
     ap.add_argument("--prefetch-which", type=int, default=3,
                     help="look-ahead: matrices the prefetch reads (bit 0 gate, 1 up, 2 down)")
     ap.add_argument("--stage-times", default="auto", choices=["auto", "live", "pass"],
-                    help="take the per-stage kernel times in the timed steps (live) or in a second eager pass "
-                         "(pass); auto: live for prefill, pass for decode, whose 50 us steps the per-dispatch "
+                    help="take the gate/up kernel's times in the timed steps (live; the other stages always come "
+                         "from a second eager pass) or every stage's in that pass (pass); auto: live for prefill, "
+                         "pass for decode, whose 50 us steps the per-dispatch "
                          "timestamps would slow")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -792,10 +793,16 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
     stage_ids = [moe.binding.STAGES.index(n) for n in stage_names]
     n_ev = moe.binding.STAGE_EVENTS
     live = graph is None and (args.stage_times == "live" or (args.stage_times == "auto" and not decode))
-    # live stage events ride on the timed steps: without the system-scope
-    # fence, so they do not hold the next dispatch; a second eager pass keeps
-    # default events (their kernel times agree with rocprofv3's trace)
-    ev = [[hip.stage_event() if live else hip.event() for _ in range(n_ev)] for _ in range(steps)]
+    # Live: the gate/up launch (the roofline kernel) carries its events in the
+    # timed steps, created without the system-scope fence so they do not hold
+    # the next dispatch; every stage's events (default ones, whose kernel times
+    # agree with rocprofv3's trace) come from a second eager pass of the same
+    # steps, which also logs the selected experts.
+    gu = moe.binding.STAGES.index("gate_up")
+    gu_ev = [(hip.stage_event(), hip.stage_event()) for _ in range(steps)] if live else None
+    gu_arr = [(ctypes.c_void_p * n_ev)(*[(p[0].value if j == 2 * gu else p[1].value if j == 2 * gu + 1 else None)
+                                         for j in range(n_ev)]) for p in gu_ev] if live else None
+    ev = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
     ev_arr = [(ctypes.c_void_p * n_ev)(*[e.value for e in row]) for row in ev]
     idx_log = torch.empty((steps, T, cfg["k"]), dtype=torch.int32, device="cuda")
     e0, e1 = hip.event(), hip.event()
@@ -808,7 +815,7 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
             graph.replay()
     elif live:
         for i in range(steps):
-            step(warmup + i, events=ev_arr[i], dbg={"topk_idx": idx_log[i]})
+            step(warmup + i, events=gu_arr[i])
     else:
         for i in range(steps):
             step(warmup + i)
@@ -819,18 +826,21 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
     total_ms = hip.ms(e0, e1)
     ms_per_step = total_ms / steps
 
-    if not live:  # the same steps again, eagerly, for the stage times and the expert log
-        for i in range(steps):
-            step(warmup + i, events=ev_arr[i], dbg={"topk_idx": idx_log[i]})
-        torch.cuda.synchronize()
+    # the same steps again, eagerly, for the stage times and the expert log
+    for i in range(steps):
+        step(warmup + i, events=ev_arr[i], dbg={"topk_idx": idx_log[i]})
+    torch.cuda.synchronize()
     # a stage whose kernels the path does not launch has unrecorded events
-    # and is left out
+    # and is left out; live, the gate/up time is the timed steps' own
     stage_ms = np.full((steps, len(stage_names)), np.nan)
     for i in range(steps):
         for col, sid in enumerate(stage_ids):
-            v = hip.ms_or_none(ev[i][2 * sid], ev[i][2 * sid + 1])
+            if live and sid == gu:
+                v = hip.ms_or_none(gu_ev[i][0], gu_ev[i][1])
+            else:
+                v = hip.ms_or_none(ev[i][2 * sid], ev[i][2 * sid + 1])
             stage_ms[i, col] = np.nan if v is None else v
-    for row in ev:
+    for row in ev + (gu_ev or []):
         for e in row:
             hip.destroy(e)
     stages_us = {name: round(float(stage_ms[:, col].mean()) * 1e3, 2) for col, name in enumerate(stage_names)
@@ -894,7 +904,8 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
         "config": {"workload": describe(cfg), "T": T, "d_model": cfg["d"], "n_expert": cfg["E"],
                    "top_k": cfg["k"], "d_ff": cfg["F"], "weights": cfg["w"], "activations": cfg["act"],
                    "path": path_kind, "weight_copies": n_copies, "hip_graph": bool(args.graph),
-                   "stage_times": "live" if live else "second eager pass",
+                   "stage_times": ("gate/up in the timed steps, the other stages in a second eager pass" if live
+                                   else "second eager pass"),
                    "distinct_tokens": n_tok_rows if decode else T, "router_lookahead": la},
         "roofline": roofline,
         "layer_hbm_GBs": round(float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9, 1),
