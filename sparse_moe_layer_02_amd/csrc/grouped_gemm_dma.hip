@@ -55,7 +55,7 @@ namespace {
 constexpr int SK = 32;        // K per stage
 constexpr int SROW = SK * 2;  // LDS bytes per row of a stage
 constexpr int SBN = 256;      // B rows per tile
-constexpr int XS = SBN * SROW;  // bytes of one LDS array: one stage's A rows or its B rows (16 KB)
+constexpr int XS = SBN * SROW;  // bytes of one LDS array (16 KB): half of a B pair, or two quarters of an A pair
 
 // N items spread evenly over MFMAs [A, B) of a K16 step: the items issued with
 // MFMA t are [spread(t), spread(t + 1)).
@@ -273,9 +273,6 @@ template <class GEO, class GM, int MW>
 __device__ __forceinline__ void frag_offsets(GM& g, int mh, const int (&brow)[GEO::NI], int lane) {
     if constexpr (GM::NF > 0) {
         const int r = lane & 31;
-        const int slot0 = (lane >> 5) ^ ((lane >> 1) & 3) ^ ((lane >> 3) & 1);  // chunk lane / 32 of row lane & 31
-        const int base = r * SROW + slot0 * 16;
-        (void)base;
         // row r of a 32-row block of a pair (A: in its quarter, B: in its
         // half), logical chunk lane / 32
         const int bslot = (lane >> 5) ^ pair_swz(r);
@@ -313,20 +310,19 @@ __device__ __forceinline__ void dispatch_pairs(int ai, int ncaa, B& body) {
 }
 
 // ---------------------------------------------------------------------------
-// Cold tiles: tiles of at most COLD_ROWS rows (an expert with few rows, or
+// Cold tiles: tiles of at most COLD_WIDE rows (an expert with few rows, or
 // the short tail of a hot one).  Their matrix work is a sliver of their weight
-// stream, so what bounds them is how many weight bytes a CU keeps in flight:
-// with the hot tiles' four K32 stages (A and B rows in each) three stages are
-// in flight, about 22 GB/s per CU.  A cold tile uses the same eight LDS arrays
-// as eight B-only K32 stages, seven of them in flight.  Its A rows (up to 64)
-// go to eight small arrays of their own (4 KB each), one 16-row copy per
-// chunk issued by each of two or four wavefronts: the A rows then cross the
-// load path once per workgroup, in copies of 16 rows, rather than once per
-// computing wavefront in fragment loads that each touch 32 rows (about 3% of
-// the cold tiles' time at d = 6144).  Tiles of up to 32 rows are one row
-// block, computed by the first wavefront row while two wavefronts of the
-// second copy its A rows; tiles of 33-64 rows give each wavefront row one
-// block, and the first four wavefronts copy the A rows.
+// stream, so what bounds them is how many weight bytes a CU keeps in flight.
+// A cold tile uses the eight 16 KB LDS arrays as four B pair slots (K64 pairs
+// of 128-byte rows, as in the hot loop), three pairs in flight while the
+// fourth is read.  Its A rows (up to 64) go to the four 8 KB A pair arrays,
+// in K64 pairs too, one copy of 8 rows per pair from each copying wavefront:
+// the A rows cross the load path once per workgroup, in whole-line copies,
+// rather than once per computing wavefront in fragment loads that each touch
+// 32 rows.  Tiles of up to 32 rows are one row block, computed by the first
+// wavefront row while the four wavefronts of the second copy its A rows;
+// tiles of 33-64 rows give each wavefront row one block, and all eight
+// wavefronts copy A rows.
 // ---------------------------------------------------------------------------
 #ifndef COLD_ROWS_MAX
 #define COLD_ROWS_MAX 32
