@@ -118,15 +118,6 @@ class Hip:
         assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
         return e
 
-    def stage_event(self):
-        """A timing event for the dispatch timestamps of a stage's kernels,
-        without the system-scope fence a default event performs when it
-        completes (that fence writes back the caches after the kernel and
-        holds the next dispatch by several microseconds)."""
-        e = ctypes.c_void_p()
-        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) == 0
-        return e
-
     def sync_event(self):
         """An event that only orders streams (the work after it reads no data
         that the work before it writes): no timing and no system-scope fence,
@@ -793,13 +784,14 @@ def measure_layer(args, wname, steps, warmup, with_cpu):
     stage_ids = [moe.binding.STAGES.index(n) for n in stage_names]
     n_ev = moe.binding.STAGE_EVENTS
     live = graph is None and (args.stage_times == "live" or (args.stage_times == "auto" and not decode))
-    # Live: the gate/up launch (the roofline kernel) carries its events in the
-    # timed steps, created without the system-scope fence so they do not hold
-    # the next dispatch; every stage's events (default ones, whose kernel times
-    # agree with rocprofv3's trace) come from a second eager pass of the same
-    # steps, which also logs the selected experts.
+    # Live: only the gate/up launch (the roofline kernel) carries its events
+    # in the timed steps (each timed event's cache fence holds the next
+    # dispatch by several microseconds); every stage's events come from a
+    # second eager pass of the same steps, which also logs the selected
+    # experts.  Default events: with the system-scope fence turned off, the
+    # start timestamp moved ahead of the dispatch (a 163 us launch read 177).
     gu = moe.binding.STAGES.index("gate_up")
-    gu_ev = [(hip.stage_event(), hip.stage_event()) for _ in range(steps)] if live else None
+    gu_ev = [(hip.event(), hip.event()) for _ in range(steps)] if live else None
     gu_arr = [(ctypes.c_void_p * n_ev)(*[(p[0].value if j == 2 * gu else p[1].value if j == 2 * gu + 1 else None)
                                          for j in range(n_ev)]) for p in gu_ev] if live else None
     ev = [[hip.event() for _ in range(n_ev)] for _ in range(steps)]
