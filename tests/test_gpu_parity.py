@@ -353,6 +353,53 @@ def test_split_entry_points(torch_cuda, orc):
         assert H.rownorm_err(y2.cpu().numpy(), orc.combine(cfg, r_slot, r_shared)) < 1e-6
 
 
+def test_expert_ffn_masked_to_hot_experts(torch_cuda, orc):
+    """moe_expert_ffn over a routing masked to its most-loaded experts (every
+    other assignment replaced by -1, as the c5hot benchmark does), on the
+    256-row LDS-copy tiles (T*k >= 96 E): experts of two and three tiles whose
+    last tiles run through the cold loop (5, 13 and 41 rows) or the hot one
+    (232 and 253 rows), with and without the shared expert.  The grouping is
+    exact, every listed slot row (and shared_out) matches the oracle's, and no
+    other slot row is written."""
+    import torch
+    import sparse_moe_layer_02_amd as moe
+    for n_shared, hot in ((0, 3), (1, 5)):
+        cfg = _custom(T=1800, d=256, E=16, k=4, F=128, n_shared=n_shared)
+        T, E, k, d = cfg["T"], cfg["E"], cfg["k"], cfg["d"]
+        assert T * k >= 96 * E
+        say("case masked", dict(n_shared=n_shared, hot=hot))
+        L = configs.make_layer(cfg)
+        r_lg, r_idx, r_w = orc.route(cfg, L["x"], L["w_router"], L["bias"])
+        counts = np.bincount(r_idx.reshape(-1), minlength=E)
+        keep = np.argsort(-counts, kind="stable")[:hot]
+        idx = np.where(np.isin(r_idx, keep), r_idx, -1).astype(np.int32)
+        r_off, r_perm, r_inv = orc.permute(cfg, idx)
+        rows = np.diff(r_off)
+        assert rows.max() > 512 and (rows[keep] % 256).min() > 0  # three-tile experts, ragged tails
+        dev = H.upload_layer(L)
+        c = moe.config_from(cfg)
+        ws = moe.workspace(c)
+        off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        moe.moe_permute(c, H.to_dev(idx), off, perm, inv, ws)
+        slot = torch.full((T * k, d), float("nan"), dtype=torch.float32, device="cuda")
+        shared = torch.empty((T, d), dtype=torch.float32, device="cuda") if n_shared else None
+        moe.moe_expert_ffn(c, dev["x"], moe.make_weights(dev), off, perm, H.to_dev(r_w), slot, shared, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(off.cpu().numpy(), r_off)
+        assert np.array_equal(perm.cpu().numpy(), r_perm)
+        assert np.array_equal(inv.cpu().numpy(), r_inv)
+        r_slot, r_shared = orc.expert_ffn(cfg, L, r_off, r_perm, r_w)
+        listed = r_perm[r_perm >= 0]
+        got = slot.cpu().numpy()
+        H.check_y(got[listed], r_slot[listed], cfg, "slot_out of the kept experts")
+        unlisted = np.setdiff1d(np.arange(T * k), listed)
+        assert np.isnan(got[unlisted]).all(), "a slot row outside the kept experts was written"
+        if n_shared:
+            H.check_y(shared.cpu().numpy(), r_shared, cfg, "shared_out")
+
+
 @pytest.mark.parametrize("spec", [dict(T=4100, d=128, E=192, k=8, F=64, act="bf16", w="bf16"),
                                   dict(T=2100, d=192, E=250, k=6, F=64, act="f32", w="f32",
                                        score="sqrt_softplus", scale=1.5, bias="none"),
