@@ -46,6 +46,19 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 
+// 16 bytes read or written once per launch (weights streamed by the GEMVs,
+// slot rows on their way to the combine): non-temporal accesses, which pass
+// the caches without displacing the data other accesses reuse.
+typedef uint32_t stream_u4 __attribute__((ext_vector_type(4)));
+typedef float stream_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+    const stream_u4 v = __builtin_nontemporal_load(static_cast<const stream_u4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream16(float* p, float4 v) {
+    __builtin_nontemporal_store(stream_f4{v.x, v.y, v.z, v.w}, reinterpret_cast<stream_f4*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Wavefront reductions, all on the VALU (no LDS-crossbar round trips): an
 // inclusive scan inside each 16-lane row with DPP row_shr 1, 2, 4, 8 (lanes

@@ -431,7 +431,7 @@ __device__ __forceinline__ void down_load_batch(DownBatch<WF, NC>& B, const FfnA
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int col = (c * WAVE + lane) * EPL;
-            B.w[g][c] = *reinterpret_cast<const uint4*>(q + (size_t)col * ESZ);
+            B.w[g][c] = ld_stream16(q + (size_t)col * ESZ);
             if constexpr (WF == MOE_DT_Q8B32) B.sc[g][c] = sp[col >> 5];
         }
         __builtin_amdgcn_sched_barrier(0);  // issue order = slot order (reductions wait in that order)

@@ -33,6 +33,12 @@ __device__ __forceinline__ bool tile_rows(const FfnArgs& a, int tile, TileRows& 
 // end up in scratch memory when staged across a loop).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// A weight row piece that no other tile of the launch reads: non-temporal.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16w(const uint16_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return ld16(p);
+}
 __device__ __forceinline__ void st16(uint8_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // The dispatcher deals consecutive workgroups to the 8 XCDs in turn, and each

@@ -112,7 +112,7 @@ __device__ __forceinline__ void wave_dot(const uint8_t* const (&wq)[NR], const u
         uint16_t sraw[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            w[r] = *reinterpret_cast<const uint4*>(wq[r] + (size_t)c * ESZ);
+            w[r] = ld_stream16(wq[r] + (size_t)c * ESZ);
             if constexpr (WF == MOE_DT_Q8B32) sraw[r] = wsc[r][c >> 5];
         }
         float sc[NR];

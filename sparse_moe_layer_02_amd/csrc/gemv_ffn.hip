@@ -85,21 +85,22 @@ __global__ __launch_bounds__(256) void down_slots_kernel(FfnArgs a) {
 
 // ---------------------------------------------------------------------------
 // combine: y[t] = shared_out[t] + sum_j slot_out[t*k + j], four columns per thread.
+// Every input is read once and y is written once, so the accesses are
+// non-temporal: the slot rows stream past the caches instead of displacing
+// what they hold (c5: 188 -> 161 us).  The additions keep their order.
 // ---------------------------------------------------------------------------
+typedef float cf4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const size_t n4 = (size_t)a.T * a.d / 4;
     for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (size_t)gridDim.x * blockDim.x) {
         const size_t t = q * 4 / a.d, c = q * 4 % a.d;
-        float4 acc = a.shared_out ? *reinterpret_cast<const float4*>(a.shared_out + t * a.d + c)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < a.k; ++j) {
-            const float4 s = *reinterpret_cast<const float4*>(a.slot_out + (t * a.k + j) * a.d + c);
-            acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
-        }
-        *reinterpret_cast<float4*>(a.y + t * a.d + c) = acc;
+        cf4 acc = a.shared_out ? __builtin_nontemporal_load(reinterpret_cast<const cf4*>(a.shared_out + t * a.d + c))
+                               : cf4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < a.k; ++j)
+            acc += __builtin_nontemporal_load(reinterpret_cast<const cf4*>(a.slot_out + (t * a.k + j) * a.d + c));
+        __builtin_nontemporal_store(acc, reinterpret_cast<cf4*>(a.y + t * a.d + c));
     }
 }
-
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------

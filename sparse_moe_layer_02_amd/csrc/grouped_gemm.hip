@@ -49,8 +49,9 @@ constexpr int GU_BN = 64;  // columns of gate (and of up) per workgroup
 
 // BM rows x (64 gate + 64 up) columns per workgroup; wavefront (mh, nh) owns
 // rows [BM/2 * mh, BM/2 * (mh + 1)) and columns [32 nh, 32 nh + 32) of both
-// gate and up, as MT = BM/64 blocks of 32 rows.
-template <int BM>
+// gate and up, as MT = BM/64 blocks of 32 rows.  NTW: weight loads
+// non-temporal (experts of one tile: no other workgroup reads the rows).
+template <int BM, bool NTW>
 __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
     constexpr int MT = BM / 64, AP = BM / 32;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + 2 * GU_BN) * ROWB];
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(256, 2) void gateup_mfma_kernel(FfnArgs a) {
         for (int p = 0; p < AP; ++p) R.a[p] = ld16(ap[p] + k0);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            R.g[p] = ld16(gp[p] + k0);
-            R.u[p] = ld16(up[p] + k0);
+            R.g[p] = ld16w<NTW>(gp[p] + k0);
+            R.u[p] = ld16w<NTW>(up[p] + k0);
         }
     };
     auto lstore = [&](const Stage& R, int s) {
@@ -203,8 +204,8 @@ constexpr int DN_BN = 128;
 
 // BM rows x 128 output columns per workgroup; wavefront (mh, nh) owns rows
 // [BM/2 * mh, BM/2 * (mh + 1)) as MT = BM/64 blocks of 32, and columns
-// [64 nh, 64 nh + 64) as two 32-column blocks.
-template <int BM>
+// [64 nh, 64 nh + 64) as two 32-column blocks.  NTW as for gate/up.
+template <int BM, bool NTW>
 __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
     constexpr int MT = BM / 64, AP = BM / 32;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + DN_BN) * ROWB];
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
 #pragma unroll
         for (int p = 0; p < AP; ++p) R.a[p] = ld16(ap[p] + k0);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) R.b[p] = ld16(bp[p] + k0);
+        for (int p = 0; p < 4; ++p) R.b[p] = ld16w<NTW>(bp[p] + k0);
     };
     auto lstore = [&](const Stage& R, int s) {
 #pragma unroll
@@ -334,12 +335,19 @@ __global__ __launch_bounds__(256, 2) void down_mfma_kernel(FfnArgs a) {
         }
 }
 
+// Weight loads non-temporal when the experts average at most 32 rows (one
+// 64-row tile each, mostly): c4 (16 rows) 3.50 -> 3.33 ms.  Experts of two or
+// more tiles share their weight rows between tiles in L2, which non-temporal
+// loads give up (87 rows per expert: 5.62 -> 7.25 ms).
+static bool stream_weights(const FfnArgs& a) { return (long)a.T * a.k <= 32L * a.E; }
+
 hipError_t launch_gateup_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     if (a.bm == 256) return launch_gateup_dma(a, st, kt);
     if (a.bm != 64) return hipErrorInvalidValue;
     const int fmax = a.n_shared && a.Fs > a.F ? a.Fs : a.F;
     dim3 grid(a.max_tiles, (fmax + GU_BN - 1) / GU_BN);
-    launch_kernel(gateup_mfma_kernel<64>, grid, 256, st, kt, a);
+    if (stream_weights(a)) launch_kernel(gateup_mfma_kernel<64, true>, grid, 256, st, kt, a);
+    else launch_kernel(gateup_mfma_kernel<64, false>, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 
@@ -347,7 +355,8 @@ hipError_t launch_down_mfma(const FfnArgs& a, hipStream_t st, const KTime& kt) {
     if (a.bm == 256) return launch_down_dma(a, st, kt);
     if (a.bm != 64) return hipErrorInvalidValue;
     dim3 grid(a.max_tiles, (a.d + DN_BN - 1) / DN_BN);
-    launch_kernel(down_mfma_kernel<64>, grid, 256, st, kt, a);
+    if (stream_weights(a)) launch_kernel(down_mfma_kernel<64, true>, grid, 256, st, kt, a);
+    else launch_kernel(down_mfma_kernel<64, false>, grid, 256, st, kt, a);
     return hipGetLastError();
 }
 

@@ -501,7 +501,7 @@ __device__ __forceinline__ void store_block_rows(uint8_t* wl, const f32x16_t& v,
         const int R = 8 * p + (lane >> 3), c = lane & 7;
         const float4 val = *reinterpret_cast<const float4*>(wl + R * 128 + ((c ^ ((R >> 1) & 7)) * 16));
         float* o = dst(R);
-        if (o) *reinterpret_cast<float4*>(o + 4 * c) = val;
+        if (o) st_stream16(o + 4 * c, val);
     }
 }
 
