@@ -37,6 +37,11 @@ __device__ __forceinline__ void copy16(const uint8_t* src, uint8_t* dst) {
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(dst), 16, 0, 0);
 }
 
+// The same copy marked non-temporal (rows no other workgroup reads).
+__device__ __forceinline__ void copy16_nt(const uint8_t* src, uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(dst), 16, 0, 2);
+}
+
 template <int K>
 using ic = std::integral_constant<int, K>;
 

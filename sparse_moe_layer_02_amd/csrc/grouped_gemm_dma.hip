@@ -95,8 +95,9 @@ constexpr int PROW = 2 * SROW;  // LDS bytes per row of a pair
 // K32 stages (K64: 128-byte rows, eight whole lines per copy).  An A pair
 // array is four quarters of 64 rows (copy q fills quarter q; row block i,
 // rows 32 (2 i + mh), lies in quarter i), a B pair array two halves of 128
-// rows (block j < NI / 2 in the first).
-template <class GEO, int AI, int NCAA>
+// rows (block j < NI / 2 in the first).  BNT: the weight (B) copies are
+// non-temporal.
+template <class GEO, int AI, int NCAA, bool BNT>
 struct Gemm {
     static constexpr int NI = GEO::NI, NCA_ = NCAA;
     static constexpr int NCB = SBN / 8 / GEO::NWV;    // B copies per wavefront per pair (eight rows each)
@@ -118,7 +119,8 @@ struct Gemm {
     }
     // B copy ci (>= NCAA): the first NCB / 2 fill rows 0..127 (Blo), the rest rows 128..255
     __device__ __forceinline__ void copy_b(uint8_t* Blo, uint8_t* Bhi, int ci, size_t pb) const {
-        copy16(src[ci] + pb, (ci - NCAA < NCB / 2 ? Blo : Bhi) + dst[ci]);
+        if constexpr (BNT) copy16_nt(src[ci] + pb, (ci - NCAA < NCB / 2 ? Blo : Bhi) + dst[ci]);
+        else copy16(src[ci] + pb, (ci - NCAA < NCB / 2 ? Blo : Bhi) + dst[ci]);
     }
     // fragment fi at K16 step sp (0..3) of its pair (logical chunk c + 2 sp: slot ^ 2 sp)
     __device__ __forceinline__ bf16x8_t frag(uint8_t* const (&AQ)[4], const uint8_t* Blo, const uint8_t* Bhi, int fi,
@@ -336,9 +338,10 @@ static_assert(COLD_ROWS <= 32 && COLD_WIDE <= 64, "a cold tile is at most two 32
 constexpr int YS = 64 * PROW;  // bytes of one A pair array of a cold tile: 64 rows x 128 bytes (8 KB)
 
 // AI: row blocks this wavefront computes (0 or 1); NA: 8-row A copies it
-// issues per pair of stages (0 or 1).
-template <class GEO, int AI, int NA>
+// issues per pair of stages (0 or 1); BNT: the weight copies are non-temporal.
+template <class GEO, int AI, int NA, bool BNT>
 struct GemmCold {
+    static constexpr bool BNT_ = BNT;
     static_assert(AI == 0 || AI == 1, "a cold tile gives a wavefront at most one row block");
     static_assert(NA == 0 || NA == 1, "at most one A copy per wavefront and pair");
     static constexpr int BLOCKS = AI, ACOPIES = NA;
@@ -397,7 +400,10 @@ __device__ __forceinline__ void k_loop_cold(GC& g, int nst, uint8_t* X0, uint8_t
         const size_t p0 = pb(c);
         if constexpr (GC::ACOPIES == 1) copy16(g.asrc + p0, aslot(kc) + g.adst);
 #pragma unroll
-        for (int q = 0; q < NCB; ++q) copy16(g.src[q] + p0, (q < NCB / 2 ? slot(kc) : slot(ic<K + 1>())) + g.dst[q]);
+        for (int q = 0; q < NCB; ++q) {
+            if constexpr (GC::BNT_) copy16_nt(g.src[q] + p0, (q < NCB / 2 ? slot(kc) : slot(ic<K + 1>())) + g.dst[q]);
+            else copy16(g.src[q] + p0, (q < NCB / 2 ? slot(kc) : slot(ic<K + 1>())) + g.dst[q]);
+        }
     };
     auto stage = [&](auto kc, int j) {
         constexpr int K = decltype(kc)::value;
@@ -520,7 +526,17 @@ __device__ __forceinline__ void store_h4(uint16_t* dst, const f32x16_t& g, const
 // ---------------------------------------------------------------------------
 // gate/up: BM rows x (128 gate + 128 up) columns per workgroup
 // ---------------------------------------------------------------------------
-template <int BM, int MW, int WV>
+// The expert owns a single tile of rows: its weight rows are read by this
+// tile's workgroups only (and each by one of them), so the gate/up kernel
+// copies them non-temporal (BNT) and leaves the caches to the rows that are
+// shared: the A rows, and the weights of experts with several tiles (c5
+// gate/up 2.83 -> 2.78 ms; marking every weight copy non-temporal cost 7%).
+__device__ __forceinline__ bool one_tile_expert(const FfnArgs& a, const TileRows& tr) {
+    const int rows = tr.g == a.E ? a.T : a.offsets[tr.g + 1] - a.offsets[tr.g];
+    return rows <= 256;
+}
+
+template <int BM, int MW, int WV, bool BNT>
 struct GateUpTile {
     using GEO = Geo<BM, MW, WV>;
     const FfnArgs& a;
@@ -532,7 +548,7 @@ struct GateUpTile {
 
     template <int AI, int NCAA>
     __device__ __forceinline__ void run() {
-        using G = Gemm<GEO, AI, NCAA>;
+        using G = Gemm<GEO, AI, NCAA, BNT>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
         const int K = a.d;
@@ -599,7 +615,7 @@ struct GateUpTile {
     // wavefront copies when NA = 1 (rows 16 ac .. 16 ac + 15)
     template <int AI, int NA>
     __device__ __forceinline__ void run_cold(int ac) {
-        using G = GemmCold<GEO, AI, NA>;
+        using G = GemmCold<GEO, AI, NA, BNT>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
         const int K = a.d;
@@ -707,19 +723,21 @@ __global__ __launch_bounds__(64 * WV, 1) void gateup_dma_kernel(FfnArgs a) {
         src_row[r] = t;
     }
     __syncthreads();
-    GateUpTile<BM, MW, WV> body{a, tr, src_row, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, F, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
-    if (tr.nrows <= COLD_WIDE) {
-        cold_dispatch<MW, WV>(body, tr.nrows, wave);
-    } else {
-        dispatch_pairs<GEO, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
-    }
+    auto go = [&](auto bnt) {
+        GateUpTile<BM, MW, WV, decltype(bnt)::value> body{a,  tr, src_row, X0, X1, X2, X3, X4, X5, X6,
+                                                          X7, Y0, Y1,      Y2, Y3, F,  n0, wave, lane};
+        if (tr.nrows <= COLD_WIDE) cold_dispatch<MW, WV>(body, tr.nrows, wave);
+        else dispatch_pairs<GEO, 1>(ai, active_a_copies<GEO, WV>(tr.nrows), body);
+    };
+    if (one_tile_expert(a, tr)) go(std::true_type());
+    else go(std::false_type());
 }
 
 // ---------------------------------------------------------------------------
 // down + weighted scatter: BM rows x 256 output columns per workgroup
 // ---------------------------------------------------------------------------
-template <int BM, int MW, int WV>
+template <int BM, int MW, int WV, bool BNT>
 struct DownTile {
     using GEO = Geo<BM, MW, WV>;
     const FfnArgs& a;
@@ -732,7 +750,7 @@ struct DownTile {
 
     template <int AI, int NCAA>
     __device__ __forceinline__ void run() {
-        using G = Gemm<GEO, AI, NCAA>;
+        using G = Gemm<GEO, AI, NCAA, BNT>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
         const int K = shared ? a.Fs : a.F;
@@ -808,7 +826,7 @@ struct DownTile {
     // wavefront copies when NA = 1 (rows 16 ac .. 16 ac + 15)
     template <int AI, int NA>
     __device__ __forceinline__ void run_cold(int ac) {
-        using G = GemmCold<GEO, AI, NA>;
+        using G = GemmCold<GEO, AI, NA, BNT>;
         constexpr int NI = GEO::NI, NW = GEO::NW;
         const bool shared = tr.g == a.E;
         const int K = shared ? a.Fs : a.F;
@@ -924,7 +942,9 @@ __global__ __launch_bounds__(64 * WV, 1) void down_dma_kernel(FfnArgs a) {
         wrow[r] = w;
     }
     __syncthreads();
-    DownTile<BM, MW, WV> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, n0, wave, lane};
+    // (non-temporal weight copies for one-tile experts help gate/up, not down:
+    // c5 down 1.61 -> 1.65 ms with them)
+    DownTile<BM, MW, WV, false> body{a, tr, dst_row, wrow, X0, X1, X2, X3, X4, X5, X6, X7, Y0, Y1, Y2, Y3, n0, wave, lane};
     const int ai = active_blocks<GEO, MW, WV>(tr.nrows, wave % MW);
     if (tr.nrows <= COLD_WIDE) {
         cold_dispatch<MW, WV>(body, tr.nrows, wave);
