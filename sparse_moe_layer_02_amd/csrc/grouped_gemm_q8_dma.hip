@@ -99,8 +99,8 @@ __device__ __forceinline__ int a_copy_chunk(int lane) { return (lane & 7) ^ ((la
 // j + 2 .. j + 5 may still be in flight) and every wavefront has finished
 // reading slots j - 2 and j - 1, which then receive the pair (j + 6, j + 7).
 // HASA: this wavefront copies A rows (one more vector-memory operation per
-// chunk, so its wait counts differ).
-template <bool HASA>
+// chunk, so its wait counts differ); WNT: the weight copies are non-temporal.
+template <bool HASA, bool WNT>
 __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
     constexpr int NC = QNCB + (HASA ? 1 : 0);  // copies per chunk
     uint4 sc[2];
@@ -116,7 +116,10 @@ __device__ __forceinline__ void q8_k_loop_dma(QTile& g, int nst, uint8_t* const 
         }
         const size_t p0 = (size_t)(c0 & ~1) * QSK;  // the pair's 128 bytes of each weight row
 #pragma unroll
-        for (int q = 0; q < QNCP; ++q) copy16(g.src[q] + p0, (q < QNCP / 2 ? X[K] : X[K + 1]) + g.dst[q]);
+        for (int q = 0; q < QNCP; ++q) {
+            if constexpr (WNT) copy16_nt(g.src[q] + p0, (q < QNCP / 2 ? X[K] : X[K + 1]) + g.dst[q]);
+            else copy16(g.src[q] + p0, (q < QNCP / 2 ? X[K] : X[K + 1]) + g.dst[q]);
+        }
     };
     auto stage = [&](auto kk, int j) {
         constexpr int K = decltype(kk)::value;
@@ -219,12 +222,14 @@ __device__ __forceinline__ int q8_copy_byte(int sr, int lane) { return 16 * ((la
     uint8_t* const X[8] = {X0, X1, X2, X3, X4, X5, X6, X7};                        \
     uint8_t* const Y[8] = {Y0, Y1, Y2, Y3, Y4, Y5, Y6, Y7}
 
+template <bool WNT>
 __device__ __forceinline__ void q8_run(QTile& g, int nst, int wave, uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
-    if (wave < QAW) q8_k_loop_dma<true>(g, nst, X, Y);
-    else q8_k_loop_dma<false>(g, nst, X, Y);
+    if (wave < QAW) q8_k_loop_dma<true, WNT>(g, nst, X, Y);
+    else q8_k_loop_dma<false, WNT>(g, nst, X, Y);
 }
 
 // One pass of a gate/up tile: rows [tr.rbeg, tr.rbeg + tr.nrows), at most 32.
+template <bool WNT>
 __device__ __forceinline__ void gateup_q8_dma_pass(const FfnArgs& a, const TileRows& tr, int F, int n0, int wave,
                                                    int lane, uint8_t* const (&X)[8], uint8_t* const (&Y)[8]) {
     const bool shared = tr.g == a.E;
@@ -267,7 +272,7 @@ __device__ __forceinline__ void gateup_q8_dma_pass(const FfnArgs& a, const TileR
         g.asrc = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(a.x) + (size_t)t * K) +
                  a_copy_chunk(lane) * 16;
     }
-    q8_run(g, K / QSK, wave, X, Y);
+    q8_run<WNT>(g, K / QSK, wave, X, Y);
 
     // lane l (l & 31 < 16) holds gate column n0 + 16w + (l & 15) of rows
     // 8*(v/4) + 4*(l/32) + v%4; lane l ^ 16 the same up column
@@ -308,7 +313,7 @@ __device__ __forceinline__ void down_q8_dma_pass(const FfnArgs& a, const TileRow
                                                   (size_t)(tr.rbeg + (r < tr.nrows ? r : 0)) * a.ldh) +
                  a_copy_chunk(lane) * 16;
     }
-    q8_run(g, K / QSK, wave, X, Y);
+    q8_run<false>(g, K / QSK, wave, X, Y);
 
     const int col = n0 + br;
     float* out = shared ? a.shared_out : a.slot_out;
@@ -328,7 +333,7 @@ __device__ __forceinline__ void down_q8_dma_pass(const FfnArgs& a, const TileRow
                 w = a.topk_w[f];
             }
         }
-        if (dst >= 0) out[(size_t)dst * N + col] = w * g.acc[v];
+        if (dst >= 0) __builtin_nontemporal_store(w * g.acc[v], out + (size_t)dst * N + col);  // read once, by the combine
     }
 }
 
@@ -345,10 +350,18 @@ __global__ __launch_bounds__(64 * QWV, 1) void gateup_q8_dma_kernel(FfnArgs a) {
     const int n0 = ntile * (QBN / 2);
     if (n0 >= F) return;
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int erows = t64.g == a.E ? a.T : a.offsets[t64.g + 1] - a.offsets[t64.g];
+    // an expert of at most 32 rows is one pass of one tile: no other pass or
+    // tile reads its weight rows, which are then copied non-temporal (c2p
+    // gate/up 1.00 -> 0.96 ms)
+    if (erows <= QROWS) {
+        gateup_q8_dma_pass<true>(a, t64, F, n0, wave, lane, X, Y);
+        return;
+    }
     for (int p = 0; p * QROWS < t64.nrows; ++p) {
         if (p) __syncthreads();
         const TileRows tr{t64.g, t64.rbeg + p * QROWS, min(QROWS, t64.nrows - p * QROWS)};
-        gateup_q8_dma_pass(a, tr, F, n0, wave, lane, X, Y);
+        gateup_q8_dma_pass<false>(a, tr, F, n0, wave, lane, X, Y);
     }
 }
 
