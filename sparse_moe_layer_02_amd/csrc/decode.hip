@@ -432,7 +432,7 @@ __device__ __forceinline__ void down_load_batch(DownBatch<WF, NC>& B, const FfnA
         for (int c = 0; c < NC; ++c) {
             const int col = (c * WAVE + lane) * EPL;
             B.w[g][c] = ld_stream16(q + (size_t)col * ESZ);
-            if constexpr (WF == MOE_DT_Q8B32) B.sc[g][c] = sp[col >> 5];
+            if constexpr (WF == MOE_DT_Q8B32) B.sc[g][c] = __builtin_nontemporal_load(&sp[col >> 5]);  // read once, as the row
         }
         __builtin_amdgcn_sched_barrier(0);  // issue order = slot order (reductions wait in that order)
     }

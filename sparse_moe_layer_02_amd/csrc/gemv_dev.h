@@ -113,7 +113,7 @@ __device__ __forceinline__ void wave_dot(const uint8_t* const (&wq)[NR], const u
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             w[r] = ld_stream16(wq[r] + (size_t)c * ESZ);
-            if constexpr (WF == MOE_DT_Q8B32) sraw[r] = wsc[r][c >> 5];
+            if constexpr (WF == MOE_DT_Q8B32) sraw[r] = __builtin_nontemporal_load(&wsc[r][c >> 5]);  // read once, as the row
         }
         float sc[NR];
 #pragma unroll
